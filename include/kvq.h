@@ -1,0 +1,219 @@
+/*
+ * kvq.h — C ABI of a low-bit KV cache for block-diffusion language models on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two operations make up the path:
+ *
+ *  1. kvq_commit: when a block of tokens is finished, its keys and values are
+ *     quantized once into packed 2- or 4-bit codes and appended to a per-layer
+ *     cache.  Keys use KIVI-style asymmetric quantization with one (scale, zero)
+ *     per channel over a group of 32 consecutive tokens; values use one
+ *     (scale, zero) per token over a group of G_v consecutive channels.  A
+ *     per-layer set of key token rows chosen by the caller is kept in bf16 and is
+ *     excluded from quantization.
+ *     Sources: Tai et al., "KV Cache Quantization for Diffusion Language Models"
+ *     (Findings of EMNLP 2026, ACL Anthology record, abstract: KIVI adapted to
+ *     prefix and dual cache reuse; KProtect keeps chosen per-layer K-cache
+ *     entries in high precision while values use standard low-bit quantization);
+ *     "SoloQ: Calibration-Free Quantization for Diffusion Language Models"
+ *     (summary page, paragraph on block diffusion: KV entries are quantized only
+ *     when a block is committed, the block being denoised stays in full
+ *     precision, keys use KIVI-style per-channel asymmetric quantization).
+ *
+ *  2. kvq_block_attn: the block still being denoised (32 query tokens per
+ *     sequence, full precision) attends bidirectionally to itself and to the
+ *     quantized prefix cache, optionally also to a quantized suffix cache of
+ *     masked future tokens ("dual cache").  Attention is computed directly from
+ *     the low-bit codes; no full-precision copy of the cache is materialised.
+ *     Sources: MaskAhead / Q-MaskAhead abstract (attention directly from low-bit
+ *     KV, cache attended at every denoising step); SoloQ summary page (a
+ *     diffusion LM revisits bidirectional context at every denoising step);
+ *     Elastic-Cache abstract, observation (1) (distant MASK tokens can be cached
+ *     block-wise beyond the active window), for the suffix segment.
+ *
+ * The pages give no formula; the quantizer is the plain asymmetric min/max one,
+ * evaluated in IEEE fp32 in this order:
+ *     mn = min(group), mx = max(group)
+ *     scale = (mx - mn) / (2^b - 1)   (fp32 subtract, fp32 division), then + 0.0f
+ *     zero  = mn + 0.0f               (both stored as canonical +0 when zero)
+ *     code  = scale == 0 ? 0 : clamp(rint((x - mn) / scale), 0, 2^b - 1)
+ *             (fp32 subtract, fp32 division, round half to even)
+ * Dequantized value: code * scale + zero.
+ *
+ * ------------------------------------------------------------------------
+ * Ownership, threading and errors
+ * ------------------------------------------------------------------------
+ *  - The caller owns all device memory: the cache buffer handed to kvq_create
+ *    (kvq_required_bytes bytes, 256-byte aligned), inputs and outputs.  The
+ *    library never allocates device memory.  It allocates a small pinned host
+ *    staging ring and two events on first device use; kvq_destroy frees them.
+ *  - Pointers named d_* are device pointers; h_* are host pointers read only
+ *    during the call.  `stream` is a hipStream_t (NULL = default stream).
+ *  - Calls are asynchronous and stream-ordered.  All calls on one handle must be
+ *    issued on one stream or be ordered by the caller.  A handle is not
+ *    thread-safe.
+ *  - Every call returns a kvq_status.  All argument checks run on the host
+ *    before any device work; on any error the cache is unchanged.
+ *    kvq_last_error() gives a thread-local detail string for the last failure.
+ *
+ * ------------------------------------------------------------------------
+ * Packed cache layout (part of the ABI; little-endian)
+ * ------------------------------------------------------------------------
+ * A cache has two segments: PREFIX (committed blocks) and SUFFIX (the masked
+ * future tokens of the dual cache).  Each segment holds, per sequence, a list of
+ * slots; a slot holds the tokens of one 32-token quantization group.  Each
+ * commit starts a new slot at its first token; its last slot may be partial and
+ * is never reopened.
+ *
+ * Slot record, one per (segment, sequence b, kv head h, slot s), located at
+ *     records_offset[seg] + ((b * Hkv + h) * slot_cap[seg] + s) * record_bytes
+ *   Kc    at kc_offset    (= 0): 32 token rows, each D*kb/8 bytes = D*kb/32 u32.
+ *         Word w of row t holds channels [w*32/kb, (w+1)*32/kb); channel c sits
+ *         at bits [kb*(c mod 32/kb), +kb).
+ *   Vc    at vc_offset    (= 32*D*kb/8): D channel rows, each vb u32.
+ *         Token t of channel c is placed by
+ *             mm = t / 16,  h = (t / 4) % 2,  e = (t % 4) + 4 * ((t / 8) % 2)
+ *         vb = 4: word 2*mm + h, bits [4e, 4e+4)
+ *         vb = 2: word h,        bits [2*(8*mm + e), +2)
+ *         (this order puts the 8 tokens one MFMA lane consumes in one u32).
+ *   Kmeta at kmeta_offset (= vc_offset + 4*D*vb): fp32 scale[D], fp32 zero[D].
+ *   Vmeta at vmeta_offset (= kmeta_offset + 8*D): for each channel group
+ *         g < D/G_v: fp32 scale[32 tokens], fp32 zero[32 tokens].
+ *   record_bytes = the above rounded up to a multiple of 256.
+ *   Codes of invalid tokens (past the slot's count) are 0, and so are their V
+ *   scale/zero; codes of protected tokens in Kc are 0 and protected tokens do not
+ *   enter the per-channel K statistics.  A channel group with no contributing
+ *   token has scale = zero = 0.
+ *
+ * Slot header, one per (segment, b, s), 16 bytes at
+ *     headers_offset[seg] + (b * slot_cap[seg] + s) * 16:
+ *   int32 nvalid     tokens in the slot (1..32)
+ *   uint32 prot_mask bit t set <=> token t of the slot is protected
+ *   int32 prot_base  rank of the slot's first protected row in the segment
+ *   int32 token_base segment position of the slot's first token
+ *
+ * Protected K rows, per (segment, b): rank r in [0, nprot) in ascending
+ * position order:
+ *   bf16 rows at prot_rows_offset[seg] + ((b * prot_cap[seg] + r) * Hkv + h) * D * 2
+ *   int32 position at prot_pos_offset[seg] + (b * prot_cap[seg] + r) * 4
+ * A protected token's row in slot s is rank prot_base + popcount(prot_mask & ((1<<t)-1)).
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
+#define KVQ_MAX_BATCH 256
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,       /* malformed argument (null, out of range, unsorted list, ...) */
+  KVQ_EUNSUPPORTED = 2, /* well-formed but outside the supported set */
+  KVQ_ECAPACITY = 3,    /* the commit would exceed a slot or protected-row capacity */
+  KVQ_EHIP = 4          /* a HIP runtime call failed; see kvq_last_error() */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+typedef enum { KVQ_PREFIX = 0, KVQ_SUFFIX = 1 } kvq_segment;
+
+typedef struct {
+  int32_t batch;             /* B, 1..KVQ_MAX_BATCH                                 */
+  int32_t num_kv_heads;      /* Hkv >= 1                                            */
+  int32_t head_dim;          /* D in {64, 128}                                      */
+  int32_t k_bits, v_bits;    /* each in {2, 4}                                      */
+  int32_t k_group_tokens;    /* must be 32                                          */
+  int32_t v_group_channels;  /* G_v in {32, 64, 128}, G_v <= D, D % G_v == 0        */
+  int32_t prefix_slots;      /* slot capacity per sequence, 1..65535                */
+  int32_t suffix_slots;      /* 0..65535 (0 = no suffix segment)                    */
+  int32_t prefix_protected;  /* protected-row capacity per sequence, >= 0           */
+  int32_t suffix_protected;  /* >= 0                                                */
+  int32_t max_q_heads;       /* largest Hq passed to kvq_block_attn (Hq % Hkv == 0) */
+  int32_t max_splits;        /* split-K partial capacity per (b, kv head); 0 = 32   */
+} kvq_config;
+
+typedef struct {
+  uint64_t total_bytes;          /* == kvq_required_bytes                          */
+  uint64_t record_bytes;
+  uint64_t kc_offset, vc_offset, kmeta_offset, vmeta_offset; /* within a record   */
+  uint64_t records_offset[2];
+  uint64_t headers_offset[2];
+  uint64_t prot_rows_offset[2];
+  uint64_t prot_pos_offset[2];
+  int32_t slot_cap[2];
+  int32_t prot_cap[2];
+  uint64_t staging_offset, staging_bytes;     /* commit task tables (2 buffers)   */
+  uint64_t workspace_offset, workspace_bytes; /* attention split-K partials       */
+} kvq_layout;
+
+typedef struct kvq_cache kvq_cache;
+
+/* Bytes of device memory a cache with this configuration needs; 0 if the
+ * configuration is invalid or unsupported (see kvq_last_error). */
+size_t kvq_required_bytes(const kvq_config* cfg);
+
+/* Fills *out with the region offsets of a cache with this configuration. */
+kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out);
+
+/* Creates a handle over d_buf (device, >= kvq_required_bytes, 256-byte aligned,
+ * must outlive the handle).  Host-only: touches no device memory.  The cache
+ * starts empty; nothing in d_buf needs initialising. */
+kvq_status kvq_create(const kvq_config* cfg, void* d_buf, size_t buf_bytes, kvq_cache** out);
+
+/* Frees the host-side handle and its pinned staging ring.  Waits for the
+ * handle's outstanding staging copies.  NULL is accepted. */
+kvq_status kvq_destroy(kvq_cache* c);
+
+/* Quantize-on-commit.  Appends, for every sequence b, the first h_ntok[b]
+ * tokens of d_k / d_v (each [B, n_max, Hkv, D] contiguous, dtype in_dtype,
+ * 16-byte aligned) to segment `segment` as ceil(h_ntok[b] / 32) new slots.
+ * h_ntok: host [B], each in 0..n_max, or NULL for n_max everywhere.
+ * Protected rows: host CSR h_prot_off [B+1] (h_prot_off[0] == 0, non-decreasing)
+ * and h_prot_idx, positions relative to this commit's first token, strictly
+ * increasing within each sequence and < h_ntok[b]; both NULL for none.
+ * reset_segment != 0 first empties the segment for every sequence (used to
+ * replace the dual cache's suffix wholesale).
+ * Errors: KVQ_EINVAL for malformed arguments, KVQ_ECAPACITY if a sequence would
+ * exceed slot or protected capacity; the cache is unchanged in both cases. */
+kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment,
+                      const void* d_k, const void* d_v, int32_t in_dtype, int32_t n_max,
+                      const int32_t* h_ntok, const int32_t* h_prot_off, const int32_t* h_prot_idx,
+                      void* stream);
+
+/* Fused dequantize-and-attend of the current block.
+ * d_q [B, L, Hq, D], d_k_blk / d_v_blk [B, L, Hkv, D] (dtype blk_dtype),
+ * d_out [B, L, Hq, D] (dtype out_dtype), all contiguous and 16-byte aligned;
+ * L must be 32; Hq % Hkv == 0, Hq <= max_q_heads.  Query head hq uses kv head
+ * hq / (Hq / Hkv).  Every query token attends, without a mask, to all L block
+ * tokens, every valid prefix token and, if use_suffix != 0, every valid suffix
+ * token; a protected prefix/suffix key is its stored bf16 row.  Scores are
+ * q.k * softmax_scale.  MFMA operands are fp16, accumulation fp32.
+ * Inputs must be finite with |x| < 65504 (the fp16 operand range). */
+kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix,
+                          const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                          const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                          int32_t block_len, float softmax_scale,
+                          void* d_out, int32_t out_dtype, void* stream);
+
+/* Host mirror of a segment's lengths: any of the [B] arrays may be NULL. */
+kvq_status kvq_segment_info(const kvq_cache* c, int32_t segment,
+                            int32_t* h_ntok, int32_t* h_nslots, int32_t* h_nprot);
+
+/* Attention work split: slots per split-K chunk (0 = automatic). */
+kvq_status kvq_set_split_slots(kvq_cache* c, int32_t slots_per_split);
+
+const char* kvq_status_str(kvq_status s);
+const char* kvq_last_error(void);
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */
