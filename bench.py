@@ -1,0 +1,213 @@
+"""Throughput of the low-bit block-diffusion KV cache hot path on one MI355X.
+
+One step = one denoising step of one layer for a whole batch, as a
+block-diffusion decoder runs it once per block (SoloQ summary page,
+block-diffusion paragraph; Tai et al., abstract):
+    1. kvq_commit   quantize and append the previously finished 32-token block
+                    (3 of its key rows kept in bf16),
+    2. kvq_block_attn  the current 32-token block attends to itself and to the
+                    whole quantized prefix cache.
+Steps rotate over a stack of per-layer caches (28 layers, as in a Dream-7B
+model) so that every call reads its cache from HBM rather than from the
+256 MB Infinity Cache.
+
+Prints one JSON line; ``value`` is query tokens per second over the timed
+steps (B * 32 query tokens per step).  Inputs are seeded synthetic tensors with
+the layer shapes (no weights or datasets are used).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+
+def attn_algorithmic(cfg, ntok_per_seq, nslots_per_seq, nprot_per_seq, record_bytes):
+    """Bytes the method must move and flops it must do for one attention call."""
+    B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
+    act = 2 if cfg.dtype == "bf16" else 4
+    cache = sum(nslots_per_seq) * Hkv * record_bytes + sum(nslots_per_seq) * 16 \
+        + sum(nprot_per_seq) * (Hkv * D * 2 + 4)
+    io = B * 32 * Hq * D * act * 2 + B * 32 * Hkv * D * act * 2    # q, out, k_blk, v_blk
+    flops = sum(4.0 * Hq * 32 * (n + 32) * D for n in ntok_per_seq)
+    return cache + io, flops
+
+
+def commit_algorithmic(cfg, ntok, nprot, record_bytes):
+    Hkv, D = cfg.Hkv, cfg.D
+    act = 2 if cfg.dtype == "bf16" else 4
+    slots = sum(-(-n // 32) for n in ntok)
+    return sum(ntok) * Hkv * D * act * 2 + slots * (Hkv * record_bytes + 16) + nprot * (Hkv * D * 2 + 4)
+
+
+def cpu_baseline(cfg, w, steps_blocks, budget_s=20.0):
+    """The oracle (NumPy, fp32 quantization + fp64 attention) on a bounded sample:
+    sequence 0 only, all kv heads, full prefix: commit one block, then attention
+    of its 32 query tokens for every query head."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    c = cfg
+    ora = O.OracleCache(1, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group)
+    ora.commit(0, w.k_prefix[:1], w.v_prefix[:1], ntok=w.lengths[:1],
+               prot=[w.prot_prefix[0]] if c.prot_frac else None)
+    n_done, t_total = 0, 0.0
+    while t_total < budget_s and n_done < 500:
+        kb, vb, prot = steps_blocks[n_done % len(steps_blocks)]
+        t0 = time.perf_counter()
+        ora.commit(0, kb[:1], vb[:1], prot=[prot[0]] if c.step_protect else None)
+        O.block_attention(ora, w.q[:1], w.k_blk[:1], w.v_blk[:1])
+        t_total += time.perf_counter() - t0
+        n_done += 1
+    qtok = 32 * n_done
+    return {"value": qtok / t_total, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_done} step(s) of sequence 0 of {c.B} (all {c.Hq} query heads, prefix "
+                      f"{int(w.lengths[0])} tokens): oracle commit of one 32-token block + fp64 attention; "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="dream7b_4bit", choices=sorted(W.CONFIGS))
+    ap.add_argument("--layers", type=int, default=28, help="per-layer caches the steps rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only: there is no multi-GPU path; "
+                                   "run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    from bit_kv_cache_kivi_amd import kvq
+
+    cfg = W.CONFIGS[args.config]
+    w = W.make(cfg)
+    c = cfg
+    L = args.layers
+    total_steps = args.steps + args.warmup
+    commits_per_layer = -(-total_steps // L)
+    nblk = 4
+    blocks = [W.step_block(c, s) for s in range(nblk)]
+
+    dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dt).cuda().contiguous()   # noqa: E731
+    kp, vp = to(w.k_prefix), to(w.v_prefix)
+    q, kblk, vblk = to(w.q), to(w.k_blk), to(w.v_blk)
+    dblocks = [(to(k), to(v), p) for k, v, p in blocks]
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+
+    max_prefix = int(w.lengths.max())
+    prot_cap = max(len(p) for p in w.prot_prefix) + c.step_protect * commits_per_layer + 8
+    caches = []
+    for _ in range(L):
+        cache = kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
+                            prefix_tokens=max_prefix + 32 * (commits_per_layer + 1),
+                            prefix_protected=prot_cap, max_q_heads=c.Hq)
+        cache.commit(kp, vp, ntok=w.lengths, protected=w.prot_prefix if c.prot_frac else None)
+        caches.append(cache)
+    del kp, vp
+    torch.cuda.synchronize()
+    R = caches[0].layout["record_bytes"]
+    stream = torch.cuda.current_stream()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    attn_bytes = attn_flops = commit_bytes = 0.0
+
+    def step(i, timed):
+        nonlocal attn_bytes, attn_flops, commit_bytes
+        cache = caches[i % L]
+        kb, vb, prot = dblocks[i % nblk]
+        if timed:
+            ev[i][0].record(stream)
+        cache.commit(kb, vb, protected=prot if c.step_protect else None)
+        if timed:
+            ev[i][1].record(stream)
+        cache.block_attn(q, kblk, vblk, out=out)
+        if timed:
+            ev[i][2].record(stream)
+            ntok, nslots, nprot = cache.segment_info(0)
+            bts, fl = attn_algorithmic(c, ntok, nslots, nprot, R)
+            attn_bytes += bts
+            attn_flops += fl
+            commit_bytes += commit_algorithmic(c, [32] * c.B, c.step_protect * c.B, R)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    commit_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_per_step = total_ms / args.steps
+    qtok = c.B * 32
+    attn_s = attn_ms * 1e-3
+    a_bytes = attn_bytes / args.steps
+    a_flops = attn_flops / args.steps
+    achieved_tflops = a_flops / attn_s / 1e12
+    res = {
+        "metric": "block-attn query-tokens/s + achieved HBM GB/s, 4-bit KV, Dream-7B shape",
+        "value": qtok / (ms_per_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D,
+                   "prefix_tokens": int(max_prefix), "block": 32, "k_bits": c.k_bits, "v_bits": c.v_bits,
+                   "v_group": c.v_group, "protected_frac": c.prot_frac, "layers_rotated": L,
+                   "parallelism": "none"},
+        "attn_ms": attn_ms,
+        "commit_ms": commit_ms,
+        "attn_query_tokens_per_s": qtok / attn_s,
+        "attn_hbm_gbs": a_bytes / attn_s / 1e9,
+        "attn_tflops": achieved_tflops,
+        "commit_gbs": commit_bytes / args.steps / (commit_ms * 1e-3) / 1e9,
+        "host_wall_ms_per_step": wall * 1e3 / args.steps,
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_F16_TFLOPS, "traffic": None,
+                     "kernel": "attention (attn_kernel + combine_kernel)",
+                     "hbm_frac": a_bytes / attn_s / 1e9 / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(c, w, blocks, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    for cache in caches:
+        cache.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,422 @@
+// Host side of the C ABI: configuration checks, buffer layout, host mirror of
+// segment lengths, commit task tables and kernel launches.  All argument checks
+// run before any device work, so a failing call leaves the cache unchanged.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvq_internal.h"
+
+using kvq::CommitTask;
+
+namespace {
+
+thread_local std::string g_err;
+
+kvq_status fail(kvq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255u) / 256u * 256u; }
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+kvq_status check_config(const kvq_config* c) {
+  if (!c) return fail(KVQ_EINVAL, "config is NULL");
+  if (c->batch < 1 || c->batch > KVQ_MAX_BATCH) return fail(KVQ_EINVAL, "batch %d outside 1..%d", c->batch, KVQ_MAX_BATCH);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 4096) return fail(KVQ_EINVAL, "num_kv_heads %d", c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(KVQ_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
+  if ((c->k_bits != 2 && c->k_bits != 4) || (c->v_bits != 2 && c->v_bits != 4))
+    return fail(KVQ_EUNSUPPORTED, "k_bits %d / v_bits %d (supported: 2, 4)", c->k_bits, c->v_bits);
+  if (c->k_group_tokens != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "k_group_tokens %d (supported: 32)", c->k_group_tokens);
+  const int gv = c->v_group_channels;
+  if ((gv != 32 && gv != 64 && gv != 128) || gv > c->head_dim)
+    return fail(KVQ_EUNSUPPORTED, "v_group_channels %d (supported: 32, 64, 128, <= head_dim)", gv);
+  if (c->prefix_slots < 1 || c->prefix_slots > 65535) return fail(KVQ_EINVAL, "prefix_slots %d outside 1..65535", c->prefix_slots);
+  if (c->suffix_slots < 0 || c->suffix_slots > 65535) return fail(KVQ_EINVAL, "suffix_slots %d outside 0..65535", c->suffix_slots);
+  if (c->prefix_protected < 0 || c->suffix_protected < 0) return fail(KVQ_EINVAL, "negative protected capacity");
+  if (c->prefix_protected > c->prefix_slots * kvq::kSlot || c->suffix_protected > c->suffix_slots * kvq::kSlot)
+    return fail(KVQ_EINVAL, "protected capacity exceeds the segment's token capacity");
+  if (c->max_q_heads < c->num_kv_heads || c->max_q_heads % c->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "max_q_heads %d must be a positive multiple of num_kv_heads %d", c->max_q_heads, c->num_kv_heads);
+  if (c->max_q_heads / c->num_kv_heads > 8)
+    return fail(KVQ_EUNSUPPORTED, "query heads per kv head %d (supported: <= 8)", c->max_q_heads / c->num_kv_heads);
+  if (c->max_splits < 0 || c->max_splits > 256) return fail(KVQ_EINVAL, "max_splits %d outside 0..256", c->max_splits);
+  return KVQ_OK;
+}
+
+void compute_layout(const kvq_config* c, kvq_layout* L) {
+  memset(L, 0, sizeof(*L));
+  const uint64_t B = c->batch, H = c->num_kv_heads, D = c->head_dim;
+  const uint64_t R = kvq::record_bytes((int)D, c->k_bits, c->v_bits, c->v_group_channels);
+  L->record_bytes = R;
+  L->kc_offset = 0;
+  L->vc_offset = kvq::kc_bytes((int)D, c->k_bits);
+  L->kmeta_offset = L->vc_offset + kvq::vc_bytes((int)D, c->v_bits);
+  L->vmeta_offset = L->kmeta_offset + kvq::kmeta_bytes((int)D);
+  uint64_t off = 0;
+  for (int s = 0; s < 2; ++s) {
+    const uint64_t cap = s == 0 ? c->prefix_slots : c->suffix_slots;
+    const uint64_t pcap = s == 0 ? c->prefix_protected : c->suffix_protected;
+    L->slot_cap[s] = (int32_t)cap;
+    L->prot_cap[s] = (int32_t)pcap;
+    L->records_offset[s] = off;   off += align256(B * H * cap * R);
+    L->headers_offset[s] = off;   off += align256(B * cap * kvq::kHeaderBytes);
+    L->prot_rows_offset[s] = off; off += align256(B * pcap * H * D * 2);
+    L->prot_pos_offset[s] = off;  off += align256(B * pcap * 4);
+  }
+  const uint64_t maxcap = c->prefix_slots > c->suffix_slots ? c->prefix_slots : c->suffix_slots;
+  L->staging_offset = off;
+  L->staging_bytes = align256(B * maxcap * sizeof(CommitTask));
+  off += 2 * L->staging_bytes;
+  const uint64_t splits = c->max_splits ? c->max_splits : 32;
+  const uint64_t rmax = c->max_q_heads / c->num_kv_heads;
+  L->workspace_offset = off;
+  L->workspace_bytes = align256(B * H * splits * rmax * (D + 2) * kvq::kSlot * 4);
+  off += L->workspace_bytes;
+  L->total_bytes = off;
+}
+
+struct SegMirror {
+  std::vector<int32_t> ntok, nslots, nprot;
+};
+
+}  // namespace
+
+struct kvq_cache {
+  kvq_config cfg;
+  kvq_layout lay;
+  uint8_t* dbuf;
+  SegMirror seg[2];
+  int32_t split_slots = 0;
+  // pinned staging ring (created on first device use)
+  bool hip_ready = false;
+  uint8_t* h_stage = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  bool ev_used[2] = {false, false};
+  int next_stage = 0;
+  std::vector<CommitTask> tasks;
+};
+
+namespace {
+
+kvq_status ensure_hip(kvq_cache* c) {
+  if (c->hip_ready) return KVQ_OK;
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), 2 * c->lay.staging_bytes, hipHostMallocDefault);
+  if (e != hipSuccess) { c->h_stage = nullptr; return fail(KVQ_EHIP, "hipHostMalloc: %s", hipGetErrorString(e)); }
+  for (int i = 0; i < 2; ++i) {
+    e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+  }
+  c->hip_ready = true;
+  return KVQ_OK;
+}
+
+kvq::SegPtrs seg_ptrs(const kvq_cache* c, int s) {
+  kvq::SegPtrs p;
+  p.records = c->dbuf + c->lay.records_offset[s];
+  p.headers = c->dbuf + c->lay.headers_offset[s];
+  p.prot_rows = reinterpret_cast<uint16_t*>(c->dbuf + c->lay.prot_rows_offset[s]);
+  p.prot_pos = reinterpret_cast<int32_t*>(c->dbuf + c->lay.prot_pos_offset[s]);
+  p.slot_cap = c->lay.slot_cap[s];
+  p.prot_cap = c->lay.prot_cap[s];
+  return p;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration";
+    case KVQ_ECAPACITY: return "capacity exceeded";
+    case KVQ_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+size_t kvq_required_bytes(const kvq_config* cfg) {
+  if (check_config(cfg) != KVQ_OK) return 0;
+  kvq_layout L;
+  compute_layout(cfg, &L);
+  return L.total_bytes;
+}
+
+kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if (!out) return fail(KVQ_EINVAL, "layout output is NULL");
+  compute_layout(cfg, out);
+  return KVQ_OK;
+}
+
+kvq_status kvq_create(const kvq_config* cfg, void* d_buf, size_t buf_bytes, kvq_cache** out) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if (!out) return fail(KVQ_EINVAL, "output handle pointer is NULL");
+  if (!d_buf) return fail(KVQ_EINVAL, "device buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(d_buf) & 255u) return fail(KVQ_EINVAL, "device buffer is not 256-byte aligned");
+  kvq_layout L;
+  compute_layout(cfg, &L);
+  if (buf_bytes < L.total_bytes)
+    return fail(KVQ_EINVAL, "device buffer has %zu bytes, %llu needed", buf_bytes, (unsigned long long)L.total_bytes);
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return fail(KVQ_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->lay = L;
+  c->dbuf = static_cast<uint8_t*>(d_buf);
+  for (int i = 0; i < 2; ++i) {
+    c->seg[i].ntok.assign(cfg->batch, 0);
+    c->seg[i].nslots.assign(cfg->batch, 0);
+    c->seg[i].nprot.assign(cfg->batch, 0);
+  }
+  *out = c;
+  return KVQ_OK;
+}
+
+kvq_status kvq_destroy(kvq_cache* c) {
+  if (!c) return KVQ_OK;
+  if (c->hip_ready) {
+    for (int i = 0; i < 2; ++i) {
+      if (c->ev[i]) {
+        if (c->ev_used[i]) hipEventSynchronize(c->ev[i]);
+        hipEventDestroy(c->ev[i]);
+      }
+    }
+    if (c->h_stage) hipHostFree(c->h_stage);
+  }
+  delete c;
+  return KVQ_OK;
+}
+
+kvq_status kvq_segment_info(const kvq_cache* c, int32_t segment, int32_t* h_ntok, int32_t* h_nslots,
+                            int32_t* h_nprot) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  if (segment != KVQ_PREFIX && segment != KVQ_SUFFIX) return fail(KVQ_EINVAL, "segment %d", segment);
+  const SegMirror& m = c->seg[segment];
+  const size_t n = (size_t)c->cfg.batch * sizeof(int32_t);
+  if (h_ntok) memcpy(h_ntok, m.ntok.data(), n);
+  if (h_nslots) memcpy(h_nslots, m.nslots.data(), n);
+  if (h_nprot) memcpy(h_nprot, m.nprot.data(), n);
+  return KVQ_OK;
+}
+
+kvq_status kvq_set_split_slots(kvq_cache* c, int32_t slots_per_split) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  if (slots_per_split < 0) return fail(KVQ_EINVAL, "slots_per_split %d", slots_per_split);
+  c->split_slots = slots_per_split;
+  return KVQ_OK;
+}
+
+kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, const void* d_k, const void* d_v,
+                      int32_t in_dtype, int32_t n_max, const int32_t* h_ntok, const int32_t* h_prot_off,
+                      const int32_t* h_prot_idx, void* stream) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  const kvq_config& cfg = c->cfg;
+  const int B = cfg.batch;
+  if (segment != KVQ_PREFIX && segment != KVQ_SUFFIX) return fail(KVQ_EINVAL, "segment %d", segment);
+  if (segment == KVQ_SUFFIX && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
+  if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return fail(KVQ_EINVAL, "in_dtype %d", in_dtype);
+  if (n_max < 0) return fail(KVQ_EINVAL, "n_max %d", n_max);
+  if (h_prot_idx && !h_prot_off) return fail(KVQ_EINVAL, "protected index list given without offsets");
+  std::vector<int32_t> ntok(B);
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    ntok[b] = h_ntok ? h_ntok[b] : n_max;
+    if (ntok[b] < 0 || ntok[b] > n_max) return fail(KVQ_EINVAL, "h_ntok[%d] = %d outside 0..%d", b, ntok[b], n_max);
+    total += ntok[b];
+  }
+  if (total > 0) {
+    if (!d_k || !d_v) return fail(KVQ_EINVAL, "k or v is NULL");
+    if (!aligned16(d_k) || !aligned16(d_v)) return fail(KVQ_EINVAL, "k and v must be 16-byte aligned");
+  }
+  if (h_prot_off) {
+    if (h_prot_off[0] != 0) return fail(KVQ_EINVAL, "h_prot_off[0] must be 0");
+    for (int b = 0; b < B; ++b) {
+      if (h_prot_off[b + 1] < h_prot_off[b]) return fail(KVQ_EINVAL, "h_prot_off decreases at %d", b);
+      if (h_prot_off[b + 1] > h_prot_off[b] && !h_prot_idx) return fail(KVQ_EINVAL, "h_prot_idx is NULL");
+      for (int i = h_prot_off[b]; i < h_prot_off[b + 1]; ++i) {
+        const int p = h_prot_idx[i];
+        if (p < 0 || p >= ntok[b]) return fail(KVQ_EINVAL, "protected position %d of sequence %d outside 0..%d", p, b, ntok[b] - 1);
+        if (i > h_prot_off[b] && p <= h_prot_idx[i - 1])
+          return fail(KVQ_EINVAL, "protected positions of sequence %d are not strictly increasing", b);
+      }
+    }
+  }
+  SegMirror& m = c->seg[segment];
+  const int cap = c->lay.slot_cap[segment], pcap = c->lay.prot_cap[segment];
+  for (int b = 0; b < B; ++b) {
+    const int base_slots = reset_segment ? 0 : m.nslots[b];
+    const int base_prot = reset_segment ? 0 : m.nprot[b];
+    const int add_slots = (ntok[b] + kvq::kSlot - 1) / kvq::kSlot;
+    const int add_prot = h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
+    if (base_slots + add_slots > cap)
+      return fail(KVQ_ECAPACITY, "sequence %d needs %d slots, segment capacity is %d", b, base_slots + add_slots, cap);
+    if (base_prot + add_prot > pcap)
+      return fail(KVQ_ECAPACITY, "sequence %d needs %d protected rows, capacity is %d", b, base_prot + add_prot, pcap);
+  }
+
+  // ---- task table
+  auto& tasks = c->tasks;
+  tasks.clear();
+  for (int b = 0; b < B; ++b) {
+    const int base_slots = reset_segment ? 0 : m.nslots[b];
+    int rank = reset_segment ? 0 : m.nprot[b];
+    const int tok0 = reset_segment ? 0 : m.ntok[b];
+    const int* pidx = h_prot_off ? h_prot_idx + h_prot_off[b] : nullptr;
+    const int np = h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
+    int pi = 0;
+    for (int j = 0; j * kvq::kSlot < ntok[b]; ++j) {
+      CommitTask t;
+      t.b = b;
+      t.dst_slot = base_slots + j;
+      t.src_tok = j * kvq::kSlot;
+      t.nvalid = std::min(kvq::kSlot, ntok[b] - t.src_tok);
+      t.mask = 0;
+      t.rank_base = rank;
+      t.token_base = tok0 + t.src_tok;
+      t.pad = 0;
+      while (pi < np && pidx[pi] < t.src_tok + t.nvalid) {
+        t.mask |= 1u << (pidx[pi] - t.src_tok);
+        ++pi;
+        ++rank;
+      }
+      tasks.push_back(t);
+    }
+  }
+
+  if (!tasks.empty()) {
+    kvq_status s = ensure_hip(c);
+    if (s != KVQ_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int k = c->next_stage;
+    if (c->ev_used[k]) {
+      hipError_t e = hipEventSynchronize(c->ev[k]);
+      if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    }
+    const size_t bytes = tasks.size() * sizeof(CommitTask);
+    uint8_t* hs = c->h_stage + k * c->lay.staging_bytes;
+    uint8_t* ds = c->dbuf + c->lay.staging_offset + k * c->lay.staging_bytes;
+    memcpy(hs, tasks.data(), bytes);
+    hipError_t e = hipMemcpyAsync(ds, hs, bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    e = hipEventRecord(c->ev[k], st);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+    c->ev_used[k] = true;
+    c->next_stage = k ^ 1;
+    kvq::CommitArgs a;
+    a.k = d_k;
+    a.v = d_v;
+    a.tasks = reinterpret_cast<const CommitTask*>(ds);
+    a.seg = seg_ptrs(c, segment);
+    a.n_max = n_max;
+    a.hkv = cfg.num_kv_heads;
+    a.gv_log2 = ilog2(cfg.v_group_channels);
+    a.record_bytes = (uint32_t)c->lay.record_bytes;
+    e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "commit launch: %s", hipGetErrorString(e));
+  }
+
+  // ---- host mirror
+  for (int b = 0; b < B; ++b) {
+    if (reset_segment) { m.ntok[b] = 0; m.nslots[b] = 0; m.nprot[b] = 0; }
+    m.ntok[b] += ntok[b];
+    m.nslots[b] += (ntok[b] + kvq::kSlot - 1) / kvq::kSlot;
+    m.nprot[b] += h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                          const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
+                          float softmax_scale, void* d_out, int32_t out_dtype, void* stream) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  const kvq_config& cfg = c->cfg;
+  const int B = cfg.batch, H = cfg.num_kv_heads;
+  if (use_suffix && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
+  if (block_len != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "block_len %d (supported: 32)", block_len);
+  if (num_q_heads < H || num_q_heads % H != 0 || num_q_heads > cfg.max_q_heads)
+    return fail(KVQ_EINVAL, "num_q_heads %d must be a multiple of %d and <= %d", num_q_heads, H, cfg.max_q_heads);
+  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (blk_dtype != KVQ_F32 && blk_dtype != KVQ_BF16) ||
+      (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
+    return fail(KVQ_EINVAL, "dtype must be KVQ_F32 or KVQ_BF16");
+  if (!d_q || !d_k_blk || !d_v_blk || !d_out) return fail(KVQ_EINVAL, "q, k_blk, v_blk and out must be non-NULL");
+  if (!aligned16(d_q) || !aligned16(d_k_blk) || !aligned16(d_v_blk) || !aligned16(d_out))
+    return fail(KVQ_EINVAL, "q, k_blk, v_blk and out must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
+
+  const int max_splits = cfg.max_splits ? cfg.max_splits : 32;
+  int max_units = 0;
+  int64_t total_units = 0;
+  kvq::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int b = 0; b < B; ++b) {
+    const int np = c->seg[0].nslots[b], ns = use_suffix ? c->seg[1].nslots[b] : 0;
+    a.nslots[0][b] = (uint16_t)np;
+    a.nslots[1][b] = (uint16_t)(use_suffix ? ns : 0);
+    const int U = np + ns + 1;
+    max_units = std::max(max_units, U);
+    total_units += U;
+  }
+  int split_units;
+  if (c->split_slots > 0) {
+    split_units = c->split_slots;
+  } else {
+    // aim for about two workgroups per compute unit over the whole grid
+    const int64_t target = 512;
+    const int64_t pairs_units = total_units * H;
+    split_units = (int)std::max<int64_t>(8, (pairs_units + target - 1) / target);
+  }
+  split_units = std::max(split_units, (max_units + max_splits - 1) / max_splits);
+  const int grid_splits = (max_units + split_units - 1) / split_units;
+
+  a.q = d_q;
+  a.k_blk = d_k_blk;
+  a.v_blk = d_v_blk;
+  a.out = d_out;
+  a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
+  a.seg[0] = seg_ptrs(c, 0);
+  a.seg[1] = seg_ptrs(c, 1);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.hq = num_q_heads;
+  a.hkv = H;
+  a.r = num_q_heads / H;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.blk_f32 = blk_dtype == KVQ_F32;
+  a.out_f32 = out_dtype == KVQ_F32;
+  a.gv_log2 = ilog2(cfg.v_group_channels);
+  a.record_bytes = (uint32_t)c->lay.record_bytes;
+  a.split_units = split_units;
+  a.max_splits = max_splits;
+  a.use_suffix = use_suffix ? 1 : 0;
+  hipError_t e = kvq::launch_attention(a, grid_splits, B, cfg.head_dim, cfg.k_bits, cfg.v_bits,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "attention launch: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // extern "C"

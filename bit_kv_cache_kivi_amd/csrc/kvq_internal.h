@@ -1,0 +1,80 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kSlot = 32;         // tokens per slot = K group = block length
+constexpr int kHeaderBytes = 16;  // slot header
+
+// One new slot of a commit: tokens [src_tok, src_tok + nvalid) of sequence b.
+struct CommitTask {
+  int32_t b;
+  int32_t dst_slot;    // slot index inside the segment
+  int32_t src_tok;     // first token row in the commit's input
+  int32_t nvalid;      // 1..32
+  uint32_t mask;       // protected tokens of the slot
+  int32_t rank_base;   // rank of its first protected row
+  int32_t token_base;  // segment position of its first token
+  int32_t pad;
+};
+static_assert(sizeof(CommitTask) == 32, "task layout");
+
+struct SegPtrs {
+  uint8_t* records;     // [B][Hkv][slot_cap] records
+  uint8_t* headers;     // [B][slot_cap] 16-byte headers
+  uint16_t* prot_rows;  // [B][prot_cap][Hkv][D] bf16 bits
+  int32_t* prot_pos;    // [B][prot_cap]
+  int32_t slot_cap;
+  int32_t prot_cap;
+};
+
+struct CommitArgs {
+  const void* k;        // [B, n_max, Hkv, D]
+  const void* v;
+  const CommitTask* tasks;
+  SegPtrs seg;
+  int32_t n_max;
+  int32_t hkv;
+  int32_t gv_log2;
+  uint32_t record_bytes;
+};
+
+struct AttnArgs {
+  const void* q;        // [B, 32, Hq, D]
+  const void* k_blk;    // [B, 32, Hkv, D]
+  const void* v_blk;
+  void* out;            // [B, 32, Hq, D]
+  float* partial;       // split-K partials
+  SegPtrs seg[2];
+  float scale_log2;     // softmax_scale * log2(e)
+  int32_t hq, hkv, r;
+  int32_t q_f32, blk_f32, out_f32;
+  int32_t gv_log2;
+  uint32_t record_bytes;
+  int32_t split_units;  // units (slots + block) per split
+  int32_t max_splits;
+  int32_t use_suffix;
+  uint16_t nslots[2][KVQ_MAX_BATCH];   // per-sequence slot counts of both segments
+};
+
+// Record field offsets for (D, kb, vb, G_v): see include/kvq.h.
+__host__ __device__ constexpr uint32_t kc_bytes(int D, int kb) { return kSlot * D * kb / 8; }
+__host__ __device__ constexpr uint32_t vc_bytes(int D, int vb) { return D * vb * 4; }
+__host__ __device__ constexpr uint32_t kmeta_bytes(int D) { return 2 * D * 4; }
+__host__ __device__ constexpr uint32_t vmeta_bytes(int D, int gv) { return (D / gv) * 2 * kSlot * 4; }
+__host__ __device__ constexpr uint32_t record_bytes(int D, int kb, int vb, int gv) {
+  return (kc_bytes(D, kb) + vc_bytes(D, vb) + kmeta_bytes(D) + vmeta_bytes(D, gv) + 255u) / 256u * 256u;
+}
+
+// Launchers (defined in the .hip files); return the launch status.
+hipError_t launch_commit(const CommitArgs& a, int ntasks, int D, int kb, int vb, bool f32_in,
+                         hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
+                            hipStream_t stream);
+
+}  // namespace kvq

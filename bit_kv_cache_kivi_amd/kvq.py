@@ -1,0 +1,235 @@
+"""Python binding of the kvq C ABI (include/kvq.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libkvq.so.  PyTorch supplies device memory (the cache buffer, inputs, outputs)
+and the current stream.  Importing this module loads libkvq.so and raises if it
+has not been built; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, byref, c_char_p, c_float, c_int32, c_size_t, c_uint64, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EHIP = range(5)
+KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_PREFIX, KVQ_SUFFIX = 0, 1
+SLOT = 32
+
+
+class KvqConfig(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in (
+        "batch", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group_tokens",
+        "v_group_channels", "prefix_slots", "suffix_slots", "prefix_protected",
+        "suffix_protected", "max_q_heads", "max_splits")]
+
+
+class KvqLayout(ctypes.Structure):
+    _fields_ = [
+        ("total_bytes", c_uint64), ("record_bytes", c_uint64),
+        ("kc_offset", c_uint64), ("vc_offset", c_uint64), ("kmeta_offset", c_uint64),
+        ("vmeta_offset", c_uint64),
+        ("records_offset", c_uint64 * 2), ("headers_offset", c_uint64 * 2),
+        ("prot_rows_offset", c_uint64 * 2), ("prot_pos_offset", c_uint64 * 2),
+        ("slot_cap", c_int32 * 2), ("prot_cap", c_int32 * 2),
+        ("staging_offset", c_uint64), ("staging_bytes", c_uint64),
+        ("workspace_offset", c_uint64), ("workspace_bytes", c_uint64),
+    ]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"kvq status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                          " (or python bit_kv_cache_kivi_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = POINTER
+    sig = {
+        "kvq_required_bytes": (c_size_t, [P(KvqConfig)]),
+        "kvq_get_layout": (c_int32, [P(KvqConfig), P(KvqLayout)]),
+        "kvq_create": (c_int32, [P(KvqConfig), c_void_p, c_size_t, P(c_void_p)]),
+        "kvq_destroy": (c_int32, [c_void_p]),
+        "kvq_commit": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                 P(c_int32), P(c_int32), P(c_int32), c_void_p]),
+        "kvq_block_attn": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                     c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
+        "kvq_segment_info": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_int32)]),
+        "kvq_set_split_slots": (c_int32, [c_void_p, c_int32]),
+        "kvq_status_str": (c_char_p, [c_int32]),
+        "kvq_last_error": (c_char_p, []),
+        "kvq_abi_version": (c_int32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.kvq_last_error().decode()
+
+
+def check(status: int):
+    if status != KVQ_OK:
+        raise KvqError(status, f"{lib.kvq_status_str(status).decode()}: {last_error()}")
+
+
+def _int_array(vals):
+    if vals is None:
+        return None
+    arr = (c_int32 * len(vals))(*[int(x) for x in vals])
+    return arr
+
+
+def make_config(batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128, prefix_slots=1,
+                suffix_slots=0, prefix_protected=0, suffix_protected=0, max_q_heads=None, max_splits=0):
+    return KvqConfig(batch, num_kv_heads, head_dim, k_bits, v_bits, SLOT, v_group, prefix_slots,
+                     suffix_slots, prefix_protected, suffix_protected,
+                     max_q_heads if max_q_heads is not None else num_kv_heads, max_splits)
+
+
+def get_layout(cfg: KvqConfig) -> dict:
+    lay = KvqLayout()
+    check(lib.kvq_get_layout(byref(cfg), byref(lay)))
+    out = {}
+    for name, _ in KvqLayout._fields_:
+        v = getattr(lay, name)
+        out[name] = list(v) if hasattr(v, "__len__") else int(v)
+    return out
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    if t.dtype == torch.bfloat16:
+        return KVQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void_p(s.cuda_stream)
+
+
+class KVCache:
+    """One layer's low-bit cache in a torch-owned device buffer."""
+
+    def __init__(self, batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128,
+                 prefix_tokens=32, suffix_tokens=0, prefix_protected=0, suffix_protected=0,
+                 max_q_heads=None, max_splits=0, device="cuda"):
+        import torch
+        self.cfg = make_config(batch, num_kv_heads, head_dim, k_bits, v_bits, v_group,
+                               -(-prefix_tokens // SLOT), -(-suffix_tokens // SLOT),
+                               prefix_protected, suffix_protected, max_q_heads, max_splits)
+        self.layout = get_layout(self.cfg)
+        nbytes = self.layout["total_bytes"]
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = c_void_p()
+        check(lib.kvq_create(byref(self.cfg), c_void_p(self.buffer.data_ptr()), nbytes, byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h:
+            check(lib.kvq_destroy(self._h))
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def commit(self, k, v, ntok=None, protected=None, segment=KVQ_PREFIX, reset=False, stream=None):
+        """k, v: [B, n_max, Hkv, D] (fp32 or bf16, contiguous, on the device).
+
+        ntok: per-sequence token counts (default n_max); protected: per-sequence
+        sorted positions, relative to this commit, of key rows kept in bf16."""
+        assert k.is_contiguous() and v.is_contiguous() and k.dtype == v.dtype and k.shape == v.shape
+        B = self.cfg.batch
+        nt = _int_array(ntok)
+        off = idx = None
+        if protected is not None:
+            o = [0]
+            flat = []
+            for p in protected:
+                p = [int(x) for x in p]
+                flat.extend(p)
+                o.append(len(flat))
+            off = _int_array(o)
+            idx = _int_array(flat) if flat else (c_int32 * 1)(0)
+        check(lib.kvq_commit(self._h, int(segment), int(bool(reset)), c_void_p(k.data_ptr()),
+                             c_void_p(v.data_ptr()), _dtype_code(k), int(k.shape[1]), nt, off, idx,
+                             _stream_ptr(stream)))
+
+    def block_attn(self, q, k_blk, v_blk, use_suffix=False, softmax_scale=None, out_dtype=None,
+                   out=None, stream=None):
+        """q [B, 32, Hq, D]; k_blk, v_blk [B, 32, Hkv, D].  Returns out [B, 32, Hq, D]."""
+        import torch
+        assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
+        assert k_blk.dtype == v_blk.dtype
+        D = self.cfg.head_dim
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
+        check(lib.kvq_block_attn(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
+                                 _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
+                                 _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
+                                 c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
+        return out
+
+    def segment_info(self, segment=KVQ_PREFIX):
+        B = self.cfg.batch
+        a, b_, c = (c_int32 * B)(), (c_int32 * B)(), (c_int32 * B)()
+        check(lib.kvq_segment_info(self._h, int(segment), a, b_, c))
+        return list(a), list(b_), list(c)
+
+    def set_split_slots(self, n: int):
+        check(lib.kvq_set_split_slots(self._h, int(n)))
+
+    # ---- raw views of the buffer (for inspection and tests)
+    def records(self, segment, b):
+        """uint8 tensor [nslots, Hkv, record_bytes] of sequence b's slots."""
+        L = self.layout
+        H, cap, R = self.cfg.num_kv_heads, L["slot_cap"][segment], L["record_bytes"]
+        n = self.segment_info(segment)[1][b]
+        base = L["records_offset"][segment] + b * H * cap * R
+        return self.buffer[base:base + H * cap * R].view(H, cap, R)[:, :n].permute(1, 0, 2)
+
+    def headers(self, segment, b):
+        L = self.layout
+        cap = L["slot_cap"][segment]
+        n = self.segment_info(segment)[1][b]
+        base = L["headers_offset"][segment] + b * cap * 16
+        return self.buffer[base:base + n * 16].view(n, 16)
+
+    def protected_rows(self, segment, b):
+        """(positions int32 [nprot], bf16 bits int16 [nprot, Hkv, D])."""
+        import torch
+        L = self.layout
+        H, D, pcap = self.cfg.num_kv_heads, self.cfg.head_dim, L["prot_cap"][segment]
+        n = self.segment_info(segment)[2][b]
+        rb = L["prot_rows_offset"][segment] + b * pcap * H * D * 2
+        pb = L["prot_pos_offset"][segment] + b * pcap * 4
+        rows = self.buffer[rb:rb + n * H * D * 2].view(torch.int16).view(n, H, D)
+        pos = self.buffer[pb:pb + n * 4].view(torch.int32)
+        return pos, rows

@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and exports
+every symbol include/kvq.h declares, the layout matches the documented record
+format, and malformed calls fail with the right status before any device work
+(leaving the host mirror unchanged)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SO = os.path.join(ROOT, "bit_kv_cache_kivi_amd", "libkvq.so")
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    if not os.path.exists(SO):
+        from bit_kv_cache_kivi_amd import build
+        build.build()
+    from bit_kv_cache_kivi_amd import kvq as m
+    return m
+
+
+def header_symbols():
+    txt = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(kvq):
+    syms = header_symbols()
+    assert {"kvq_create", "kvq_destroy", "kvq_commit", "kvq_block_attn"} <= set(syms)
+    lib = ctypes.CDLL(SO)
+    for s in syms:
+        assert hasattr(lib, s), f"{s} not exported"
+    assert kvq.lib.kvq_abi_version() == 1
+
+
+def test_layout_matches_documented_record(kvq):
+    import oracle
+    for (D, kb, vb, gv) in [(128, 4, 4, 64), (128, 2, 2, 64), (128, 4, 4, 128), (64, 4, 4, 64), (64, 2, 4, 32)]:
+        cfg = kvq.make_config(3, 2, D, kb, vb, gv, prefix_slots=10, suffix_slots=4, prefix_protected=7,
+                              suffix_protected=3, max_q_heads=6)
+        L = kvq.get_layout(cfg)
+        ref = oracle.record_layout(D, kb, vb, gv)
+        for k in ("record_bytes", "kc_offset", "vc_offset", "kmeta_offset", "vmeta_offset"):
+            assert L[k] == ref[k], (k, L[k], ref[k])
+        assert L["slot_cap"] == [10, 4] and L["prot_cap"] == [7, 3]
+        regions = []
+        for s in range(2):
+            regions += [(L["records_offset"][s], 3 * 2 * L["slot_cap"][s] * L["record_bytes"]),
+                        (L["headers_offset"][s], 3 * L["slot_cap"][s] * 16),
+                        (L["prot_rows_offset"][s], 3 * L["prot_cap"][s] * 2 * D * 2),
+                        (L["prot_pos_offset"][s], 3 * L["prot_cap"][s] * 4)]
+        regions += [(L["staging_offset"], 2 * L["staging_bytes"]), (L["workspace_offset"], L["workspace_bytes"])]
+        regions.sort()
+        for (o1, n1), (o2, _) in zip(regions, regions[1:]):
+            assert o1 % 256 == 0 and o1 + n1 <= o2
+        assert regions[-1][0] + regions[-1][1] <= L["total_bytes"] == kvq.lib.kvq_required_bytes(ctypes.byref(cfg))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, 1), ("batch", 257, 1), ("head_dim", 96, 2), ("k_bits", 3, 2), ("v_bits", 8, 2),
+    ("k_group_tokens", 64, 2), ("v_group_channels", 48, 2), ("v_group_channels", 256, 2),
+    ("prefix_slots", 0, 1), ("suffix_slots", -1, 1), ("max_q_heads", 3, 1), ("max_q_heads", 36, 2),
+    ("max_splits", 1000, 1), ("prefix_protected", -1, 1)])
+def test_bad_configs(kvq, field, value, status):
+    cfg = kvq.make_config(2, 4, 128, 4, 4, 64, prefix_slots=8, max_q_heads=8)
+    setattr(cfg, field, value)
+    assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0
+    h = ctypes.c_void_p()
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), 1 << 40, ctypes.byref(h)) == status
+    assert kvq.last_error()
+
+
+def _handle(kvq, **kw):
+    cfg = kvq.make_config(2, 2, 64, 4, 4, 64, prefix_slots=3, suffix_slots=1, prefix_protected=4,
+                          max_q_heads=4, **kw)
+    n = kvq.lib.kvq_required_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 32)          # never dereferenced: every call below fails validation
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), fake, n, ctypes.byref(h)) == 0
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), ctypes.c_void_p((1 << 32) + 16), n, ctypes.byref(h)) == 1
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), fake, n - 1, ctypes.byref(h)) == 1
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), fake, n, ctypes.byref(h)) == 0
+    return h
+
+
+def test_commit_validation_leaves_cache_unchanged(kvq):
+    h = _handle(kvq)
+    I = lambda *v: (ctypes.c_int32 * len(v))(*v)   # noqa: E731
+    k = ctypes.c_void_p(1 << 33)
+    before = [(ctypes.c_int32 * 2)() for _ in range(3)]
+    kvq.lib.kvq_segment_info(h, 0, *before)
+    cases = [
+        (dict(seg=2), 1), (dict(dtype=5), 1), (dict(n_max=-1), 1),
+        (dict(ntok=I(5, 41)), 1),                             # ntok > n_max
+        (dict(ntok=I(-1, 3)), 1),
+        (dict(n_max=100), 3),                                 # 4 slots > capacity 3
+        (dict(off=I(0, 2, 2), idx=I(3, 3)), 1),               # duplicate position
+        (dict(off=I(0, 2, 2), idx=I(5, 3)), 1),               # not increasing
+        (dict(off=I(0, 1, 1), idx=I(40)), 1),                 # position >= ntok
+        (dict(off=I(1, 1, 1), idx=I(0)), 1),                  # offsets must start at 0
+        (dict(off=I(0, 5, 5), idx=I(0, 1, 2, 3, 4)), 3),      # 5 rows > protected capacity 4
+        (dict(off=None, idx=I(1)), 1),
+        (dict(kptr=ctypes.c_void_p((1 << 33) + 8)), 1),       # misaligned input
+        (dict(kptr=None), 1),
+    ]
+    for kw, status in cases:
+        st = kvq.lib.kvq_commit(h, kw.get("seg", 0), 0, kw.get("kptr", k), k, kw.get("dtype", 1),
+                                kw.get("n_max", 40), kw.get("ntok"), kw.get("off"), kw.get("idx"), None)
+        assert st == status, (kw, st, kvq.last_error())
+        after = [(ctypes.c_int32 * 2)() for _ in range(3)]
+        kvq.lib.kvq_segment_info(h, 0, *after)
+        assert [list(a) for a in after] == [list(b) for b in before]
+    # the suffix segment of a cache without one
+    cfg = kvq.make_config(1, 1, 64, 4, 4, 64, prefix_slots=2)
+    h2 = ctypes.c_void_p()
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 32), 1 << 30, ctypes.byref(h2)) == 0
+    assert kvq.lib.kvq_commit(h2, 1, 0, k, k, 1, 32, None, None, None, None) == 1
+    # a commit of zero tokens is a no-op that needs no device work
+    assert kvq.lib.kvq_commit(h2, 0, 0, None, None, 1, 0, None, None, None, None) == 0
+    assert kvq.lib.kvq_destroy(h2) == 0
+    assert kvq.lib.kvq_destroy(h) == 0
+    assert kvq.lib.kvq_destroy(None) == 0
+
+
+def test_attention_validation(kvq):
+    h = _handle(kvq)
+    p = ctypes.c_void_p(1 << 33)
+    ok = dict(suf=0, q=p, hq=4, qd=1, kb=p, vb=p, bd=1, L=32, scale=0.125, out=p, od=1)
+    cases = [(dict(hq=3), 1), (dict(hq=6), 1), (dict(L=16), 2), (dict(qd=7), 1), (dict(od=2), 1),
+             (dict(q=None), 1), (dict(out=ctypes.c_void_p((1 << 33) + 4)), 1), (dict(scale=float("nan")), 1),
+             (dict(scale=-1.0), 1)]
+    for kw, status in cases:
+        a = dict(ok, **kw)
+        st = kvq.lib.kvq_block_attn(h, a["suf"], a["q"], a["hq"], a["qd"], a["kb"], a["vb"], a["bd"], a["L"],
+                                    a["scale"], a["out"], a["od"], None)
+        assert st == status, (kw, st, kvq.last_error())
+    cfg = kvq.make_config(1, 1, 64, 4, 4, 64, prefix_slots=2)
+    h2 = ctypes.c_void_p()
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 32), 1 << 30, ctypes.byref(h2)) == 0
+    assert kvq.lib.kvq_block_attn(h2, 1, p, 1, 1, p, p, 1, 32, 0.1, p, 1, None) == 1   # no suffix segment
+    kvq.lib.kvq_destroy(h2)
+    kvq.lib.kvq_destroy(h)
+
+
+def test_status_strings(kvq):
+    for s in range(5):
+        assert kvq.lib.kvq_status_str(s)
+    assert kvq.lib.kvq_status_str(99) == b"unknown status"

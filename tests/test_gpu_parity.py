@@ -1,0 +1,185 @@
+"""GPU-vs-oracle parity through the C ABI (needs an MI355X).
+
+Commit: every byte of every slot record (codes, scales, zeros), slot header and
+protected bf16 row must equal the oracle's.  Attention: max |gpu - oracle| <= 2e-3
+with fp32 output; with bf16 output the bound adds half a bf16 ulp of the exact
+value (the rounding of the output itself).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from bit_kv_cache_kivi_amd import kvq  # noqa: E402
+from gpu_util import announce, attention_error, compare_commit, dev  # noqa: E402
+
+
+def build_case(cfg, T=None, B=None, extra_slots=4):
+    w = W.make(cfg, T=T, B=B)
+    c = w.cfg
+    nprot_p = max([len(p) for p in w.prot_prefix] + [0]) + 64
+    nprot_s = max([len(p) for p in (w.prot_suffix or [])] + [0]) + 64
+    cache = kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
+                        prefix_tokens=int(w.lengths.max()) + 32 * extra_slots,
+                        suffix_tokens=c.suffix + (32 if c.suffix else 0),
+                        prefix_protected=nprot_p, suffix_protected=nprot_s if c.suffix else 0,
+                        max_q_heads=c.Hq)
+    ora = O.OracleCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group)
+    prot = w.prot_prefix if c.prot_frac > 0 else None
+    cache.commit(dev(w.k_prefix, c.dtype), dev(w.v_prefix, c.dtype), ntok=w.lengths, protected=prot)
+    ora.commit(0, w.k_prefix, w.v_prefix, ntok=w.lengths, prot=prot)
+    if c.suffix:
+        sprot = w.prot_suffix if c.prot_frac > 0 else None
+        cache.commit(dev(w.k_suffix, c.dtype), dev(w.v_suffix, c.dtype), protected=sprot, segment=kvq.KVQ_SUFFIX)
+        ora.commit(1, w.k_suffix, w.v_suffix, prot=sprot)
+    return w, cache, ora
+
+
+SMALL = [("tiny", None, None), ("llada8b", 512, None), ("dream7b_2bit", 384, 2), ("dream7b_4bit", 384, 2),
+         ("serve_b32", 384, 6), ("dual_long", 640, 2)]
+
+
+@pytest.mark.parametrize("name,T,B", SMALL)
+def test_commit_and_attention_small(name, T, B):
+    announce("small", name, T, B)
+    cfg = W.CONFIGS[name]
+    w, cache, ora = build_case(cfg, T, B)
+    c = w.cfg
+    compare_commit(cache, ora, 0, c.B)
+    if c.suffix:
+        compare_commit(cache, ora, 1, c.B)
+    ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk, use_suffix=bool(c.suffix))
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    out32 = cache.block_attn(q, kb, vb, use_suffix=bool(c.suffix), out_dtype=torch.float32)
+    e32, x32 = attention_error(out32, ref, "f32")
+    out16 = cache.block_attn(q, kb, vb, use_suffix=bool(c.suffix), out_dtype=torch.bfloat16)
+    e16, x16 = attention_error(out16, ref, "bf16")
+    print(f"{name}: max|o|={np.abs(ref).max():.3f} fp32-out err={e32:.2e} bf16-out err={e16:.2e}")
+    assert x32 <= 0, f"fp32 output error {e32}"
+    assert x16 <= 0, f"bf16 output error {e16} exceeds 2e-3 + ulp/2"
+
+
+def test_adversarial_groups():
+    """Constant groups, exact rounding ties, signed zeros, subnormal ranges,
+    partial slots, fully protected slots, fp32 input."""
+    announce("adversarial")
+    B, H, D = 3, 2, 64
+    g = np.random.default_rng(123)
+    n = 96
+    k = g.standard_normal((B, n, H, D)).astype(np.float32)
+    v = g.standard_normal((B, n, H, D)).astype(np.float32)
+    k[0, :32, 0, 0] = 1.25                                   # constant K channel
+    k[0, :32, 0, 1] = np.tile(np.array([0, 0.5, 1, 1.5, 2, 2.5, 3, 3], np.float32), 4)   # 2-bit ties
+    k[0, :32, 0, 2] = np.tile(np.arange(16, dtype=np.float32) * 0.5 + 0.25, 2)
+    k[0, :32, 1, 3] = np.where(np.arange(32) % 2, 0.0, -0.0).astype(np.float32)  # +-0
+    k[1, :32, 0, 4] = (np.arange(32) % 4).astype(np.float32) * np.float32(2.0 ** -149)  # subnormal
+    k[1, :32, 0, 5] = np.float32(3e38) * (np.arange(32) % 2) - np.float32(1e38)           # huge range
+    v[0, 0, 0, :] = 0.75                                     # constant V group
+    v[0, 1, 0, :] = np.tile(np.array([0, 1, 2, 3, 1.5, 0.5, 2.5, 3], np.float32), 8)     # V ties
+    v[2, 5, 1, :32] = -0.0
+    v[2, 5, 1, 32:] = np.float32(2.0 ** -140) * (np.arange(32) % 3)
+    ntok = [96, 70, 33]
+    prot = [np.arange(0, 32), np.array([0, 31, 32, 69]), np.array([], np.int64)]
+    for kb, vb, gv in [(2, 2, 32), (4, 4, 64), (2, 4, 64), (4, 2, 32)]:
+        announce("adversarial bits", kb, vb, gv)
+        cache = kvq.KVCache(B, H, D, kb, vb, gv, prefix_tokens=256, prefix_protected=64, max_q_heads=H)
+        ora = O.OracleCache(B, H, D, kb, vb, gv)
+        cache.commit(dev(k, "f32"), dev(v, "f32"), ntok=ntok, protected=prot)
+        ora.commit(0, k, v, ntok=ntok, prot=prot)
+        # a second commit appends fresh slots after partial ones
+        cache.commit(dev(v[:, :40], "f32"), dev(k[:, :40], "f32"), ntok=[40, 1, 0])
+        ora.commit(0, v[:, :40], k[:, :40], ntok=[40, 1, 0])
+        compare_commit(cache, ora, 0, B)
+
+
+def test_reset_suffix_and_dual():
+    announce("suffix reset")
+    cfg = W.CONFIGS["dual_long"]
+    w, cache, ora = build_case(cfg, T=256, B=2)
+    c = w.cfg
+    # replace the suffix with a shorter one
+    ks, vs = w.k_suffix[:, :100], w.v_suffix[:, :100]
+    cache.commit(dev(ks, c.dtype), dev(vs, c.dtype), segment=kvq.KVQ_SUFFIX, reset=True,
+                 protected=[np.array([3, 99]), np.array([])])
+    ora.commit(1, ks, vs, prot=[np.array([3, 99]), np.array([])], reset=True)
+    compare_commit(cache, ora, 1, c.B)
+    ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk, use_suffix=True)
+    out = cache.block_attn(dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype), use_suffix=True,
+                           out_dtype=torch.float32)
+    e, x = attention_error(out, ref)
+    assert x <= 0, e
+    ref0 = O.block_attention(ora, w.q, w.k_blk, w.v_blk, use_suffix=False)
+    out0 = cache.block_attn(dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype), use_suffix=False,
+                            out_dtype=torch.float32)
+    e0, x0 = attention_error(out0, ref0)
+    assert x0 <= 0, e0
+
+
+def test_split_invariance_and_determinism():
+    """Any split of the cache into chunks gives a result within the oracle gate.
+
+    Splits do not agree bit for bit: P is rounded to fp16 relative to each
+    chunk's running maximum, so a key's rounding error (<= 2^-11 of its weight)
+    differs between splits; the spread stays far below the gate."""
+    announce("split invariance")
+    cfg = W.CONFIGS["dream7b_4bit"]
+    w, cache, ora = build_case(cfg, T=512, B=2)
+    c = w.cfg
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk)
+    outs = []
+    for s in (1, 2, 3, 5, 17, 1000):
+        cache.set_split_slots(s)
+        out = cache.block_attn(q, kb, vb, out_dtype=torch.float32)
+        e, x = attention_error(out, ref)
+        assert x <= 0, (s, e)
+        outs.append(out.cpu().numpy())
+    spread = max(np.abs(o - outs[0]).max() for o in outs[1:])
+    print(f"split spread {spread:.2e}")
+    assert spread < 1e-3
+    cache.set_split_slots(3)
+    a = cache.block_attn(q, kb, vb, out_dtype=torch.float32).cpu().numpy()
+    b = cache.block_attn(q, kb, vb, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def test_empty_cache_attends_to_block_only():
+    announce("empty cache")
+    B, H, r, D = 2, 2, 3, 128
+    g = np.random.default_rng(5)
+    q = g.standard_normal((B, 32, H * r, D)).astype(np.float32)
+    kb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+    vb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+    cache = kvq.KVCache(B, H, D, 4, 4, 128, prefix_tokens=64, max_q_heads=H * r)
+    ora = O.OracleCache(B, H, D, 4, 4, 128)
+    ref = O.block_attention(ora, q, kb, vb)
+    out = cache.block_attn(dev(q, "f32"), dev(kb, "f32"), dev(vb, "f32"), out_dtype=torch.float32)
+    e, x = attention_error(out, ref)
+    assert x <= 0, e
+
+
+def test_per_step_commit_then_attend():
+    """Decode loop shape: commit the previous 32-token block, then attend."""
+    announce("per-step loop")
+    cfg = W.CONFIGS["dream7b_2bit"]
+    w, cache, ora = build_case(cfg, T=256, B=2, extra_slots=4)
+    c = w.cfg
+    for step in range(3):
+        k, v, prot = W.step_block(c, step)
+        cache.commit(dev(k, c.dtype), dev(v, c.dtype), protected=prot)
+        ora.commit(0, k, v, prot=prot)
+        ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk)
+        out = cache.block_attn(dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype),
+                               out_dtype=torch.float32)
+        e, x = attention_error(out, ref)
+        assert x <= 0, (step, e)
+    compare_commit(cache, ora, 0, c.B)
