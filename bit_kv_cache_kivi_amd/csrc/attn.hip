@@ -7,342 +7,410 @@
 // context revisited every step; Tai et al., abstract: prefix and dual cache).
 //
 // Work unit = one 32-token slot of the cache, or the block itself.  A
-// workgroup (4 waves) owns one (sequence, kv head) and a contiguous range of
-// units; all Hq/Hkv query heads of that kv head share every dequantized slot.
-// Per unit:
-//   1. the packed slot record (codes + fp32 meta) is copied HBM -> LDS with
-//      coalesced 16-byte loads, prefetched into registers one unit ahead;
-//   2. the 256 threads dequantize it once into fp16 MFMA operand tiles in LDS
-//      (K tile: A operand of S^T = K Q^T; V tile: A operand of O^T = V^T P^T),
-//      patching protected key rows from their bf16 copies;
-//   3. each wave runs, for each of its query heads (32 query tokens = one
-//      32-wide MFMA tile), S^T on v_mfma_f32_32x32x16_f16, an online softmax in
-//      fp32 (exp2 with the softmax scale folded in), and O^T += V^T P^T.
-//      Computing the transposed products lets the S accumulator registers feed
-//      the PV product's B operand directly (lane = query, 16 tokens per lane).
-// A split's partial (running max, sum, unnormalised O) goes to the workspace
-// and the combine kernel merges splits with log-sum-exp weights; with a
-// single split the workgroup writes the normalised output itself.
+// workgroup owns one (sequence, kv head) and a contiguous range of units.
+// Each wave owns one query head of that kv head (32 query tokens = one 32-wide
+// MFMA tile); with NW = 8 waves two waves share each SIMD, so one wave's MFMA
+// work overlaps the other's softmax and dequantization.  A slot is dequantized
+// once per workgroup and shared by all query heads through LDS.
+//
+// Per slot, as a software pipeline with one barrier per slot:
+//   * every thread loads its share of a slot record (16-byte chunks) and, for
+//     protected key tokens, its share of the bf16 rows into registers with
+//     buffer loads, four slots ahead; two slots later it stores them into one
+//     of two LDS stages, so each load has two pipeline steps to arrive;
+//   * all threads dequantize the next slot into fp16 MFMA operand tiles
+//     (double-buffered): K as an fp16 hi + lo pair (the scores then keep about
+//     22 bits of the dequantized keys), V as fp16;
+//   * each wave runs S^T = K Q^T on v_mfma_f32_32x32x16_f16, an online softmax
+//     in fp32 (exp2 with the scale folded in; the reference maximum is raised
+//     only when the running maximum exceeds it by more than 2^8, so O is
+//     rarely rescaled), and O^T += V^T P^T.  The transposed products let the S
+//     accumulators feed the PV B operand directly (lane = query, 16 tokens per
+//     lane).
+// A split's partial (reference maximum, sum, unnormalised O) goes to the
+// workspace and the combine kernel merges splits with log-sum-exp weights; a
+// single split writes the normalised output itself.
 #include "device_common.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-template <int KB, int VB, int D, int TPW>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
-  constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
-  constexpr int CT = D / 32;   // 32-channel output tiles
-  constexpr int CPT = D / 8;   // K channels dequantized per thread
+constexpr int kStage = 8192;       // bytes of one LDS record stage (>= any record)
+constexpr int kMaxUnits = 256;     // units per split (the host keeps splits within this)
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kMaxSplitsLds = 256;   // splits the combine can merge (host limit on max_splits)
+
+template <int KB, int VB, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
+  constexpr int NT = NW * 64;                // threads
+  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
+  constexpr int CT = D / 32;                 // 32-channel output tiles
+  constexpr int NG = D / 8;                  // 8-channel groups of a token row
+  constexpr int NKG = kSlot * NG;            // (token, 8-channel group) pairs of K
+  constexpr int NVC = D * 4;                 // (channel, token-octet) pairs of V
+  constexpr int GPT = (NKG + NT - 1) / NT;   // K groups dequantized per thread
+  constexpr int VPT = (NVC + NT - 1) / NT;   // V pairs dequantized per thread
+  constexpr int RPT = kStage / 16 / NT;      // record chunks loaded per thread
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
   constexpr uint32_t KM = kmeta_bytes(D);
-  constexpr uint32_t RAW_MAX = record_bytes(D, KB, VB, 32);
-  constexpr int RAW_ITERS = (RAW_MAX + 256 * 16 - 1) / (256 * 16);
+  constexpr int KCH = KC / 16;               // 16-byte chunks of K codes
+  constexpr int CPR = D * KB / 128;          // K-code chunks per token row
+  static_assert(GPT >= 1 && VPT >= 1 && RPT >= 1, "thread mapping");
+  static_assert(record_bytes(D, KB, VB, 32) <= kStage, "record fits a stage");
 
-  __shared__ __align__(16) uint8_t raw[RAW_MAX];
-  __shared__ __align__(16) half8 kop_lds[2][KS][64];   // dequantized K as fp16 hi + lo
-  __shared__ __align__(16) half8 vop_lds[CT][2][64];
+  __shared__ __align__(16) uint8_t rawbuf[2][kStage];       // packed slot records
+  __shared__ __align__(16) uint4 prtbuf[2][GPT][NT];        // this thread's protected-row chunks
+  __shared__ __align__(16) half8 kop[2][2][KS][64];         // [buffer][hi, lo][k-step][lane]
+  __shared__ __align__(16) half8 vop[2][CT][2][64];         // [buffer][channel tile][k-half][lane]
+  __shared__ __align__(16) int4 hdr[kMaxUnits];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int np = a.nslots[0][b];
   const int ns = a.use_suffix ? a.nslots[1][b] : 0;
-  const int U = np + ns + 1;
+  const int U = np + ns + 1;                 // slots + the block itself (last unit)
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (split >= nsplit) return;
   const int u0 = split * a.split_units;
   const int u1 = min(U, u0 + a.split_units);
+  const int nq = min(u1, U - 1) - u0;        // quantized units of this split
+  const bool has_block = u1 == U;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = a.r;
+  const bool active = wave < r;              // this wave owns query head kvh*r + wave
   const uint32_t rbytes = a.record_bytes;
+  const float c2 = a.scale_log2;
 
-  // ---- Q operands (B operand of S^T): lane = query token j, half hh holds
-  //      channels (D/2)*hh + 8s + [0, 8) at k-step s.
-  half8 qop[TPW][KS];
+  auto seg_of = [&](int u) { return u < np ? 0 : 1; };
+  auto slot_of = [&](int u) { return u < np ? u : u - np; };
+
+  // ---------------- prologue: Q operands, slot headers
+  // Q is the B operand of S^T: lane = query token j; half hh holds channels
+  // (D/2)*hh + 8s + [0, 8) at k-step s.
+  half8 qop[KS];
   {
     const int j = lane & 31, hh = lane >> 5;
+    const int hq = kvh * r + (active ? wave : 0);
+    const size_t base = (((size_t)b * kSlot + j) * a.hq + hq) * D + (D / 2) * hh;
+    if (a.q_f32) {
+      float4 raw[KS][2];
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + base);
 #pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-      const int hl = wave + 4 * ti;
-      const int hq = kvh * r + (hl < r ? hl : 0);
-      const size_t row = ((size_t)b * kSlot + j) * a.hq + hq;
+      for (int s = 0; s < KS; ++s) { raw[s][0] = p[2 * s]; raw[s][1] = p[2 * s + 1]; }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        float x[8];
-        load8(a.q, row * D + (D / 2) * hh + 8 * s, a.q_f32, x);
-        qop[ti][s] = to_half8(x);
+        const float x[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
+                            raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
+        qop[s] = to_half8(x);
+      }
+    } else {
+      uint4 raw[KS];
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + base);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) raw[s] = p[s];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float x[8] = {bf16_lo(raw[s].x), bf16_hi(raw[s].x), bf16_lo(raw[s].y), bf16_hi(raw[s].y),
+                            bf16_lo(raw[s].z), bf16_hi(raw[s].z), bf16_lo(raw[s].w), bf16_hi(raw[s].w)};
+        qop[s] = to_half8(x);
       }
     }
   }
-
-  float m_run[TPW], l_run[TPW];
-  floatx16 o[TPW][CT];
-#pragma unroll
-  for (int ti = 0; ti < TPW; ++ti) {
-    m_run[ti] = -__builtin_inff();
-    l_run[ti] = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[ti][ct][i] = 0.f;
+  for (int i = tid; i < nq; i += NT) {
+    const int u = u0 + i, seg = seg_of(u);
+    const uint8_t* hb = seg ? a.seg[1].headers : a.seg[0].headers;
+    const int cap = seg ? a.seg[1].slot_cap : a.seg[0].slot_cap;
+    hdr[i] = *reinterpret_cast<const int4*>(hb + ((size_t)b * cap + slot_of(u)) * kHeaderBytes);
   }
+  __syncthreads();
 
-  // segment fields chosen by value: taking the address of the by-value kernel
-  // argument would copy the whole argument block to scratch memory
-  auto seg_field = [&](int seg, auto SegPtrs::*f) { return seg ? a.seg[1].*f : a.seg[0].*f; };
-
-  // prefetch registers for the next quantized unit
-  uint4 pre[RAW_ITERS];
-  int pre_nvalid = 0, pre_base = 0, pre_seg = 0;
-  uint32_t pre_mask = 0;
-  auto prefetch = [&](int u) {
-    if (u < np + ns) {
-      const int seg = u < np ? 0 : 1;
-      const int slot = u < np ? u : u - np;
-      const int cap = seg_field(seg, &SegPtrs::slot_cap);
-      const int4 hd = *reinterpret_cast<const int4*>(seg_field(seg, &SegPtrs::headers) +
-                                                      ((size_t)b * cap + slot) * kHeaderBytes);
-      pre_nvalid = hd.x;
-      pre_mask = (uint32_t)hd.y;
-      pre_base = hd.z;
-      pre_seg = seg;
-      const uint8_t* src = seg_field(seg, &SegPtrs::records) + (((size_t)b * a.hkv + kvh) * cap + slot) * rbytes;
+  // ---------------- register prefetch of one unit: record chunks (K codes
+  // placed chunk-column-major so that the dequantizing threads read
+  // consecutive 16-byte chunks) and this thread's chunks of protected bf16
+  // key rows.  Buffer loads: their range check turns reads past a segment, or
+  // of rows a thread does not need, into zeros without memory traffic, so
+  // every thread issues the same loads per unit and they stay independent
+  // in-flight loads.
+  __amdgpu_buffer_rsrc_t rec_rsrc[2], prot_rsrc[2];
 #pragma unroll
-      for (int i = 0; i < RAW_ITERS; ++i) {
-        const uint32_t off = (tid + 256 * i) * 16;
-        if (off < rbytes) pre[i] = *reinterpret_cast<const uint4*>(src + off);
+  for (int sg = 0; sg < 2; ++sg) {
+    const SegPtrs& sp = sg ? a.seg[1] : a.seg[0];
+    rec_rsrc[sg] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(sp.records + ((size_t)b * a.hkv + kvh) * sp.slot_cap * rbytes), 0,
+        (int)min((size_t)sp.slot_cap * rbytes, (size_t)0x7fffffff), 0x00020000);
+    prot_rsrc[sg] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(sp.prot_rows + ((size_t)b * a.hkv + kvh) * sp.prot_cap * D), 0,
+        (int)min((size_t)sp.prot_cap * D * 2, (size_t)0x7fffffff), 0x00020000);
+  }
+  struct Pre { uint4 rec[RPT]; uint4 prt[GPT]; };
+  // Loads are issued unconditionally (units past the split read out of range)
+  // so that every path through the loop has the same number of loads in
+  // flight and each store waits only for its own unit's loads.
+  constexpr int kOutOfRange = 0x7ff00000;
+  auto load_unit = [&](int q, Pre& pr) __attribute__((always_inline)) {
+    const bool valid = q < nq;
+    const int u = u0 + (valid ? q : 0), sg = valid ? seg_of(u) : 0;
+    const __amdgpu_buffer_rsrc_t rr = sg ? rec_rsrc[1] : rec_rsrc[0];
+    const __amdgpu_buffer_rsrc_t prr = sg ? prot_rsrc[1] : prot_rsrc[0];
+    const int rbase = valid ? slot_of(u) * (int)rbytes : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int k = j * NT + tid;
+      const int gc = k < KCH ? (k & 31) * CPR + (k >> 5) : k;
+      pr.rec[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, rbase + gc * 16, 0, 0));
+    }
+    const int4 h = valid ? hdr[q] : make_int4(0, 0, 0, 0);
+    const uint32_t mask = (uint32_t)h.y;
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
+      const int rank = h.z + __popc(mask & ((1u << t) - 1u));
+      const int poff = (idx < NKG && ((mask >> t) & 1u)) ? (rank * D + 8 * cg) * 2 : kOutOfRange;
+      pr.prt[gi] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prr, poff, 0, 0));
+    }
+  };
+  auto store_unit = [&](int q, const Pre& pr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) *reinterpret_cast<uint4*>(rawbuf[q & 1] + (j * NT + tid) * 16) = pr.rec[j];
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) prtbuf[q & 1][gi][tid] = pr.prt[gi];
+  };
+
+  // ---------------- dequantize unit q into operand buffer q & 1
+  auto dequant = [&](int q) __attribute__((always_inline)) {
+    const uint8_t* rawS = rawbuf[q & 1];
+    const int ob = q & 1;
+    const uint32_t mask = (uint32_t)hdr[q].y;
+    const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC);
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      // K: (token t, 8-channel group cg)
+      const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
+      if (NKG % NT != 0 && idx >= NKG) break;
+      float x[8];
+      if ((mask >> t) & 1u) {
+        const uint4 w = prtbuf[q & 1][gi][tid];
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+      } else {
+        const int bo = cg * KB;               // byte offset of the group's codes in the token row
+        const uint4 ch = *reinterpret_cast<const uint4*>(rawS + ((bo >> 4) * 32 + t) * 16);
+        const int wsel = (bo & 15) >> 2;
+        const uint32_t word = wsel == 0 ? ch.x : wsel == 1 ? ch.y : wsel == 2 ? ch.z : ch.w;
+        const uint32_t bits = KB == 4 ? word : (word >> (8 * (bo & 3)));
+        const float4 s0 = *reinterpret_cast<const float4*>(kmeta + 8 * cg);
+        const float4 s1 = *reinterpret_cast<const float4*>(kmeta + 8 * cg + 4);
+        const float4 z0 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg);
+        const float4 z1 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg + 4);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] = fmaf((float)((bits >> (KB * e)) & ((1u << KB) - 1u)), sc[e], zr[e]);
       }
+      const int hh = cg / (D / 16), s = cg % (D / 16);
+      store_hi_lo(kop[ob][0][s][t + 32 * hh], kop[ob][1][s][t + 32 * hh], x);
+    }
+#pragma unroll
+    for (int vi = 0; vi < VPT; ++vi) {
+      // V: channel c, token octet (mm, hh)
+      const int idx = vi * NT + tid, c = idx % D, combo = idx / D;
+      if (NVC % NT != 0 && idx >= NVC) break;
+      const int mm = combo >> 1, hh = combo & 1;
+      uint32_t bits;
+      if (VB == 4) bits = *reinterpret_cast<const uint32_t*>(rawS + KC + c * 16 + (2 * mm + hh) * 4);
+      else         bits = *reinterpret_cast<const uint32_t*>(rawS + KC + c * 8 + hh * 4) >> (16 * mm);
+      const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (c >> a.gv_log2) * 256);
+      const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
+      const float4 s0 = *reinterpret_cast<const float4*>(vs + ta);
+      const float4 s1 = *reinterpret_cast<const float4*>(vs + ta + 8);
+      const float4 z0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
+      const float4 z1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
+      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = fmaf((float)((bits >> (VB * e)) & ((1u << VB) - 1u)), sc[e], zr[e]);
+      vop[ob][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
     }
   };
 
-  prefetch(u0);
-  for (int u = u0; u < u1; ++u) {
-    int nvalid = kSlot;
-    if (u < np + ns) {
-      // ---------------- stage the packed record, then dequantize into LDS
-      const int cur_nvalid = pre_nvalid, cur_base = pre_base;
-      const uint32_t cur_mask = pre_mask;
-      const uint16_t* cur_prot = seg_field(pre_seg, &SegPtrs::prot_rows);
-      const int cur_pcap = seg_field(pre_seg, &SegPtrs::prot_cap);
+  // ---------------- this wave's MFMA + online softmax over operand buffer ob
+  float m_ref = -__builtin_inff(), l_run = 0.f;
+  floatx16 o[CT];
 #pragma unroll
-      for (int i = 0; i < RAW_ITERS; ++i) {
-        const uint32_t off = (tid + 256 * i) * 16;
-        if (off < rbytes) *reinterpret_cast<uint4*>(raw + off) = pre[i];
-      }
-      __syncthreads();
-      if (u + 1 < u1) prefetch(u + 1);
-      nvalid = cur_nvalid;
-      // K: thread -> token t, channels [p*CPT, (p+1)*CPT)
-      {
-        const int t = tid & 31, p = tid >> 5;
-        const bool prot = (cur_mask >> t) & 1u;
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int gi = 0; gi < CPT / 8; ++gi) {
-          const int cgp = p * (CPT / 8) + gi;          // 8-channel group
-          float x[8];
-          if (prot) {
-            const int rank = cur_base + __popc(cur_mask & ((1u << t) - 1u));
-            const size_t prow = ((size_t)b * cur_pcap + rank) * a.hkv + kvh;
-            load8(cur_prot, prow * D + 8 * cgp, false, x);
-          } else {
-            uint32_t bits;
-            if (KB == 4) bits = *reinterpret_cast<const uint32_t*>(raw + t * (D / 2) + 4 * cgp);
-            else         bits = *reinterpret_cast<const uint16_t*>(raw + t * (D / 4) + 2 * cgp);
-            const float* ks = reinterpret_cast<const float*>(raw + KC + VC) + 8 * cgp;
-            const float4 s0 = *reinterpret_cast<const float4*>(ks);
-            const float4 s1 = *reinterpret_cast<const float4*>(ks + 4);
-            const float4 z0 = *reinterpret_cast<const float4*>(ks + D);
-            const float4 z1 = *reinterpret_cast<const float4*>(ks + D + 4);
-            const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-            const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    for (int i = 0; i < 16; ++i) o[ct][i] = 0.f;
+  auto compute = [&](int ob, int nvalid) __attribute__((always_inline)) {
+    if (!active) return;
+    floatx16 sacc;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              x[e] = fmaf((float)((bits >> (KB * e)) & ((1u << KB) - 1u)), sc[e], zr[e]);
-          }
-          const int hh = cgp / (D / 16), s = cgp % (D / 16);
-          store_hi_lo(kop_lds[0][s][t + 32 * hh], kop_lds[1][s][t + 32 * hh], x);
-        }
-      }
-      // V: thread -> channel lane cl, combos (ct, mm, hh)
-      {
-        const int cl = tid & 31, rest = tid >> 5;
-#pragma unroll
-        for (int qi = 0; qi < CT / 2; ++qi) {
-          const int q = rest + 8 * qi;
-          const int ct = q >> 2, mm = (q >> 1) & 1, hh = q & 1;
-          const int c = 32 * ct + cl;
-          uint32_t bits;
-          if (VB == 4) bits = *reinterpret_cast<const uint32_t*>(raw + KC + c * 16 + (2 * mm + hh) * 4);
-          else         bits = *reinterpret_cast<const uint32_t*>(raw + KC + c * 8 + hh * 4) >> (16 * mm);
-          const int g = c >> a.gv_log2;
-          const float* vs = reinterpret_cast<const float*>(raw + KC + VC + KM + g * 256);
-          const int ta = 16 * mm + 4 * hh;               // tokens ta..ta+3, ta+8..ta+11
-          const float4 s0 = *reinterpret_cast<const float4*>(vs + ta);
-          const float4 s1 = *reinterpret_cast<const float4*>(vs + ta + 8);
-          const float4 z0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
-          const float4 z1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
-          const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-          const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            x[e] = fmaf((float)((bits >> (VB * e)) & ((1u << VB) - 1u)), sc[e], zr[e]);
-          vop_lds[ct][mm][cl + 32 * hh] = to_half8(x);
-        }
-      }
-    } else {
-      // ---------------- the full-precision block itself
-      {
-        const int t = tid & 31, p = tid >> 5;
-        const size_t row = ((size_t)b * kSlot + t) * a.hkv + kvh;
-#pragma unroll
-        for (int gi = 0; gi < CPT / 8; ++gi) {
-          const int cgp = p * (CPT / 8) + gi;
-          float x[8];
-          load8(a.k_blk, row * D + 8 * cgp, a.blk_f32, x);
-          const int hh = cgp / (D / 16), s = cgp % (D / 16);
-          store_hi_lo(kop_lds[0][s][t + 32 * hh], kop_lds[1][s][t + 32 * hh], x);
-        }
-      }
-      {
-        const int cl = tid & 31, rest = tid >> 5;
-#pragma unroll
-        for (int qi = 0; qi < CT / 2; ++qi) {
-          const int q = rest + 8 * qi;
-          const int ct = q >> 2, mm = (q >> 1) & 1, hh = q & 1;
-          const int c = 32 * ct + cl;
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int t = 16 * mm + 4 * hh + (e & 3) + 8 * (e >> 2);
-            x[e] = load1(a.v_blk, (((size_t)b * kSlot + t) * a.hkv + kvh) * D + c, a.blk_f32);
-          }
-          vop_lds[ct][mm][cl + 32 * hh] = to_half8(x);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---------------- MFMA + online softmax for this wave's query heads
-    // S^T = (K_hi + K_lo) Q^T: the lo part carries the bits fp16 drops from
-    // the dequantized keys, so the scores keep about 22 significant bits.
-    floatx16 sacc[TPW];
-#pragma unroll
-    for (int ti = 0; ti < TPW; ++ti)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[ti][i] = 0.f;
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const half8 kh = kop_lds[0][s][lane];
-      const half8 kl = kop_lds[1][s][lane];
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[ob][0][s][lane], qop[s], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[ob][1][s][lane], qop[s], sacc, 0, 0, 0);
+    }
+    // sacc[i] = S[query lane%32][token 8*(i/4) + 4*(lane/32) + i%4]
+    if (nvalid < kSlot) {
 #pragma unroll
-      for (int ti = 0; ti < TPW; ++ti) {
-        if (wave + 4 * ti < r) {
-          sacc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, qop[ti][s], sacc[ti], 0, 0, 0);
-          sacc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qop[ti][s], sacc[ti], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int tok = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (tok >= nvalid) sacc[i] = -__builtin_inff();
       }
     }
-    half8 pop[TPW][2];
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-      if (wave + 4 * ti < r) {
-        // sacc[i] = S[query lane%32][token 8*(i/4) + 4*(lane/32) + i%4]
-        if (nvalid < kSlot) {
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);
+    mx = fmaxf(mx, sacc[15]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float ms = mx * c2;
+    const bool need = ms > m_ref + kRescaleSlack;
+    if (__any(need)) {
+      const float m_new = need ? ms : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tok = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (tok >= nvalid) sacc[ti][i] = -__builtin_inff();
-          }
-        }
-        float mx = sacc[ti][0];
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[ti][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[ti], mx * a.scale_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[ti] - m_new);
-        m_run[ti] = m_new;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[ti][i], a.scale_log2, -m_new));
-          psum += pv;
-          pop[ti][i >> 3][i & 7] = static_cast<_Float16>(pv);
-        }
-        l_run[ti] = fmaf(l_run[ti], alpha, psum);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[ti][ct][i] *= alpha;
-      }
+        for (int i = 0; i < 16; ++i) o[ct][i] *= alpha;
     }
+    const float mneg = -m_ref;
+    float psum = 0.f;
+    half8 pop[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, mneg));
+      psum += pv;
+      pop[i >> 3][i & 7] = static_cast<_Float16>(pv);
+    }
+    l_run += psum;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const half8 v0 = vop_lds[ct][0][lane];
-      const half8 v1 = vop_lds[ct][1][lane];
+      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[ob][ct][0][lane], pop[0], o[ct], 0, 0, 0);
+      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[ob][ct][1][lane], pop[1], o[ct], 0, 0, 0);
+    }
+  };
+
+  // ---------------- pipeline prologue
+  Pre pre0, pre1;
+  load_unit(0, pre0);
+  load_unit(1, pre1);
+  if (has_block) {
+    // the full-precision block -> operand buffer 1 (K hi/lo directly; V via a
+    // [token][channel] fp32 staging transpose in buffer 0, which the first
+    // slot overwrites only after the next barrier)
+    float* stage = reinterpret_cast<float*>(&kop[0][0][0][0]);   // 32 x D fp32
 #pragma unroll
-      for (int ti = 0; ti < TPW; ++ti) {
-        if (wave + 4 * ti < r) {
-          o[ti][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, pop[ti][0], o[ti][ct], 0, 0, 0);
-          o[ti][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, pop[ti][1], o[ti][ct], 0, 0, 0);
-        }
-      }
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
+      if (NKG % NT != 0 && idx >= NKG) break;
+      const size_t rowe = (((size_t)b * kSlot + t) * a.hkv + kvh) * D + 8 * cg;
+      float kx[8], vx[8];
+      load8(a.k_blk, rowe, a.blk_f32, kx);
+      load8(a.v_blk, rowe, a.blk_f32, vx);
+      const int hh = cg / (D / 16), s = cg % (D / 16);
+      store_hi_lo(kop[1][0][s][t + 32 * hh], kop[1][1][s][t + 32 * hh], kx);
+      *reinterpret_cast<float4*>(stage + t * D + 8 * cg) = make_float4(vx[0], vx[1], vx[2], vx[3]);
+      *reinterpret_cast<float4*>(stage + t * D + 8 * cg + 4) = make_float4(vx[4], vx[5], vx[6], vx[7]);
     }
     __syncthreads();
+#pragma unroll
+    for (int vi = 0; vi < VPT; ++vi) {
+      const int idx = vi * NT + tid, c = idx % D, combo = idx / D;
+      if (NVC % NT != 0 && idx >= NVC) break;
+      const int mm = combo >> 1, hh = combo & 1;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = stage[(16 * mm + 4 * hh + (e & 3) + 8 * (e >> 2)) * D + c];
+      vop[1][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
+    }
+    __syncthreads();
+    compute(1, kSlot);
+  }
+  if (nq > 0) {
+    store_unit(0, pre0);
+    load_unit(2, pre0);
+    __syncthreads();
+    dequant(0);
+    store_unit(1, pre1);
+    load_unit(3, pre1);
+    __syncthreads();
+
+    // ---------------- steady state, unrolled by two (register set = q & 1)
+    // Both halves always run their loads, stores and barriers (past the last
+    // unit they touch only out-of-range data and unused stages), so the number
+    // of loads in flight is the same on every path.
+    for (int q = 0; q < nq; q += 2) {
+      store_unit(q + 2, pre0);
+      if (q + 1 < nq) dequant(q + 1);
+      compute(0, hdr[q].x);
+      load_unit(q + 4, pre0);
+      __syncthreads();
+      store_unit(q + 3, pre1);
+      if (q + 2 < nq) dequant(q + 2);
+      if (q + 1 < nq) compute(1, hdr[q + 1].x);
+      load_unit(q + 5, pre1);
+      __syncthreads();
+    }
   }
 
   // ---------------- epilogue
+  if (!active) return;
+  const int hq = kvh * r + wave;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const int j = lane & 31, hh = lane >> 5;
+  if (nsplit == 1) {
+    const float inv = 1.0f / l_tot;
+    const size_t row = ((size_t)b * kSlot + j) * a.hq + hq;
 #pragma unroll
-  for (int ti = 0; ti < TPW; ++ti) {
-    const int hl = wave + 4 * ti;
-    if (hl >= r) continue;
-    const int hq = kvh * r + hl;
-    const float l_tot = l_run[ti] + __shfl_xor(l_run[ti], 32);
-    const int j = lane & 31, hh = lane >> 5;
-    if (nsplit == 1) {
-      const float inv = 1.0f / l_tot;
-      const size_t row = ((size_t)b * kSlot + j) * a.hq + hq;
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int c = 32 * ct + 8 * qd + 4 * hh;
-          const float v0 = o[ti][ct][4 * qd] * inv, v1 = o[ti][ct][4 * qd + 1] * inv;
-          const float v2 = o[ti][ct][4 * qd + 2] * inv, v3 = o[ti][ct][4 * qd + 3] * inv;
-          if (a.out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * D + c) = make_float4(v0, v1, v2, v3);
-          } else {
-            uint2 w;
-            w.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-            w.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + c) = w;
-          }
+      for (int qd = 0; qd < 4; ++qd) {
+        const int c = 32 * ct + 8 * qd + 4 * hh;
+        const float v0 = o[ct][4 * qd] * inv, v1 = o[ct][4 * qd + 1] * inv;
+        const float v2 = o[ct][4 * qd + 2] * inv, v3 = o[ct][4 * qd + 3] * inv;
+        if (a.out_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * D + c) = make_float4(v0, v1, v2, v3);
+        } else {
+          uint2 w;
+          w.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+          w.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + c) = w;
         }
-    } else {
-      const size_t idx = (((size_t)b * a.hkv + kvh) * a.max_splits + split) * r + hl;
-      float* base = a.partial + idx * (size_t)(D + 2) * kSlot;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = 32 * ct + 8 * (i >> 2) + 4 * hh + (i & 3);
-          base[c * kSlot + j] = o[ti][ct][i];
-        }
-      if (hh == 0) {
-        base[D * kSlot + j] = m_run[ti];
-        base[(D + 1) * kSlot + j] = l_tot;
       }
+  } else {
+    const size_t pidx = (((size_t)b * a.hkv + kvh) * a.max_splits + split) * r + wave;
+    float* base = a.partial + pidx * (size_t)(D + 2) * kSlot;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = 32 * ct + 8 * (i >> 2) + 4 * hh + (i & 3);
+        base[c * kSlot + j] = o[ct][i];
+      }
+    if (hh == 0) {
+      base[D * kSlot + j] = m_ref;
+      base[(D + 1) * kSlot + j] = l_tot;
     }
   }
 }
 
 // One workgroup per (query head, sequence): merges the splits of all 32 rows.
+// Thread -> (4 consecutive query tokens, channels c, c+32, ...): every split's
+// partial is read with 16-byte loads, many in flight, and the result is
+// transposed through LDS for row-contiguous output stores.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
-  __shared__ float w_lds[256][kSlot];
-  __shared__ float out_lds[kSlot][D + 1];
-  __shared__ float inv_l[kSlot];
+  __shared__ __align__(16) float w_lds[kMaxSplitsLds][kSlot];
+  __shared__ __align__(16) float out_lds[kSlot][D + 4];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int np = a.nslots[0][b];
   const int ns = a.use_suffix ? a.nslots[1][b] : 0;
@@ -351,41 +419,83 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   if (nsplit <= 1) return;
   const int r = a.r, kvh = hq / r, hl = hq % r;
   const int tid = threadIdx.x;
-  auto part = [&](int sp) {
-    return a.partial + ((((size_t)b * a.hkv + kvh) * a.max_splits + sp) * r + hl) * (size_t)(D + 2) * kSlot;
-  };
+  const size_t pstride = (size_t)r * (D + 2) * kSlot;           // one split's partial
+  const float* p0 = a.partial + ((((size_t)b * a.hkv + kvh) * a.max_splits) * r + hl) * (size_t)(D + 2) * kSlot;
   if (tid < kSlot) {
     float mstar = -__builtin_inff();
-    for (int sp = 0; sp < nsplit; ++sp) mstar = fmaxf(mstar, part(sp)[D * kSlot + tid]);
+    for (int sp = 0; sp < nsplit; ++sp) mstar = fmaxf(mstar, p0[sp * pstride + D * kSlot + tid]);
     float l = 0.f;
     for (int sp = 0; sp < nsplit; ++sp) {
-      const float w = __builtin_amdgcn_exp2f(part(sp)[D * kSlot + tid] - mstar);
+      const float w = __builtin_amdgcn_exp2f(p0[sp * pstride + D * kSlot + tid] - mstar);
+      l = fmaf(p0[sp * pstride + (D + 1) * kSlot + tid], w, l);
       w_lds[sp][tid] = w;
-      l = fmaf(part(sp)[(D + 1) * kSlot + tid], w, l);
     }
-    inv_l[tid] = 1.0f / l;
+    const float inv = 1.0f / l;
+    for (int sp = 0; sp < nsplit; ++sp) w_lds[sp][tid] *= inv;
   }
   __syncthreads();
-  const int j = tid & 31, cq = tid >> 5;
-  for (int c = cq; c < D; c += 8) {
-    float acc = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) acc = fmaf(part(sp)[c * kSlot + j], w_lds[sp][j], acc);
-    out_lds[j][c] = acc * inv_l[j];
+  const int jq = tid & 7, c0 = tid >> 3;      // tokens 4jq..4jq+3, channels c0 + 32k
+  constexpr int NC = D / 32;
+  float4 acc[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sp = 0;
+  for (; sp + 4 <= nsplit; sp += 4) {
+    float4 v[4][NC];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < NC; ++k)
+        v[u][k] = *reinterpret_cast<const float4*>(p0 + (sp + u) * pstride + (c0 + 32 * k) * kSlot + 4 * jq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 wv = *reinterpret_cast<const float4*>(&w_lds[sp + u][4 * jq]);
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        acc[k].x = fmaf(v[u][k].x, wv.x, acc[k].x); acc[k].y = fmaf(v[u][k].y, wv.y, acc[k].y);
+        acc[k].z = fmaf(v[u][k].z, wv.z, acc[k].z); acc[k].w = fmaf(v[u][k].w, wv.w, acc[k].w);
+      }
+    }
+  }
+  for (; sp < nsplit; ++sp) {
+    const float4 wv = *reinterpret_cast<const float4*>(&w_lds[sp][4 * jq]);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(p0 + sp * pstride + (c0 + 32 * k) * kSlot + 4 * jq);
+      acc[k].x = fmaf(v.x, wv.x, acc[k].x); acc[k].y = fmaf(v.y, wv.y, acc[k].y);
+      acc[k].z = fmaf(v.z, wv.z, acc[k].z); acc[k].w = fmaf(v.w, wv.w, acc[k].w);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int c = c0 + 32 * k;
+    out_lds[4 * jq + 0][c] = acc[k].x;
+    out_lds[4 * jq + 1][c] = acc[k].y;
+    out_lds[4 * jq + 2][c] = acc[k].z;
+    out_lds[4 * jq + 3][c] = acc[k].w;
   }
   __syncthreads();
-  for (int idx = tid; idx < kSlot * D; idx += 256) {
-    const int jj = idx / D, c = idx % D;
+  // row j of this head: D contiguous outputs, 4 per thread
+  for (int idx = tid; idx < kSlot * D / 4; idx += 256) {
+    const int jj = idx / (D / 4), c = 4 * (idx % (D / 4));
     const size_t o = (((size_t)b * kSlot + jj) * a.hq + hq) * D + c;
-    if (a.out_f32) static_cast<float*>(a.out)[o] = out_lds[jj][c];
-    else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(out_lds[jj][c]);
+    const float4 v = *reinterpret_cast<const float4*>(&out_lds[jj][c]);
+    if (a.out_f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = v;
+    } else {
+      uint2 w;
+      w.x = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
+      w.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
+    }
   }
 }
 
 template <int KB, int VB, int D>
 hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
   dim3 grid(grid_splits, a.hkv, B);
-  if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 1>), grid, dim3(256), 0, s, a);
-  else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 2>), grid, dim3(256), 0, s, a);
+  if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4>), grid, dim3(256), 0, s, a);
+  else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8>), grid, dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B), dim3(256), 0, s, a);

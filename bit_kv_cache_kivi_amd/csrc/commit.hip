@@ -86,7 +86,7 @@ __global__ __launch_bounds__(128) void commit_kernel(const CommitArgs a) {
           w.y = f32_to_bf16_bits(x[k][2]) | (f32_to_bf16_bits(x[k][3]) << 16);
           w.z = f32_to_bf16_bits(x[k][4]) | (f32_to_bf16_bits(x[k][5]) << 16);
           w.w = f32_to_bf16_bits(x[k][6]) | (f32_to_bf16_bits(x[k][7]) << 16);
-          const size_t prow = ((size_t)task.b * a.seg.prot_cap + rank) * a.hkv + h;
+          const size_t prow = ((size_t)task.b * a.hkv + h) * a.seg.prot_cap + rank;
           *reinterpret_cast<uint4*>(a.seg.prot_rows + prow * D + 8 * cg) = w;
           if (h == 0 && cg == 0) a.seg.prot_pos[(size_t)task.b * a.seg.prot_cap + rank] = task.token_base + t;
         }

@@ -14,6 +14,8 @@
 
 using kvq::CommitTask;
 
+constexpr int kMaxSplitUnits = 256;   // units one attention workgroup can hold headers for
+
 namespace {
 
 thread_local std::string g_err;
@@ -110,6 +112,7 @@ struct kvq_cache {
   hipEvent_t ev[2] = {nullptr, nullptr};
   bool ev_used[2] = {false, false};
   int next_stage = 0;
+  int num_cus = 0;                 // compute units of the device (sizes the attention grid)
   std::vector<CommitTask> tasks;
 };
 
@@ -123,6 +126,10 @@ kvq_status ensure_hip(kvq_cache* c) {
     e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
   }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c->num_cus <= 0)
+    c->num_cus = 256;
   c->hip_ready = true;
   return KVQ_OK;
 }
@@ -382,16 +389,23 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
     max_units = std::max(max_units, U);
     total_units += U;
   }
+  kvq_status hs = ensure_hip(c);
+  if (hs != KVQ_OK) return hs;
   int split_units;
   if (c->split_slots > 0) {
     split_units = c->split_slots;
   } else {
-    // aim for about two workgroups per compute unit over the whole grid
-    const int64_t target = 512;
+    // one workgroup per compute unit over the whole grid: the kernel holds one
+    // workgroup per CU, and fewer splits mean fewer partials to merge
+    const int64_t target = c->num_cus;
     const int64_t pairs_units = total_units * H;
     split_units = (int)std::max<int64_t>(8, (pairs_units + target - 1) / target);
   }
   split_units = std::max(split_units, (max_units + max_splits - 1) / max_splits);
+  split_units = std::min(split_units, kMaxSplitUnits);
+  if ((int64_t)split_units * max_splits < max_units)
+    return fail(KVQ_EUNSUPPORTED, "%d attended units per sequence exceed max_splits %d x %d units", max_units,
+                max_splits, kMaxSplitUnits);
   const int grid_splits = (max_units + split_units - 1) / split_units;
 
   a.q = d_q;

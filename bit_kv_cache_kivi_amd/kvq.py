@@ -228,8 +228,8 @@ class KVCache:
         L = self.layout
         H, D, pcap = self.cfg.num_kv_heads, self.cfg.head_dim, L["prot_cap"][segment]
         n = self.segment_info(segment)[2][b]
-        rb = L["prot_rows_offset"][segment] + b * pcap * H * D * 2
+        rb = L["prot_rows_offset"][segment] + b * H * pcap * D * 2
         pb = L["prot_pos_offset"][segment] + b * pcap * 4
-        rows = self.buffer[rb:rb + n * H * D * 2].view(torch.int16).view(n, H, D)
+        rows = self.buffer[rb:rb + H * pcap * D * 2].view(torch.int16).view(H, pcap, D)[:, :n].permute(1, 0, 2)
         pos = self.buffer[pb:pb + n * 4].view(torch.int32)
         return pos, rows

@@ -93,8 +93,8 @@
  *   int32 token_base segment position of the slot's first token
  *
  * Protected K rows, per (segment, b): rank r in [0, nprot) in ascending
- * position order:
- *   bf16 rows at prot_rows_offset[seg] + ((b * prot_cap[seg] + r) * Hkv + h) * D * 2
+ * position order (a slot's rows for one kv head are contiguous):
+ *   bf16 rows at prot_rows_offset[seg] + ((b * Hkv + h) * prot_cap[seg] + r) * D * 2
  *   int32 position at prot_pos_offset[seg] + (b * prot_cap[seg] + r) * 4
  * A protected token's row in slot s is rank prot_base + popcount(prot_mask & ((1<<t)-1)).
  */
