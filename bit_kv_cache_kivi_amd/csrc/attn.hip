@@ -55,8 +55,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
   constexpr uint32_t KM = kmeta_bytes(D);
-  constexpr int KCH = KC / 16;               // 16-byte chunks of K codes
-  constexpr int CPR = D * KB / 128;          // K-code chunks per token row
   static_assert(GPT >= 1 && VPT >= 1 && RPT >= 1, "thread mapping");
   static_assert(record_bytes(D, KB, VB, 32) <= kStage, "record fits a stage");
 
@@ -128,43 +126,53 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
   }
   __syncthreads();
 
-  // ---------------- register prefetch of one unit: record chunks (K codes
-  // placed chunk-column-major so that the dequantizing threads read
-  // consecutive 16-byte chunks) and this thread's chunks of protected bf16
-  // key rows.  Buffer loads: their range check turns reads past a segment, or
+  // ---------------- register prefetch of one unit: the slot record (16-byte
+  // chunks, as laid out in memory) and this thread's chunk of a protected bf16
+  // key row.  Buffer loads: their range check turns reads past a segment, or
   // of rows a thread does not need, into zeros without memory traffic, so
   // every thread issues the same loads per unit and they stay independent
   // in-flight loads.
-  __amdgpu_buffer_rsrc_t rec_rsrc[2], prot_rsrc[2];
-#pragma unroll
-  for (int sg = 0; sg < 2; ++sg) {
-    const SegPtrs& sp = sg ? a.seg[1] : a.seg[0];
-    rec_rsrc[sg] = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(sp.records + ((size_t)b * a.hkv + kvh) * sp.slot_cap * rbytes), 0,
-        (int)min((size_t)sp.slot_cap * rbytes, (size_t)0x7fffffff), 0x00020000);
-    prot_rsrc[sg] = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(sp.prot_rows + ((size_t)b * a.hkv + kvh) * sp.prot_cap * D), 0,
-        (int)min((size_t)sp.prot_cap * D * 2, (size_t)0x7fffffff), 0x00020000);
-  }
+  // The descriptor of a unit's segment is rebuilt per unit from base and size
+  // values passed through readfirstlane: a descriptor chosen by a select is
+  // taken as divergent and would force a per-lane loop around every load.
+  const uint8_t* rec_base0 = a.seg[0].records + ((size_t)b * a.hkv + kvh) * a.seg[0].slot_cap * rbytes;
+  const uint8_t* rec_base1 = a.seg[1].records + ((size_t)b * a.hkv + kvh) * a.seg[1].slot_cap * rbytes;
+  const int rec_n0 = (int)min((size_t)a.seg[0].slot_cap * rbytes, (size_t)0x7fffffff);
+  const int rec_n1 = (int)min((size_t)a.seg[1].slot_cap * rbytes, (size_t)0x7fffffff);
+  const uint16_t* prot_base0 = a.seg[0].prot_rows + ((size_t)b * a.hkv + kvh) * a.seg[0].prot_cap * D;
+  const uint16_t* prot_base1 = a.seg[1].prot_rows + ((size_t)b * a.hkv + kvh) * a.seg[1].prot_cap * D;
+  const int prot_n0 = (int)min((size_t)a.seg[0].prot_cap * D * 2, (size_t)0x7fffffff);
+  const int prot_n1 = (int)min((size_t)a.seg[1].prot_cap * D * 2, (size_t)0x7fffffff);
+  auto uniform_rsrc = [](const void* p, int n) __attribute__((always_inline)) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0,
+                                             __builtin_amdgcn_readfirstlane(n), 0x00020000);
+  };
   struct Pre { uint4 rec[RPT]; uint4 prt[GPT]; };
   // Loads are issued unconditionally (units past the split read out of range)
   // so that every path through the loop has the same number of loads in
   // flight and each store waits only for its own unit's loads.
   constexpr int kOutOfRange = 0x7ff00000;
+  bool rec_chunk[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) rec_chunk[j] = (uint32_t)(j * NT + tid) * 16u < rbytes;
   auto load_unit = [&](int q, Pre& pr) __attribute__((always_inline)) {
     const bool valid = q < nq;
     const int u = u0 + (valid ? q : 0), sg = valid ? seg_of(u) : 0;
-    const __amdgpu_buffer_rsrc_t rr = sg ? rec_rsrc[1] : rec_rsrc[0];
-    const __amdgpu_buffer_rsrc_t prr = sg ? prot_rsrc[1] : prot_rsrc[0];
-    const int rbase = valid ? slot_of(u) * (int)rbytes : kOutOfRange;
+    const __amdgpu_buffer_rsrc_t rr = uniform_rsrc(sg ? rec_base1 : rec_base0, sg ? rec_n1 : rec_n0);
+    const __amdgpu_buffer_rsrc_t prr = uniform_rsrc(sg ? (const void*)prot_base1 : (const void*)prot_base0, sg ? prot_n1 : prot_n0);
+    const int rbase = slot_of(u) * (int)rbytes;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int k = j * NT + tid;
-      const int gc = k < KCH ? (k & 31) * CPR + (k >> 5) : k;
-      pr.rec[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, rbase + gc * 16, 0, 0));
+      const int off = (valid && rec_chunk[j]) ? rbase + (j * NT + tid) * 16 : kOutOfRange;
+      pr.rec[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
     }
-    const int4 h = valid ? hdr[q] : make_int4(0, 0, 0, 0);
-    const uint32_t mask = (uint32_t)h.y;
+    // header read unconditionally (clamped index) and masked by a select, so
+    // no branch splits the loads of a unit
+    const int4 h = hdr[min(q, kMaxUnits - 1)];
+    const uint32_t mask = valid ? (uint32_t)h.y : 0u;
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
       const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
@@ -173,70 +181,84 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
       pr.prt[gi] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prr, poff, 0, 0));
     }
   };
+  // Wait for the oldest unit's loads (the newer unit's RPT + GPT loads may stay
+  // in flight).  Stating the wait once, before the conditional stores, keeps
+  // the compiler from adding waits later where it reuses these registers.
+  constexpr int kLoadsPerUnit = RPT + GPT;
+  static_assert(kLoadsPerUnit < 16, "vmcnt field");
   auto store_unit = [&](int q, const Pre& pr) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xF70 | kLoadsPerUnit);   // vmcnt(kLoadsPerUnit), others unconstrained
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) *reinterpret_cast<uint4*>(rawbuf[q & 1] + (j * NT + tid) * 16) = pr.rec[j];
+    for (int j = 0; j < RPT; ++j)
+      if (rec_chunk[j]) *reinterpret_cast<uint4*>(rawbuf[q & 1] + (j * NT + tid) * 16) = pr.rec[j];
+    const uint32_t mask = q < nq ? (uint32_t)hdr[min(q, kMaxUnits - 1)].y : 0u;
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) prtbuf[q & 1][gi][tid] = pr.prt[gi];
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int idx = gi * NT + tid, t = idx & 31;
+      if ((mask >> t) & 1u) prtbuf[q & 1][gi][tid] = pr.prt[gi];
+    }
   };
 
   // ---------------- dequantize unit q into operand buffer q & 1
+  const float neg_one = opaque_neg_one();
   auto dequant = [&](int q) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
     const int ob = q & 1;
     const uint32_t mask = (uint32_t)hdr[q].y;
     const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC);
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
-      // K: (token t, 8-channel group cg)
+      // K: (token t, 8-channel group cg); its codes are word cg (4-bit) or
+      // half cg % 2 of word cg / 2 (2-bit) of token t's word column.
       const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
-      if (NKG % NT != 0 && idx >= NKG) break;
-      float x[8];
-      if ((mask >> t) & 1u) {
-        const uint4 w = prtbuf[q & 1][gi][tid];
-        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-      } else {
-        const int bo = cg * KB;               // byte offset of the group's codes in the token row
-        const uint4 ch = *reinterpret_cast<const uint4*>(rawS + ((bo >> 4) * 32 + t) * 16);
-        const int wsel = (bo & 15) >> 2;
-        const uint32_t word = wsel == 0 ? ch.x : wsel == 1 ? ch.y : wsel == 2 ? ch.z : ch.w;
-        const uint32_t bits = KB == 4 ? word : (word >> (8 * (bo & 3)));
-        const float4 s0 = *reinterpret_cast<const float4*>(kmeta + 8 * cg);
-        const float4 s1 = *reinterpret_cast<const float4*>(kmeta + 8 * cg + 4);
-        const float4 z0 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg);
-        const float4 z1 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg + 4);
-        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      if (NKG % NT == 0 || idx < NKG) {
+        float x[8];
+        if ((mask >> t) & 1u) {
+          const uint4 w = prtbuf[q & 1][gi][tid];
+          x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+          x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+        } else {
+          const uint32_t w = KB == 4 ? words[cg * 32 + t] : words[(cg >> 1) * 32 + t] >> (16 * (cg & 1));
+          float code[8];
+          unpack8<KB>(w, code);
+          const float4 s0 = *reinterpret_cast<const float4*>(kmeta + 8 * cg);
+          const float4 s1 = *reinterpret_cast<const float4*>(kmeta + 8 * cg + 4);
+          const float4 z0 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg);
+          const float4 z1 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg + 4);
+          const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x[e] = fmaf((float)((bits >> (KB * e)) & ((1u << KB) - 1u)), sc[e], zr[e]);
+          for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], sc[e], zr[e]);
+        }
+        const int hh = cg / (D / 16), s = cg % (D / 16);
+        store_hi_lo(kop[ob][0][s][t + 32 * hh], kop[ob][1][s][t + 32 * hh], x, neg_one);
       }
-      const int hh = cg / (D / 16), s = cg % (D / 16);
-      store_hi_lo(kop[ob][0][s][t + 32 * hh], kop[ob][1][s][t + 32 * hh], x);
     }
 #pragma unroll
     for (int vi = 0; vi < VPT; ++vi) {
-      // V: channel c, token octet (mm, hh)
+      // V: channel c, token octet (mm, hh); 4-bit: word 2mm+hh of channel c;
+      // 2-bit: half mm of word hh.
       const int idx = vi * NT + tid, c = idx % D, combo = idx / D;
-      if (NVC % NT != 0 && idx >= NVC) break;
-      const int mm = combo >> 1, hh = combo & 1;
-      uint32_t bits;
-      if (VB == 4) bits = *reinterpret_cast<const uint32_t*>(rawS + KC + c * 16 + (2 * mm + hh) * 4);
-      else         bits = *reinterpret_cast<const uint32_t*>(rawS + KC + c * 8 + hh * 4) >> (16 * mm);
-      const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (c >> a.gv_log2) * 256);
-      const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
-      const float4 s0 = *reinterpret_cast<const float4*>(vs + ta);
-      const float4 s1 = *reinterpret_cast<const float4*>(vs + ta + 8);
-      const float4 z0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
-      const float4 z1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
-      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      float x[8];
+      if (NVC % NT == 0 || idx < NVC) {
+        const int mm = combo >> 1, hh = combo & 1;
+        const uint32_t w = VB == 4 ? words[KC / 4 + (2 * mm + hh) * D + c]
+                                   : words[KC / 4 + hh * D + c] >> (16 * mm);
+        float code[8];
+        unpack8<VB>(w, code);
+        const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (c >> a.gv_log2) * 256);
+        const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
+        const float4 s0 = *reinterpret_cast<const float4*>(vs + ta);
+        const float4 s1 = *reinterpret_cast<const float4*>(vs + ta + 8);
+        const float4 z0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
+        const float4 z1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = fmaf((float)((bits >> (VB * e)) & ((1u << VB) - 1u)), sc[e], zr[e]);
-      vop[ob][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
+        for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], sc[e], zr[e]);
+        vop[ob][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
+      }
     }
   };
 
@@ -268,8 +290,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);
-    mx = fmaxf(mx, sacc[15]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(fmaxf(mx, sacc[15]));
     const float ms = mx * c2;
     const bool need = ms > m_ref + kRescaleSlack;
     if (__any(need)) {
@@ -283,15 +304,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         for (int i = 0; i < 16; ++i) o[ct][i] *= alpha;
     }
     const float mneg = -m_ref;
-    float psum = 0.f;
+    // P is rounded to fp16 for the PV product; the row sum takes the same
+    // rounded values (v_dot2_f32_f16 against (1, 1)), so numerator and
+    // denominator see identical weights.
     half8 pop[2];
+    float psum = l_run;
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, mneg));
-      psum += pv;
-      pop[i >> 3][i & 7] = static_cast<_Float16>(pv);
+    for (int i = 0; i < 16; i += 2) {
+      const half2_t pp = to_half2(__builtin_amdgcn_exp2f(fmaf(sacc[i], c2, mneg)),
+                                  __builtin_amdgcn_exp2f(fmaf(sacc[i + 1], c2, mneg)));
+      pop[i >> 3][i & 7] = pp.x;
+      pop[i >> 3][(i & 7) + 1] = pp.y;
+      psum = __builtin_amdgcn_fdot2(pp, ones, psum, false);
     }
-    l_run += psum;
+    l_run = psum;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[ob][ct][0][lane], pop[0], o[ct], 0, 0, 0);
@@ -317,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
       load8(a.k_blk, rowe, a.blk_f32, kx);
       load8(a.v_blk, rowe, a.blk_f32, vx);
       const int hh = cg / (D / 16), s = cg % (D / 16);
-      store_hi_lo(kop[1][0][s][t + 32 * hh], kop[1][1][s][t + 32 * hh], kx);
+      store_hi_lo(kop[1][0][s][t + 32 * hh], kop[1][1][s][t + 32 * hh], kx, neg_one);
       *reinterpret_cast<float4*>(stage + t * D + 8 * cg) = make_float4(vx[0], vx[1], vx[2], vx[3]);
       *reinterpret_cast<float4*>(stage + t * D + 8 * cg + 4) = make_float4(vx[4], vx[5], vx[6], vx[7]);
     }
@@ -365,7 +392,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
   // ---------------- epilogue
   if (!active) return;
   const int hq = kvh * r + wave;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   const int j = lane & 31, hh = lane >> 5;
   if (nsplit == 1) {
     const float inv = 1.0f / l_tot;

@@ -136,8 +136,9 @@ __global__ __launch_bounds__(128) void commit_kernel(const CommitArgs a) {
         }
         word |= code << (KB * c);
       }
-      if (KB == 4) *reinterpret_cast<uint32_t*>(rec + t * (D / 2) + 4 * cg) = word;
-      else         *reinterpret_cast<uint16_t*>(rec + t * (D / 4) + 2 * cg) = (uint16_t)word;
+      // word-major: the word holding channel group cg of token t
+      if (KB == 4) *reinterpret_cast<uint32_t*>(rec + (cg * 32 + t) * 4) = word;
+      else         *reinterpret_cast<uint16_t*>(rec + ((cg >> 1) * 32 + t) * 4 + 2 * (cg & 1)) = (uint16_t)word;
     }
   } else {
     // ================= values: per-token groups along G_v channels
@@ -194,10 +195,11 @@ __global__ __launch_bounds__(128) void commit_kernel(const CommitArgs a) {
         // token t0 = 4-aligned group start; its place in the channel row
         const int t0 = tq * TPL + k0;
         const int mm = t0 / 16, hh = (t0 / 4) % 2, eb = 4 * ((t0 / 8) % 2);
+        // word-major: word j of channel ch sits at (j * D + ch) * 4
         if (VB == 4)
-          *reinterpret_cast<uint16_t*>(rec + KC + ch * 16 + (2 * mm + hh) * 4 + eb / 2) = (uint16_t)chunk;
+          *reinterpret_cast<uint16_t*>(rec + KC + ((2 * mm + hh) * D + ch) * 4 + eb / 2) = (uint16_t)chunk;
         else
-          rec[KC + ch * 8 + hh * 4 + 2 * mm + eb / 4] = (uint8_t)chunk;
+          rec[KC + (hh * D + ch) * 4 + 2 * mm + eb / 4] = (uint8_t)chunk;
       }
     }
   }

@@ -39,24 +39,84 @@ __device__ __forceinline__ float load1(const void* base, size_t elem, bool is_f3
   return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[elem]) << 16);
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two fp16 (round to nearest even) in one instruction.
+__device__ __forceinline__ half2_t to_half2(float a, float b) {
+  return __builtin_convertvector((float2_t){a, b}, half2_t);
+}
+
 __device__ __forceinline__ half8 to_half8(const float (&x)[8]) {
   half8 h;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[i]);
+  for (int i = 0; i < 8; i += 2) {
+    const half2_t p = to_half2(x[i], x[i + 1]);
+    h[i] = p.x;
+    h[i + 1] = p.y;
+  }
   return h;
+}
+
+// -1.0f in a register the compiler cannot see through, so that x - (float)h
+// becomes one mixed-precision fma (v_fma_mix_f32) instead of convert + subtract.
+__device__ __forceinline__ float opaque_neg_one() {
+  float m = -1.0f;
+  asm("" : "+s"(m));
+  return m;
+}
+
+// max over the two 32-lane halves of a wave (v_permlane32_swap, no LDS).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // x -> (hi, lo) fp16 pair with hi = fp16(x), lo = fp16(x - hi): hi + lo keeps
 // about 22 significant bits of x.
-__device__ __forceinline__ void store_hi_lo(half8& hi, half8& lo, const float (&x)[8]) {
+__device__ __forceinline__ void store_hi_lo(half8& hi, half8& lo, const float (&x)[8], float neg_one) {
   half8 h, l;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = static_cast<_Float16>(x[i]);
-    l[i] = static_cast<_Float16>(x[i] - static_cast<float>(h[i]));
+  for (int i = 0; i < 8; i += 2) {
+    const half2_t p = to_half2(x[i], x[i + 1]);
+    const half2_t q = to_half2(fmaf(static_cast<float>(p.x), neg_one, x[i]),
+                               fmaf(static_cast<float>(p.y), neg_one, x[i + 1]));
+    h[i] = p.x; h[i + 1] = p.y;
+    l[i] = q.x; l[i + 1] = q.y;
   }
   hi = h;
   lo = l;
+}
+
+// Eight b-bit codes of a u32 as floats.  b = 4: code e at bits [4e, 4e+4);
+// b = 2: code e at bits [2e, 2e+2) (the low 16 bits).  Codes are split into
+// bytes first so that each float comes from one byte-convert instruction.
+template <int B>
+__device__ __forceinline__ void unpack8(uint32_t w, float (&c)[8]) {
+  if (B == 4) {
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // keep the byte split: without the barrier the compiler folds it into
+    // one bit-field extract per code (two instructions per code instead of one)
+    asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[2 * j] = static_cast<float>((lo >> (8 * j)) & 0xFFu);
+      c[2 * j + 1] = static_cast<float>((hi >> (8 * j)) & 0xFFu);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t p = (w >> (2 * j)) & 0x0303u;
+      asm("" : "+v"(p));
+      c[j] = static_cast<float>(p & 0xFFu);
+      c[j + 4] = static_cast<float>(p >> 8);
+    }
+  }
 }
 
 }  // namespace kvq

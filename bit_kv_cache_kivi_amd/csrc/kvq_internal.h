@@ -27,7 +27,7 @@ static_assert(sizeof(CommitTask) == 32, "task layout");
 struct SegPtrs {
   uint8_t* records;     // [B][Hkv][slot_cap] records
   uint8_t* headers;     // [B][slot_cap] 16-byte headers
-  uint16_t* prot_rows;  // [B][prot_cap][Hkv][D] bf16 bits
+  uint16_t* prot_rows;  // [B][Hkv][prot_cap][D] bf16 bits
   int32_t* prot_pos;    // [B][prot_cap]
   int32_t slot_cap;
   int32_t prot_cap;

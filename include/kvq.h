@@ -67,15 +67,17 @@
  *
  * Slot record, one per (segment, sequence b, kv head h, slot s), located at
  *     records_offset[seg] + ((b * Hkv + h) * slot_cap[seg] + s) * record_bytes
- *   Kc    at kc_offset    (= 0): 32 token rows, each D*kb/8 bytes = D*kb/32 u32.
- *         Word w of row t holds channels [w*32/kb, (w+1)*32/kb); channel c sits
- *         at bits [kb*(c mod 32/kb), +kb).
- *   Vc    at vc_offset    (= 32*D*kb/8): D channel rows, each vb u32.
- *         Token t of channel c is placed by
+ *   Kc    at kc_offset    (= 0): D*kb/32 word columns of 32 tokens; word w
+ *         of token t is the u32 at byte (w*32 + t)*4.  Word w holds channels
+ *         [w*32/kb, (w+1)*32/kb); channel c sits at bits [kb*(c mod 32/kb), +kb).
+ *   Vc    at vc_offset    (= 32*D*kb/8): vb word rows of D channels; word j of
+ *         channel c is the u32 at byte (j*D + c)*4.  Token t of channel c is
+ *         placed by
  *             mm = t / 16,  h = (t / 4) % 2,  e = (t % 4) + 4 * ((t / 8) % 2)
  *         vb = 4: word 2*mm + h, bits [4e, 4e+4)
  *         vb = 2: word h,        bits [2*(8*mm + e), +2)
- *         (this order puts the 8 tokens one MFMA lane consumes in one u32).
+ *         (this order puts the 8 tokens one MFMA lane consumes in one u32, and
+ *         the word-major order lets consecutive threads read consecutive words).
  *   Kmeta at kmeta_offset (= vc_offset + 4*D*vb): fp32 scale[D], fp32 zero[D].
  *   Vmeta at vmeta_offset (= kmeta_offset + 8*D): for each channel group
  *         g < D/G_v: fp32 scale[32 tokens], fp32 zero[32 tokens].

@@ -9,10 +9,11 @@ loops over bit fields, independently of the kernels, so that the GPU's bytes can
 be compared with the oracle's.
 
 A slot record holds one 32-token group of one (sequence, kv head):
-    Kc    32 token rows x D*kb/32 u32; word w of row t holds channels
-          [w*32/kb, (w+1)*32/kb), channel c at bits kb*(c mod 32/kb)
-    Vc    D channel rows x vb u32; token t goes to (word, first bit) given by
-          v_token_position(t, vb)
+    Kc    D*kb/32 word columns x 32 tokens: word w of token t at byte
+          (w*32 + t)*4; word w holds channels [w*32/kb, (w+1)*32/kb), channel c
+          at bits kb*(c mod 32/kb)
+    Vc    vb word rows x D channels: word j of channel c at byte (j*D + c)*4;
+          token t goes to (word, first bit) given by v_token_position(t, vb)
     Kmeta fp32 scale[D], fp32 zero[D]
     Vmeta per channel group g < D/G_v: fp32 scale[32], fp32 zero[32]
 padded with zero bytes to a multiple of 256.
@@ -94,8 +95,8 @@ def pack_record(kcodes, vcodes, kscale, kzero, vscale, vzero, kb: int, vb: int, 
         b = np.ascontiguousarray(arr).reshape(n, -1).view(np.uint8)
         out[:, off:off + b.shape[1]] = b
 
-    put(lay["kc_offset"], pack_k_words(kcodes, kb).astype("<u4"))
-    put(lay["vc_offset"], pack_v_words(vcodes, vb).astype("<u4"))
+    put(lay["kc_offset"], np.swapaxes(pack_k_words(kcodes, kb), -1, -2).astype("<u4"))   # [.., word, token]
+    put(lay["vc_offset"], np.swapaxes(pack_v_words(vcodes, vb), -1, -2).astype("<u4"))   # [.., word, channel]
     put(lay["kmeta_offset"], np.concatenate([np.asarray(kscale, "<f4"), np.asarray(kzero, "<f4")], axis=-1))
     vm = np.stack([np.asarray(vscale, "<f4"), np.asarray(vzero, "<f4")], axis=-2)   # [..., G, 2, 32]
     put(lay["vmeta_offset"], vm)
@@ -114,12 +115,12 @@ def unpack_record(rec: np.ndarray, D: int, kb: int, vb: int, gv: int) -> dict:
         return rec[:, off:off + count * 4].copy().view(dt)
 
     per = 32 // kb
-    kw = get(lay["kc_offset"], SLOT * D // per, "<u4").reshape(n, SLOT, D // per)
+    kw = np.swapaxes(get(lay["kc_offset"], SLOT * D // per, "<u4").reshape(n, D // per, SLOT), 1, 2)
     kcodes = np.zeros((n, SLOT, D), dtype=np.uint16)
     for c in range(D):
         w, pos = divmod(c, per)
         kcodes[:, :, c] = (kw[:, :, w] >> np.uint32(kb * pos)) & np.uint32(2 ** kb - 1)
-    vw = get(lay["vc_offset"], D * vb, "<u4").reshape(n, D, vb)
+    vw = np.swapaxes(get(lay["vc_offset"], D * vb, "<u4").reshape(n, vb, D), 1, 2)
     vcodes = np.zeros((n, D, SLOT), dtype=np.uint16)
     for t in range(SLOT):
         w, bit = v_token_position(t, vb)

@@ -166,6 +166,22 @@ def test_v_token_positions_by_hand():
     assert w[0, 0] == 0xBA983210 and w[0, 1] == 0xFEDC7654
 
 
+def test_record_words_are_word_major():
+    # Kc: word w of token t at byte (w*32 + t)*4; Vc: word j of channel c at
+    # byte kc_bytes + (j*D + c)*4 (ABI header, packed cache layout).
+    D = 64
+    kcodes = (np.arange(32)[:, None] + 3 * np.arange(D)[None, :]) % 16
+    vcodes = np.tile(np.arange(32) % 16, (D, 1))
+    z = np.zeros
+    rec = O.pack_record(kcodes, vcodes, z(D, F32), z(D, F32), z((1, 32), F32), z((1, 32), F32), 4, 4, 64)
+    u32 = lambda off: int(rec[off:off + 4].view("<u4")[0])
+    assert u32((0 * 32 + 0) * 4) == 0x52FC9630
+    assert u32((1 * 32 + 1) * 4) == 0xEB852FC9
+    kc = 32 * D * 4 // 8
+    assert u32(kc + (0 * D + 0) * 4) == 0xBA983210
+    assert u32(kc + (1 * D + 5) * 4) == 0xFEDC7654
+
+
 def test_pack_unpack_round_trip():
     g = np.random.default_rng(5)
     for (D, kb, vb, gv) in [(128, 4, 4, 64), (128, 2, 2, 64), (64, 4, 2, 32), (128, 2, 4, 128)]:
