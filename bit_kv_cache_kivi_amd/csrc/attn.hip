@@ -6,27 +6,27 @@
 // Q-MaskAhead attends from low-bit KV; SoloQ summary page: bidirectional
 // context revisited every step; Tai et al., abstract: prefix and dual cache).
 //
-// Work unit = one 32-token slot of the cache, or the block itself.  A
-// workgroup owns one (sequence, kv head) and a contiguous range of units.
-// Each wave owns one query head of that kv head (32 query tokens = one 32-wide
-// MFMA tile); with NW = 8 waves two waves share each SIMD, so one wave's MFMA
-// work overlaps the other's softmax and dequantization.  A slot is dequantized
-// once per workgroup and shared by all query heads through LDS.
-//
-// Per slot, as a software pipeline with one barrier per slot:
-//   * every thread loads its share of a slot record (16-byte chunks) and, for
-//     protected key tokens, its share of the bf16 rows into registers with
-//     buffer loads, four slots ahead; two slots later it stores them into one
-//     of two LDS stages, so each load has two pipeline steps to arrive;
-//   * all threads dequantize the next slot into fp16 MFMA operand tiles
-//     (double-buffered): K as an fp16 hi + lo pair (the scores then keep about
-//     22 bits of the dequantized keys), V as fp16;
-//   * each wave runs S^T = K Q^T on v_mfma_f32_32x32x16_f16, an online softmax
-//     in fp32 (exp2 with the scale folded in; the reference maximum is raised
-//     only when the running maximum exceeds it by more than 2^8, so O is
-//     rarely rescaled), and O^T += V^T P^T.  The transposed products let the S
+// Work unit = one 32-token slot of the cache, or the block itself (the last
+// unit of the split that holds it).  A workgroup owns one (sequence, kv head)
+// and a contiguous range of units, and is split into two roles:
+//   * 4 producer waves (one per SIMD) stream the packed slot records and the
+//     protected bf16 key rows from HBM (buffer loads into registers, three
+//     units ahead), stage them in LDS, and dequantize each unit into fp16 MFMA
+//     operand tiles: K as an fp16 hi + lo pair (the scores keep about 22 bits
+//     of the dequantized keys), V as fp16;
+//   * one consumer wave per query head of the kv head (32 query tokens = one
+//     32-wide MFMA tile) runs S^T = K Q^T on v_mfma_f32_32x32x16_f16, an online
+//     softmax in fp32 (exp2 with the scale folded in; the reference maximum is
+//     raised only when the running maximum exceeds it by more than 2^8, so O is
+//     rarely rescaled) and O^T += V^T P^T.  The transposed products let the S
 //     accumulators feed the PV B operand directly (lane = query, 16 tokens per
 //     lane).
+// A slot is dequantized once per workgroup and shared by all query heads
+// through LDS.  One barrier per unit: in interval i producers store unit i+1,
+// dequantize unit i and issue the loads of unit i+3, while consumers work on
+// unit i-1.  Consumers 4..7 run half a unit behind (softmax and PV of unit
+// i-2, then the scores of unit i-1), so on each SIMD one consumer's MFMA work
+// overlaps the other consumer's softmax and the producer's dequantization.
 // A split's partial (reference maximum, sum, unnormalised O) goes to the
 // workspace and the combine kernel merges splits with log-sum-exp weights; a
 // single split writes the normalised output itself.
@@ -36,113 +36,102 @@
 namespace kvq {
 namespace {
 
-constexpr int kStage = 8192;       // bytes of one LDS record stage (>= any record)
 constexpr int kMaxUnits = 256;     // units per split (the host keeps splits within this)
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kMaxSplitsLds = 256;   // splits the combine can merge (host limit on max_splits)
+constexpr int kProducerWaves = 4;
+constexpr int kProducerThreads = kProducerWaves * 64;
 
-template <int KB, int VB, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
-  constexpr int NT = NW * 64;                // threads
-  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
-  constexpr int CT = D / 32;                 // 32-channel output tiles
-  constexpr int NG = D / 8;                  // 8-channel groups of a token row
-  constexpr int NKG = kSlot * NG;            // (token, 8-channel group) pairs of K
-  constexpr int NVC = D * 4;                 // (channel, token-octet) pairs of V
-  constexpr int GPT = (NKG + NT - 1) / NT;   // K groups dequantized per thread
-  constexpr int VPT = (NVC + NT - 1) / NT;   // V pairs dequantized per thread
-  constexpr int RPT = kStage / 16 / NT;      // record chunks loaded per thread
+template <class T>
+__device__ __forceinline__ T pick(bool c, T x, T y) { return c ? x : y; }
+
+template <int D>
+struct Shape {
+  static constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
+  static constexpr int CT = D / 32;                  // 32-channel output tiles
+  static constexpr int NKG = kSlot * (D / 8);        // (token, 8-channel group) pairs of K
+  static constexpr int NVC = D * 4;                  // (channel, token-octet) pairs of V
+  static constexpr int GPT = NKG / kProducerThreads; // K groups per producer thread
+  static constexpr int VPT = NVC / kProducerThreads; // V pairs per producer thread
+  // one LDS stage holds a slot record (at most 48*D bytes) or the block as
+  // fp32 K rows followed by fp16 V rows (192*D bytes)
+  static constexpr int STAGE = 192 * D;
+  static constexpr int RPT = (48 * D / 16 + kProducerThreads - 1) / kProducerThreads;   // record chunks per thread
+  static_assert(NKG % kProducerThreads == 0 && NVC % kProducerThreads == 0, "thread mapping");
+  static_assert(RPT >= GPT, "the block's K rows use the record prefetch slots");
+};
+
+template <int KB, int VB, int D, int NC>
+__global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const AttnArgs a) {
+  using S = Shape<D>;
+  constexpr int KS = S::KS, CT = S::CT, GPT = S::GPT, VPT = S::VPT, RPT = S::RPT;
+  constexpr int NPT = kProducerThreads;
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
   constexpr uint32_t KM = kmeta_bytes(D);
-  static_assert(GPT >= 1 && VPT >= 1 && RPT >= 1, "thread mapping");
-  static_assert(record_bytes(D, KB, VB, 32) <= kStage, "record fits a stage");
+  static_assert(record_bytes(D, KB, VB, 32) <= 48 * D, "record fits a stage");
 
-  __shared__ __align__(16) uint8_t rawbuf[2][kStage];       // packed slot records
-  __shared__ __align__(16) uint4 prtbuf[2][GPT][NT];        // this thread's protected-row chunks
-  __shared__ __align__(16) half8 kop[2][2][KS][64];         // [buffer][hi, lo][k-step][lane]
-  __shared__ __align__(16) half8 vop[2][CT][2][64];         // [buffer][channel tile][k-half][lane]
+  __shared__ __align__(16) uint8_t rawbuf[2][S::STAGE];      // packed slot records / the block
+  __shared__ __align__(16) uint4 prtbuf[2][GPT][NPT];        // a producer thread's protected-row chunks
+  __shared__ __align__(16) half8 kop[2][2][KS][64];          // [buffer][hi, lo][k-step][lane]
+  __shared__ __align__(16) half8 vop[3][CT][2][64];          // [buffer][channel tile][k-half][lane]
   __shared__ __align__(16) int4 hdr[kMaxUnits];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // Kernel-argument fields as locals: lambdas below capture these, never the
+  // argument struct itself (capturing it by reference would copy the whole
+  // struct to scratch memory).
+  const int hkv = a.hkv, hq_all = a.hq, gv_log2 = a.gv_log2;
+  const bool blk_f32 = a.blk_f32, q_f32 = a.q_f32;
+  const void* const q_ptr = a.q;
+  const void* const k_blk = a.k_blk;
+  const void* const v_blk = a.v_blk;
+  const SegPtrs seg0 = a.seg[0], seg1 = a.seg[1];
   const int np = a.nslots[0][b];
   const int ns = a.use_suffix ? a.nslots[1][b] : 0;
-  const int U = np + ns + 1;                 // slots + the block itself (last unit)
+  const int U = np + ns + 1;                 // slots + the block itself
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (split >= nsplit) return;
   const int u0 = split * a.split_units;
   const int u1 = min(U, u0 + a.split_units);
-  const int nq = min(u1, U - 1) - u0;        // quantized units of this split
+  const int nq = min(u1, U - 1) - u0;        // slot units of this split
   const bool has_block = u1 == U;
+  const int NU = nq + (has_block ? 1 : 0);   // units; the block, if here, is unit nq
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < kProducerWaves;
+  const int ci = wave - kProducerWaves;      // consumer index = query head kvh*r + ci
+  const bool late = NC > 4 && ci >= 4;
   const int r = a.r;
-  const bool active = wave < r;              // this wave owns query head kvh*r + wave
   const uint32_t rbytes = a.record_bytes;
   const float c2 = a.scale_log2;
 
   auto seg_of = [&](int u) { return u < np ? 0 : 1; };
   auto slot_of = [&](int u) { return u < np ? u : u - np; };
 
-  // ---------------- prologue: Q operands, slot headers
-  // Q is the B operand of S^T: lane = query token j; half hh holds channels
-  // (D/2)*hh + 8s + [0, 8) at k-step s.
+  // ---------------- prologues (run inside the role branches below): headers
+  // and the block's raw rows (producers), Q operands (consumers)
   half8 qop[KS];
-  {
-    const int j = lane & 31, hh = lane >> 5;
-    const int hq = kvh * r + (active ? wave : 0);
-    const size_t base = (((size_t)b * kSlot + j) * a.hq + hq) * D + (D / 2) * hh;
-    if (a.q_f32) {
-      float4 raw[KS][2];
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + base);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) { raw[s][0] = p[2 * s]; raw[s][1] = p[2 * s + 1]; }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float x[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
-                            raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
-        qop[s] = to_half8(x);
-      }
-    } else {
-      uint4 raw[KS];
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + base);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) raw[s] = p[s];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float x[8] = {bf16_lo(raw[s].x), bf16_hi(raw[s].x), bf16_lo(raw[s].y), bf16_hi(raw[s].y),
-                            bf16_lo(raw[s].z), bf16_hi(raw[s].z), bf16_lo(raw[s].w), bf16_hi(raw[s].w)};
-        qop[s] = to_half8(x);
-      }
-    }
-  }
-  for (int i = tid; i < nq; i += NT) {
-    const int u = u0 + i, seg = seg_of(u);
-    const uint8_t* hb = seg ? a.seg[1].headers : a.seg[0].headers;
-    const int cap = seg ? a.seg[1].slot_cap : a.seg[0].slot_cap;
-    hdr[i] = *reinterpret_cast<const int4*>(hb + ((size_t)b * cap + slot_of(u)) * kHeaderBytes);
-  }
-  __syncthreads();
 
-  // ---------------- register prefetch of one unit: the slot record (16-byte
-  // chunks, as laid out in memory) and this thread's chunk of a protected bf16
-  // key row.  Buffer loads: their range check turns reads past a segment, or
-  // of rows a thread does not need, into zeros without memory traffic, so
-  // every thread issues the same loads per unit and they stay independent
-  // in-flight loads.
-  // The descriptor of a unit's segment is rebuilt per unit from base and size
-  // values passed through readfirstlane: a descriptor chosen by a select is
-  // taken as divergent and would force a per-lane loop around every load.
-  const uint8_t* rec_base0 = a.seg[0].records + ((size_t)b * a.hkv + kvh) * a.seg[0].slot_cap * rbytes;
-  const uint8_t* rec_base1 = a.seg[1].records + ((size_t)b * a.hkv + kvh) * a.seg[1].slot_cap * rbytes;
-  const int rec_n0 = (int)min((size_t)a.seg[0].slot_cap * rbytes, (size_t)0x7fffffff);
-  const int rec_n1 = (int)min((size_t)a.seg[1].slot_cap * rbytes, (size_t)0x7fffffff);
-  const uint16_t* prot_base0 = a.seg[0].prot_rows + ((size_t)b * a.hkv + kvh) * a.seg[0].prot_cap * D;
-  const uint16_t* prot_base1 = a.seg[1].prot_rows + ((size_t)b * a.hkv + kvh) * a.seg[1].prot_cap * D;
-  const int prot_n0 = (int)min((size_t)a.seg[0].prot_cap * D * 2, (size_t)0x7fffffff);
-  const int prot_n1 = (int)min((size_t)a.seg[1].prot_cap * D * 2, (size_t)0x7fffffff);
+  // ---------------- producers: register prefetch of one unit -- the slot
+  // record (16-byte chunks, as laid out in memory) and this thread's chunks of
+  // protected bf16 key rows.  Buffer loads: their range check turns reads past
+  // a segment, or of rows a thread does not need, into zeros without memory
+  // traffic, so every thread issues the same loads per unit and they stay
+  // independent in-flight loads.  The descriptor of a unit's segment is
+  // rebuilt per unit from values passed through readfirstlane: a descriptor
+  // chosen by a select is taken as divergent and would force a per-lane loop
+  // around every load.
+  const uint8_t* rec_base0 = seg0.records + ((size_t)b * hkv + kvh) * seg0.slot_cap * rbytes;
+  const uint8_t* rec_base1 = seg1.records + ((size_t)b * hkv + kvh) * seg1.slot_cap * rbytes;
+  const int rec_n0 = (int)min((size_t)seg0.slot_cap * rbytes, (size_t)0x7fffffff);
+  const int rec_n1 = (int)min((size_t)seg1.slot_cap * rbytes, (size_t)0x7fffffff);
+  const uint16_t* prot_base0 = seg0.prot_rows + ((size_t)b * hkv + kvh) * seg0.prot_cap * D;
+  const uint16_t* prot_base1 = seg1.prot_rows + ((size_t)b * hkv + kvh) * seg1.prot_cap * D;
+  const int prot_n0 = (int)min((size_t)seg0.prot_cap * D * 2, (size_t)0x7fffffff);
+  const int prot_n1 = (int)min((size_t)seg1.prot_cap * D * 2, (size_t)0x7fffffff);
   auto uniform_rsrc = [](const void* p, int n) __attribute__((always_inline)) {
     const uint64_t v = (uint64_t)p;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -151,22 +140,36 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
                                              __builtin_amdgcn_readfirstlane(n), 0x00020000);
   };
   struct Pre { uint4 rec[RPT]; uint4 prt[GPT]; };
-  // Loads are issued unconditionally (units past the split read out of range)
-  // so that every path through the loop has the same number of loads in
-  // flight and each store waits only for its own unit's loads.
   constexpr int kOutOfRange = 0x7ff00000;
   bool rec_chunk[RPT];
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) rec_chunk[j] = (uint32_t)(j * NT + tid) * 16u < rbytes;
+  for (int j = 0; j < RPT; ++j) rec_chunk[j] = (uint32_t)(j * NPT + tid) * 16u < rbytes;
+  // Loads are issued unconditionally (units past the slots read out of range)
+  // so that every path has the same number of loads in flight.
+  // The block unit (bf16 input) takes the same loads: its K rows through the
+  // record descriptor slots and its V rows through the protected-row slots.
+  const uint8_t* kblk_base = static_cast<const uint8_t*>(k_blk) + ((size_t)b * kSlot * hkv + kvh) * D * 2;
+  const uint8_t* vblk_base = static_cast<const uint8_t*>(v_blk) + ((size_t)b * kSlot * hkv + kvh) * D * 2;
+  const int blk_n = kSlot * hkv * D * 2;
+  const int blk_row = hkv * D * 2;                 // bytes between the block's token rows
   auto load_unit = [&](int q, Pre& pr) __attribute__((always_inline)) {
     const bool valid = q < nq;
+    const bool blk_unit = has_block && q == nq && !blk_f32;
     const int u = u0 + (valid ? q : 0), sg = valid ? seg_of(u) : 0;
-    const __amdgpu_buffer_rsrc_t rr = uniform_rsrc(sg ? rec_base1 : rec_base0, sg ? rec_n1 : rec_n0);
-    const __amdgpu_buffer_rsrc_t prr = uniform_rsrc(sg ? (const void*)prot_base1 : (const void*)prot_base0, sg ? prot_n1 : prot_n0);
+    // (selects on values: a conditional on the captured lvalues would select
+    // their addresses and keep them in scratch memory)
+    const __amdgpu_buffer_rsrc_t rr =
+        uniform_rsrc(pick(blk_unit, (const void*)kblk_base, pick(sg, (const void*)rec_base1, (const void*)rec_base0)),
+                     pick(blk_unit, blk_n, pick(sg, rec_n1, rec_n0)));
+    const __amdgpu_buffer_rsrc_t prr =
+        uniform_rsrc(pick(blk_unit, (const void*)vblk_base, pick(sg, (const void*)prot_base1, (const void*)prot_base0)),
+                     pick(blk_unit, blk_n, pick(sg, prot_n1, prot_n0)));
     const int rbase = slot_of(u) * (int)rbytes;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int off = (valid && rec_chunk[j]) ? rbase + (j * NT + tid) * 16 : kOutOfRange;
+      const int idx = j * NPT + tid;
+      const int boff = j < GPT ? (idx & 31) * blk_row + (idx >> 5) * 16 : kOutOfRange;
+      const int off = blk_unit ? boff : (valid && rec_chunk[j]) ? rbase + idx * 16 : kOutOfRange;
       pr.rec[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
     }
     // header read unconditionally (clamped index) and masked by a select, so
@@ -175,9 +178,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     const uint32_t mask = valid ? (uint32_t)h.y : 0u;
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
-      const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
+      const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
       const int rank = h.z + __popc(mask & ((1u << t) - 1u));
-      const int poff = (idx < NKG && ((mask >> t) & 1u)) ? (rank * D + 8 * cg) * 2 : kOutOfRange;
+      const int poff = blk_unit ? t * blk_row + cg * 16
+                                : ((mask >> t) & 1u) ? (rank * D + 8 * cg) * 2 : kOutOfRange;
       pr.prt[gi] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prr, poff, 0, 0));
     }
   };
@@ -188,31 +192,60 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
   static_assert(kLoadsPerUnit < 16, "vmcnt field");
   auto store_unit = [&](int q, const Pre& pr) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xF70 | kLoadsPerUnit);   // vmcnt(kLoadsPerUnit), others unconstrained
+    uint8_t* stage = rawbuf[q & 1];
+    if (q < nq) {
 #pragma unroll
-    for (int j = 0; j < RPT; ++j)
-      if (rec_chunk[j]) *reinterpret_cast<uint4*>(rawbuf[q & 1] + (j * NT + tid) * 16) = pr.rec[j];
-    const uint32_t mask = q < nq ? (uint32_t)hdr[min(q, kMaxUnits - 1)].y : 0u;
+      for (int j = 0; j < RPT; ++j)
+        if (rec_chunk[j]) *reinterpret_cast<uint4*>(stage + (j * NPT + tid) * 16) = pr.rec[j];
+      const uint32_t mask = (uint32_t)hdr[q].y;
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
-      const int idx = gi * NT + tid, t = idx & 31;
-      if ((mask >> t) & 1u) prtbuf[q & 1][gi][tid] = pr.prt[gi];
+      for (int gi = 0; gi < GPT; ++gi) {
+        const int t = (gi * NPT + tid) & 31;
+        if ((mask >> t) & 1u) prtbuf[q & 1][gi][tid] = pr.prt[gi];
+      }
+    } else if (q == nq && has_block) {
+      // the block: K rows as fp32 [32][D], then V rows as fp16 [32][D]; bf16
+      // rows arrived through the prefetch registers, fp32 rows are read here
+      float* kst = reinterpret_cast<float*>(stage);
+      _Float16* vst = reinterpret_cast<_Float16*>(stage + kSlot * D * 4);
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi) {
+        const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
+        float kx[8], vx[8];
+        if (blk_f32) {
+          const size_t e = (((size_t)b * kSlot + t) * hkv + kvh) * D + 8 * cg;
+          load8(k_blk, e, true, kx);
+          load8(v_blk, e, true, vx);
+        } else {
+          const uint4 k0 = pr.rec[gi], v0 = pr.prt[gi];
+          kx[0] = bf16_lo(k0.x); kx[1] = bf16_hi(k0.x); kx[2] = bf16_lo(k0.y); kx[3] = bf16_hi(k0.y);
+          kx[4] = bf16_lo(k0.z); kx[5] = bf16_hi(k0.z); kx[6] = bf16_lo(k0.w); kx[7] = bf16_hi(k0.w);
+          vx[0] = bf16_lo(v0.x); vx[1] = bf16_hi(v0.x); vx[2] = bf16_lo(v0.y); vx[3] = bf16_hi(v0.y);
+          vx[4] = bf16_lo(v0.z); vx[5] = bf16_hi(v0.z); vx[6] = bf16_lo(v0.w); vx[7] = bf16_hi(v0.w);
+        }
+        float* kd = kst + t * D + 8 * cg;
+        *reinterpret_cast<float4*>(kd) = make_float4(kx[0], kx[1], kx[2], kx[3]);
+        *reinterpret_cast<float4*>(kd + 4) = make_float4(kx[4], kx[5], kx[6], kx[7]);
+        *reinterpret_cast<half8*>(vst + t * D + 8 * cg) = to_half8(vx);
+      }
     }
   };
 
-  // ---------------- dequantize unit q into operand buffer q & 1
+  // ---------------- producers: dequantize unit q into K buffer q & 1 and
+  // V buffer q % 3
   const float neg_one = opaque_neg_one();
   auto dequant = [&](int q) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
-    const int ob = q & 1;
-    const uint32_t mask = (uint32_t)hdr[q].y;
-    const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC);
+    const int kb = q & 1, vbuf = q % 3;
+    if (q < nq) {
+      const uint32_t mask = (uint32_t)hdr[q].y;
+      const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC);
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
-      // K: (token t, 8-channel group cg); its codes are word cg (4-bit) or
-      // half cg % 2 of word cg / 2 (2-bit) of token t's word column.
-      const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
-      if (NKG % NT == 0 || idx < NKG) {
+      for (int gi = 0; gi < GPT; ++gi) {
+        // K: (token t, 8-channel group cg); its codes are word cg (4-bit) or
+        // half cg % 2 of word cg / 2 (2-bit) of token t's word column.
+        const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
         float x[8];
         if ((mask >> t) & 1u) {
           const uint4 w = prtbuf[q & 1][gi][tid];
@@ -232,21 +265,19 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
           for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], sc[e], zr[e]);
         }
         const int hh = cg / (D / 16), s = cg % (D / 16);
-        store_hi_lo(kop[ob][0][s][t + 32 * hh], kop[ob][1][s][t + 32 * hh], x, neg_one);
+        store_hi_lo(kop[kb][0][s][t + 32 * hh], kop[kb][1][s][t + 32 * hh], x, neg_one);
       }
-    }
 #pragma unroll
-    for (int vi = 0; vi < VPT; ++vi) {
-      // V: channel c, token octet (mm, hh); 4-bit: word 2mm+hh of channel c;
-      // 2-bit: half mm of word hh.
-      const int idx = vi * NT + tid, c = idx % D, combo = idx / D;
-      if (NVC % NT == 0 || idx < NVC) {
+      for (int vi = 0; vi < VPT; ++vi) {
+        // V: channel c, token octet (mm, hh); 4-bit: word 2mm+hh of channel c;
+        // 2-bit: half mm of word hh.
+        const int idx = vi * NPT + tid, c = idx % D, combo = idx / D;
         const int mm = combo >> 1, hh = combo & 1;
         const uint32_t w = VB == 4 ? words[KC / 4 + (2 * mm + hh) * D + c]
                                    : words[KC / 4 + hh * D + c] >> (16 * mm);
         float code[8];
         unpack8<VB>(w, code);
-        const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (c >> a.gv_log2) * 256);
+        const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (c >> gv_log2) * 256);
         const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
         const float4 s0 = *reinterpret_cast<const float4*>(vs + ta);
         const float4 s1 = *reinterpret_cast<const float4*>(vs + ta + 8);
@@ -257,28 +288,70 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], sc[e], zr[e]);
-        vop[ob][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
+        vop[vbuf][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
+      }
+    } else if (q == nq && has_block) {
+      const float* kst = reinterpret_cast<const float*>(rawS);
+      const _Float16* vst = reinterpret_cast<const _Float16*>(rawS + kSlot * D * 4);
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi) {
+        const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
+        const float4 x0 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg);
+        const float4 x1 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg + 4);
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const int hh = cg / (D / 16), s = cg % (D / 16);
+        store_hi_lo(kop[kb][0][s][t + 32 * hh], kop[kb][1][s][t + 32 * hh], x, neg_one);
+      }
+#pragma unroll
+      for (int vi = 0; vi < VPT; ++vi) {
+        const int idx = vi * NPT + tid, c = idx % D, combo = idx / D;
+        const int mm = combo >> 1, hh = combo & 1;
+        half8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = vst[(16 * mm + 4 * hh + (e & 3) + 8 * (e >> 2)) * D + c];
+        vop[vbuf][c >> 5][mm][(c & 31) + 32 * hh] = v;
       }
     }
   };
 
-  // ---------------- this wave's MFMA + online softmax over operand buffer ob
+  // ---------------- consumers: scores of unit q (part 1) and softmax + PV of
+  // unit q (part 2)
   float m_ref = -__builtin_inff(), l_run = 0.f;
   floatx16 o[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[ct][i] = 0.f;
-  auto compute = [&](int ob, int nvalid) __attribute__((always_inline)) {
-    if (!active) return;
-    floatx16 sacc;
+  floatx16 sacc;
+  // The operand tiles are read from LDS a few k-steps ahead of the MFMAs
+  // that use them (the scheduling barriers pin the interleave; left alone
+  // the compiler issues each read right before its MFMA and waits for it).
+  auto scores = [&](int q) __attribute__((always_inline)) {
+    const int kb = q & 1;
+    half8 kh[KS], kl[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) { kh[s] = kop[kb][0][s][lane]; kl[s] = kop[kb][1][s][lane]; }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[ob][0][s][lane], qop[s], sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[ob][1][s][lane], qop[s], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[s], qop[s], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl[s], qop[s], sacc, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // 4 LDS reads ahead
+#pragma unroll
+    for (int k = 0; k < 2 * KS - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  auto softmax_pv = [&](int q) __attribute__((always_inline)) {
+    const int vbuf = q % 3;
+    const int nvalid = hdr[q].x;
+    half8 va[CT][2];                     // first k-half of the V operands, read before the softmax
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) va[ct][0] = vop[vbuf][ct][0][lane];
     // sacc[i] = S[query lane%32][token 8*(i/4) + 4*(lane/32) + i%4]
     if (nvalid < kSlot) {
 #pragma unroll
@@ -320,83 +393,111 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     }
     l_run = psum;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[ob][ct][0][lane], pop[0], o[ct], 0, 0, 0);
-      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[ob][ct][1][lane], pop[1], o[ct], 0, 0, 0);
-    }
+    for (int ct = 0; ct < CT; ++ct) va[ct][1] = vop[vbuf][ct][1][lane];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ct][0], pop[0], o[ct], 0, 0, 0);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ct][1], pop[1], o[ct], 0, 0, 0);
   };
 
-  // ---------------- pipeline prologue
-  Pre pre0, pre1;
-  load_unit(0, pre0);
-  load_unit(1, pre1);
-  if (has_block) {
-    // the full-precision block -> operand buffer 1 (K hi/lo directly; V via a
-    // [token][channel] fp32 staging transpose in buffer 0, which the first
-    // slot overwrites only after the next barrier)
-    float* stage = reinterpret_cast<float*>(&kop[0][0][0][0]);   // 32 x D fp32
-#pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
-      const int idx = gi * NT + tid, t = idx & 31, cg = idx >> 5;
-      if (NKG % NT != 0 && idx >= NKG) break;
-      const size_t rowe = (((size_t)b * kSlot + t) * a.hkv + kvh) * D + 8 * cg;
-      float kx[8], vx[8];
-      load8(a.k_blk, rowe, a.blk_f32, kx);
-      load8(a.v_blk, rowe, a.blk_f32, vx);
-      const int hh = cg / (D / 16), s = cg % (D / 16);
-      store_hi_lo(kop[1][0][s][t + 32 * hh], kop[1][1][s][t + 32 * hh], kx, neg_one);
-      *reinterpret_cast<float4*>(stage + t * D + 8 * cg) = make_float4(vx[0], vx[1], vx[2], vx[3]);
-      *reinterpret_cast<float4*>(stage + t * D + 8 * cg + 4) = make_float4(vx[4], vx[5], vx[6], vx[7]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int vi = 0; vi < VPT; ++vi) {
-      const int idx = vi * NT + tid, c = idx % D, combo = idx / D;
-      if (NVC % NT != 0 && idx >= NVC) break;
-      const int mm = combo >> 1, hh = combo & 1;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = stage[(16 * mm + 4 * hh + (e & 3) + 8 * (e >> 2)) * D + c];
-      vop[1][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
-    }
-    __syncthreads();
-    compute(1, kSlot);
-  }
-  if (nq > 0) {
+  // ---------------- pipeline.  Interval i: producers store unit i+1 (register
+  // set (i+1) & 1), dequantize unit i and load unit i+3 into the freed set;
+  // early consumers take unit i-1; late consumers finish unit i-2 and score
+  // unit i-1.  Producers and consumers run separate loops with the same
+  // barrier count (the branch is uniform per wave), so neither role holds the
+  // other's loop-carried registers.
+  // intervals, rounded up to even so that the producer loop (unrolled by two
+  // for its two register sets) has no conditional half: a conditional half
+  // would merge register states at the latch and force waits on in-flight loads
+  const int n_int = (NU + (NC > 4 ? 2 : 1) + 1) & ~1;
+  if (producer) {
+      for (int i = tid; i < nq; i += NPT) {
+        const int u = u0 + i, seg = seg_of(u);
+        const uint8_t* hb = seg ? seg1.headers : seg0.headers;
+        const int cap = seg ? seg1.slot_cap : seg0.slot_cap;
+        hdr[i] = *reinterpret_cast<const int4*>(hb + ((size_t)b * cap + slot_of(u)) * kHeaderBytes);
+      }
+      if (tid == 0 && has_block) hdr[nq] = make_int4(kSlot, 0, 0, 0);
+    __syncthreads();                         // headers in LDS
+    Pre pre0, pre1;
+    load_unit(0, pre0);
+    load_unit(1, pre1);
     store_unit(0, pre0);
     load_unit(2, pre0);
     __syncthreads();
-    dequant(0);
-    store_unit(1, pre1);
-    load_unit(3, pre1);
-    __syncthreads();
-
-    // ---------------- steady state, unrolled by two (register set = q & 1)
-    // Both halves always run their loads, stores and barriers (past the last
-    // unit they touch only out-of-range data and unused stages), so the number
-    // of loads in flight is the same on every path.
-    for (int q = 0; q < nq; q += 2) {
-      store_unit(q + 2, pre0);
-      if (q + 1 < nq) dequant(q + 1);
-      compute(0, hdr[q].x);
-      load_unit(q + 4, pre0);
+    for (int i = 0; i < n_int; i += 2) {
+      store_unit(i + 1, pre1);
+      if (i < NU) dequant(i);
+      load_unit(i + 3, pre1);
       __syncthreads();
-      store_unit(q + 3, pre1);
-      if (q + 2 < nq) dequant(q + 2);
-      if (q + 1 < nq) compute(1, hdr[q + 1].x);
-      load_unit(q + 5, pre1);
+      store_unit(i + 2, pre0);
+      if (i + 1 < NU) dequant(i + 1);
+      load_unit(i + 4, pre0);
+      __syncthreads();
+    }
+    return;
+  }
+  {
+    // Q is the B operand of S^T: lane = query token j; half hh holds channels
+    // (D/2)*hh + 8s + [0, 8) at k-step s.
+    const int j = lane & 31, hh = lane >> 5;
+    const int hq = kvh * r + ci;
+    const size_t base = (((size_t)b * kSlot + j) * hq_all + hq) * D + (D / 2) * hh;
+    if (q_f32) {
+      float4 raw[KS][2];
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q_ptr) + base);
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) { raw[s][0] = p[2 * s]; raw[s][1] = p[2 * s + 1]; }
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float x[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
+                            raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
+        qop[s] = to_half8(x);
+      }
+    } else {
+      uint4 raw[KS];
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_ptr) + base);
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) raw[s] = p[s];
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float x[8] = {bf16_lo(raw[s].x), bf16_hi(raw[s].x), bf16_lo(raw[s].y), bf16_hi(raw[s].y),
+                            bf16_lo(raw[s].z), bf16_hi(raw[s].z), bf16_lo(raw[s].w), bf16_hi(raw[s].w)};
+        qop[s] = to_half8(x);
+      }
+    }
+  }
+  __syncthreads();
+  __syncthreads();
+  if (ci >= r) {
+    for (int i = 0; i < n_int; ++i) __syncthreads();
+    return;
+  }
+  if (late) {
+    for (int i = 0; i < n_int; ++i) {
+      if (i >= 2 && i - 2 < NU) softmax_pv(i - 2);
+      if (i >= 1 && i - 1 < NU) scores(i - 1);
+      __syncthreads();
+    }
+  } else {
+    for (int i = 0; i < n_int; ++i) {
+      if (i >= 1 && i - 1 < NU) {
+        scores(i - 1);
+        softmax_pv(i - 1);
+      }
       __syncthreads();
     }
   }
 
-  // ---------------- epilogue
-  if (!active) return;
-  const int hq = kvh * r + wave;
+  // ---------------- epilogue (consumers)
+  const int hq = kvh * r + ci;
   const float l_tot = sum_halves(l_run);
   const int j = lane & 31, hh = lane >> 5;
   if (nsplit == 1) {
     const float inv = 1.0f / l_tot;
-    const size_t row = ((size_t)b * kSlot + j) * a.hq + hq;
+    const size_t row = ((size_t)b * kSlot + j) * hq_all + hq;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -414,7 +515,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         }
       }
   } else {
-    const size_t pidx = (((size_t)b * a.hkv + kvh) * a.max_splits + split) * r + wave;
+    const size_t pidx = (((size_t)b * hkv + kvh) * a.max_splits + split) * r + ci;
     float* base = a.partial + pidx * (size_t)(D + 2) * kSlot;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -521,8 +622,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
 template <int KB, int VB, int D>
 hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
   dim3 grid(grid_splits, a.hkv, B);
-  if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4>), grid, dim3(256), 0, s, a);
-  else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8>), grid, dim3(512), 0, s, a);
+  const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
+  if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4>), grid, block, 0, s, a);
+  else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8>), grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B), dim3(256), 0, s, a);
