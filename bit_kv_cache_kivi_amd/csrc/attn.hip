@@ -139,7 +139,16 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0,
                                              __builtin_amdgcn_readfirstlane(n), 0x00020000);
   };
-  struct Pre { uint4 rec[RPT]; uint4 prt[GPT]; };
+  struct Pre { uint4 rec[RPT]; uint4 prt[GPT]; uint32_t mask; };
+  // Producer thread -> work mapping.  K: the thread's GPT (token, 8-channel
+  // group) pairs share the group (tokens kt0 + KTT*gi of group kcg), so the
+  // group's scales and zeros are read once.  V: the thread's VPT (channel,
+  // token octet) pairs share the octet and the channel group (channels
+  // vc0 + vi of octet vcombo), so the tokens' scales and zeros are read once.
+  constexpr int KTT = kSlot / GPT;
+  constexpr int VCT = D / VPT;
+  const int kt0 = tid % KTT, kcg = tid / KTT;
+  const int vc0 = VPT * (tid % VCT), vcombo = tid / VCT;
   constexpr int kOutOfRange = 0x7ff00000;
   bool rec_chunk[RPT];
 #pragma unroll
@@ -168,7 +177,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int idx = j * NPT + tid;
-      const int boff = j < GPT ? (idx & 31) * blk_row + (idx >> 5) * 16 : kOutOfRange;
+      const int boff = j < GPT ? (kt0 + KTT * j) * blk_row + kcg * 16 : kOutOfRange;
       const int off = blk_unit ? boff : (valid && rec_chunk[j]) ? rbase + idx * 16 : kOutOfRange;
       pr.rec[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
     }
@@ -176,9 +185,10 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     // no branch splits the loads of a unit
     const int4 h = hdr[min(q, kMaxUnits - 1)];
     const uint32_t mask = valid ? (uint32_t)h.y : 0u;
+    pr.mask = mask;
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
-      const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
+      const int t = kt0 + KTT * gi, cg = kcg;
       const int rank = h.z + __popc(mask & ((1u << t) - 1u));
       const int poff = blk_unit ? t * blk_row + cg * 16
                                 : ((mask >> t) & 1u) ? (rank * D + 8 * cg) * 2 : kOutOfRange;
@@ -197,11 +207,10 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 #pragma unroll
       for (int j = 0; j < RPT; ++j)
         if (rec_chunk[j]) *reinterpret_cast<uint4*>(stage + (j * NPT + tid) * 16) = pr.rec[j];
-      const uint32_t mask = (uint32_t)hdr[q].y;
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
-        const int t = (gi * NPT + tid) & 31;
-        if ((mask >> t) & 1u) prtbuf[q & 1][gi][tid] = pr.prt[gi];
+        const int t = kt0 + KTT * gi;
+        if ((pr.mask >> t) & 1u) prtbuf[q & 1][gi][tid] = pr.prt[gi];
       }
     } else if (q == nq && has_block) {
       // the block: K rows as fp32 [32][D], then V rows as fp16 [32][D]; bf16
@@ -210,7 +219,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       _Float16* vst = reinterpret_cast<_Float16*>(stage + kSlot * D * 4);
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
-        const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
+        const int t = kt0 + KTT * gi, cg = kcg;
         float kx[8], vx[8];
         if (blk_f32) {
           const size_t e = (((size_t)b * kSlot + t) * hkv + kvh) * D + 8 * cg;
@@ -234,60 +243,59 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // ---------------- producers: dequantize unit q into K buffer q & 1 and
   // V buffer q % 3
   const float neg_one = opaque_neg_one();
-  auto dequant = [&](int q) __attribute__((always_inline)) {
+  auto dequant = [&](int q, uint32_t mask) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
     const int kb = q & 1, vbuf = q % 3;
     if (q < nq) {
-      const uint32_t mask = (uint32_t)hdr[q].y;
-      const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC);
+      // K: tokens kt0 + KTT*gi of channel group kcg; their codes are word kcg
+      // (4-bit) or half kcg % 2 of word kcg / 2 (2-bit) of the token's word column.
+      const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC) + 8 * kcg;
+      const float4 ks0 = *reinterpret_cast<const float4*>(kmeta);
+      const float4 ks1 = *reinterpret_cast<const float4*>(kmeta + 4);
+      const float4 kz0 = *reinterpret_cast<const float4*>(kmeta + D);
+      const float4 kz1 = *reinterpret_cast<const float4*>(kmeta + D + 4);
+      const float ksc[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
+      const float kzr[8] = {kz0.x, kz0.y, kz0.z, kz0.w, kz1.x, kz1.y, kz1.z, kz1.w};
+      const int khh = kcg / (D / 16), ks = kcg % (D / 16);
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
-        // K: (token t, 8-channel group cg); its codes are word cg (4-bit) or
-        // half cg % 2 of word cg / 2 (2-bit) of token t's word column.
-        const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
+        const int t = kt0 + KTT * gi;
         float x[8];
         if ((mask >> t) & 1u) {
           const uint4 w = prtbuf[q & 1][gi][tid];
           x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
           x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
         } else {
-          const uint32_t w = KB == 4 ? words[cg * 32 + t] : words[(cg >> 1) * 32 + t] >> (16 * (cg & 1));
+          const uint32_t w = KB == 4 ? words[kcg * 32 + t] : words[(kcg >> 1) * 32 + t] >> (16 * (kcg & 1));
           float code[8];
           unpack8<KB>(w, code);
-          const float4 s0 = *reinterpret_cast<const float4*>(kmeta + 8 * cg);
-          const float4 s1 = *reinterpret_cast<const float4*>(kmeta + 8 * cg + 4);
-          const float4 z0 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg);
-          const float4 z1 = *reinterpret_cast<const float4*>(kmeta + D + 8 * cg + 4);
-          const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-          const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], sc[e], zr[e]);
+          for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], ksc[e], kzr[e]);
         }
-        const int hh = cg / (D / 16), s = cg % (D / 16);
-        store_hi_lo(kop[kb][0][s][t + 32 * hh], kop[kb][1][s][t + 32 * hh], x, neg_one);
+        store_hi_lo(kop[kb][0][ks][t + 32 * khh], kop[kb][1][ks][t + 32 * khh], x, neg_one);
       }
+      // V: channels vc0 + vi of token octet (mm, hh); 4-bit: word 2mm+hh of the
+      // channel; 2-bit: half mm of word hh.
+      const int mm = vcombo >> 1, hh = vcombo & 1;
+      const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (vc0 >> gv_log2) * 256);
+      const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
+      const float4 vs0 = *reinterpret_cast<const float4*>(vs + ta);
+      const float4 vs1 = *reinterpret_cast<const float4*>(vs + ta + 8);
+      const float4 vz0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
+      const float4 vz1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
+      const float vsc[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+      const float vzr[8] = {vz0.x, vz0.y, vz0.z, vz0.w, vz1.x, vz1.y, vz1.z, vz1.w};
 #pragma unroll
       for (int vi = 0; vi < VPT; ++vi) {
-        // V: channel c, token octet (mm, hh); 4-bit: word 2mm+hh of channel c;
-        // 2-bit: half mm of word hh.
-        const int idx = vi * NPT + tid, c = idx % D, combo = idx / D;
-        const int mm = combo >> 1, hh = combo & 1;
+        const int c = vc0 + vi;
         const uint32_t w = VB == 4 ? words[KC / 4 + (2 * mm + hh) * D + c]
                                    : words[KC / 4 + hh * D + c] >> (16 * mm);
         float code[8];
         unpack8<VB>(w, code);
-        const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (c >> gv_log2) * 256);
-        const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
-        const float4 s0 = *reinterpret_cast<const float4*>(vs + ta);
-        const float4 s1 = *reinterpret_cast<const float4*>(vs + ta + 8);
-        const float4 z0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
-        const float4 z1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
-        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], sc[e], zr[e]);
+        for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], vsc[e], vzr[e]);
         vop[vbuf][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
       }
     } else if (q == nq && has_block) {
@@ -295,7 +303,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       const _Float16* vst = reinterpret_cast<const _Float16*>(rawS + kSlot * D * 4);
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
-        const int idx = gi * NPT + tid, t = idx & 31, cg = idx >> 5;
+        const int t = kt0 + KTT * gi, cg = kcg;
         const float4 x0 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg);
         const float4 x1 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg + 4);
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -304,8 +312,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       }
 #pragma unroll
       for (int vi = 0; vi < VPT; ++vi) {
-        const int idx = vi * NPT + tid, c = idx % D, combo = idx / D;
-        const int mm = combo >> 1, hh = combo & 1;
+        const int c = vc0 + vi, mm = vcombo >> 1, hh = vcombo & 1;
         half8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = vst[(16 * mm + 4 * hh + (e & 3) + 8 * (e >> 2)) * D + c];
@@ -346,9 +353,10 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
-  auto softmax_pv = [&](int q) __attribute__((always_inline)) {
+  // nvalid (valid tokens of the unit) is read from the header one phase
+  // ahead by the caller, so its LDS latency stays off the softmax path.
+  auto softmax_pv = [&](int q, int nvalid) __attribute__((always_inline)) {
     const int vbuf = q % 3;
-    const int nvalid = hdr[q].x;
     half8 va[CT][2];                     // first k-half of the V operands, read before the softmax
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) va[ct][0] = vop[vbuf][ct][0][lane];
@@ -425,15 +433,19 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     load_unit(0, pre0);
     load_unit(1, pre1);
     store_unit(0, pre0);
+    uint32_t dmask = pre0.mask;              // protected mask of the unit dequantized next
     load_unit(2, pre0);
     __syncthreads();
     for (int i = 0; i < n_int; i += 2) {
       store_unit(i + 1, pre1);
-      if (i < NU) dequant(i);
+      const uint32_t m1 = pre1.mask;
+      if (i < NU) dequant(i, dmask);
       load_unit(i + 3, pre1);
       __syncthreads();
       store_unit(i + 2, pre0);
-      if (i + 1 < NU) dequant(i + 1);
+      const uint32_t m0 = pre0.mask;
+      if (i + 1 < NU) dequant(i + 1, m1);
+      dmask = m0;
       load_unit(i + 4, pre0);
       __syncthreads();
     }
@@ -476,16 +488,21 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     return;
   }
   if (late) {
+    int nv = 0;
     for (int i = 0; i < n_int; ++i) {
-      if (i >= 2 && i - 2 < NU) softmax_pv(i - 2);
-      if (i >= 1 && i - 1 < NU) scores(i - 1);
+      if (i >= 2 && i - 2 < NU) softmax_pv(i - 2, nv);
+      if (i >= 1 && i - 1 < NU) {
+        nv = hdr[i - 1].x;
+        scores(i - 1);
+      }
       __syncthreads();
     }
   } else {
     for (int i = 0; i < n_int; ++i) {
       if (i >= 1 && i - 1 < NU) {
+        const int nv = hdr[i - 1].x;
         scores(i - 1);
-        softmax_pv(i - 1);
+        softmax_pv(i - 1, nv);
       }
       __syncthreads();
     }

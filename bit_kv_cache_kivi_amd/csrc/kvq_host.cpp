@@ -320,25 +320,35 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     kvq_status s = ensure_hip(c);
     if (s != KVQ_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int k = c->next_stage;
-    if (c->ev_used[k]) {
-      hipError_t e = hipEventSynchronize(c->ev[k]);
-      if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    kvq::CommitArgs a;          // about 2 KB with the inline task table; the launch copies it
+    memset(&a, 0, sizeof(a));
+    hipError_t e = hipSuccess;
+    if ((int)tasks.size() <= kvq::kInlineTasks) {
+      // small commits (one block per sequence) pass the tasks by value
+      a.use_inline = 1;
+      memcpy(a.inline_tasks, tasks.data(), tasks.size() * sizeof(CommitTask));
+      a.tasks = nullptr;
+    } else {
+      const int k = c->next_stage;
+      if (c->ev_used[k]) {
+        e = hipEventSynchronize(c->ev[k]);
+        if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+      }
+      const size_t bytes = tasks.size() * sizeof(CommitTask);
+      uint8_t* hs = c->h_stage + k * c->lay.staging_bytes;
+      uint8_t* ds = c->dbuf + c->lay.staging_offset + k * c->lay.staging_bytes;
+      memcpy(hs, tasks.data(), bytes);
+      e = hipMemcpyAsync(ds, hs, bytes, hipMemcpyHostToDevice, st);
+      if (e != hipSuccess) return fail(KVQ_EHIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+      e = hipEventRecord(c->ev[k], st);
+      if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+      c->ev_used[k] = true;
+      c->next_stage = k ^ 1;
+      a.use_inline = 0;
+      a.tasks = reinterpret_cast<const CommitTask*>(ds);
     }
-    const size_t bytes = tasks.size() * sizeof(CommitTask);
-    uint8_t* hs = c->h_stage + k * c->lay.staging_bytes;
-    uint8_t* ds = c->dbuf + c->lay.staging_offset + k * c->lay.staging_bytes;
-    memcpy(hs, tasks.data(), bytes);
-    hipError_t e = hipMemcpyAsync(ds, hs, bytes, hipMemcpyHostToDevice, st);
-    if (e != hipSuccess) return fail(KVQ_EHIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-    e = hipEventRecord(c->ev[k], st);
-    if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-    c->ev_used[k] = true;
-    c->next_stage = k ^ 1;
-    kvq::CommitArgs a;
     a.k = d_k;
     a.v = d_v;
-    a.tasks = reinterpret_cast<const CommitTask*>(ds);
     a.seg = seg_ptrs(c, segment);
     a.n_max = n_max;
     a.hkv = cfg.num_kv_heads;

@@ -33,15 +33,20 @@ struct SegPtrs {
   int32_t prot_cap;
 };
 
+constexpr int kInlineTasks = 64;  // commits with at most this many new slots pass their tasks by value
+
 struct CommitArgs {
   const void* k;        // [B, n_max, Hkv, D]
   const void* v;
-  const CommitTask* tasks;
+  const CommitTask* tasks;  // device task table (used when use_inline == 0)
   SegPtrs seg;
   int32_t n_max;
   int32_t hkv;
   int32_t gv_log2;
   uint32_t record_bytes;
+  int32_t use_inline;
+  int32_t pad_;
+  CommitTask inline_tasks[kInlineTasks];
 };
 
 struct AttnArgs {
