@@ -6,47 +6,149 @@
 // their group's statistics (Tai et al., "KV Cache Quantization for Diffusion
 // Language Models", abstract; SoloQ summary page, block-diffusion paragraph).
 //
-// One workgroup = four waves per (new slot, kv head): waves 0 and 1 quantize
-// the keys of one half of the channels each (a key group spans the 32 tokens
-// of one channel, so the halves are independent), waves 2 and 3 the values of
-// one half of the tokens each (a value group spans channels of one token).
-// Each lane loads 16-byte pieces of token rows; group minima and maxima come
-// from in-lane reductions plus xor shuffles.  Codes are packed into a slot
-// record staged in LDS, then the whole record leaves with coalesced 128-bit
-// stores.
+// One workgroup = four waves per kv head, looping over new slots (task i,
+// i + gridDim.x, ...): waves 0 and 1 quantize the keys of one half of the
+// channels each (a key group spans the 32 tokens of one channel, so the halves
+// are independent), waves 2 and 3 the values of one half of the tokens each (a
+// value group spans channels of one token).  Each lane loads 16-byte pieces of
+// token rows, and loads the next slot's pieces before quantizing the current
+// one, so HBM reads stay in flight while the slot is processed.
+//
+// The kernel is bound by vector ALU issue, so every step is shaped to cost few
+// instructions per element:
+//   - group minima and maxima: in-lane min3/max3, then, for values, DPP steps
+//     between the lanes of a group, and for keys a transposed exchange through
+//     LDS that leaves each lane with the 8 or 16 partial results of one channel;
+//   - one lane per group computes the group's scale with an IEEE division and
+//     publishes scale, zero and a reciprocal through LDS;
+//   - per element: subtract, multiply by the reciprocal, round, and a
+//     distance-to-boundary test (below); key codes are packed with
+//     v_cvt_pk_u8_f32, value codes with shift-or, and each lane writes its
+//     part of the code words to the LDS record with plain stores (no atomics,
+//     no clearing), so a slot needs one workgroup barrier.
+// The record then leaves with coalesced 128-bit stores.
 //
 // Exactness: scale = (mx - mn) / (2^b - 1) uses IEEE division.  A code is
 // rint(q) of the fp32 quotient q = fl((x - mn) / scale).  The kernel forms
-// y = d * rcp(scale) and refines it once with the exact residual
-// fma(-y, scale, d); the refined y is within one ulp of q, so rint(y) equals
-// rint(q) unless y lies within 2^-19 of a rounding boundary k + 1/2 (two ulps
-// or more below 16).  Only such elements -- and every element of a group whose
-// scale lies outside [2^-100, 2^100], where rcp would overflow or underflow --
-// are recomputed with IEEE division, on a path that runs only when some lane
-// of the wave needs it.  Codes are therefore identical to the plain
-// definition.  This file is compiled with -ffp-contract=off.
+// y = fl(d * rcp(scale)) with v_rcp_f32 (1 ulp): for q < 16,
+// |y - q| < 16 * 1.5 * 2^-23 + 2^-21 < 2^-18, so rint(y) equals rint(q) unless
+// y lies within 2^-18 of a rounding boundary k + 1/2.  An element with
+// |y - rint(y)| >= 1/2 - 2^-17 takes its code from an IEEE division instead
+// (with bf16 inputs about 0.2% of elements do: exact ties are common), and a
+// wave in which some group's scale lies outside [2^-100, 2^100] (where rcp
+// would overflow or underflow) recomputes all its codes that way.  For members of a group d lies in [0, mx - mn], so
+// y < LEV + 1/2 and rint(y) needs no clamp; elements that are not members
+// (protected or padding tokens) are masked to code 0.  Codes are therefore
+// identical to the plain definition.  This file is compiled with
+// -ffp-contract=off.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-// Code of one element from the refined quotient; sets 'redo' when the element
-// must be recomputed with an exact division.
-__device__ __forceinline__ uint32_t fast_code(float d, float scale, float rcp, float lev, bool& redo) {
-  float y = d * rcp;
-  const float r = fmaf(-y, scale, d);
-  y = fmaf(r, rcp, y);
-  redo = fabsf((y - floorf(y)) - 0.5f) <= 0x1p-19f;
-  return (uint32_t)fminf(fmaxf(rintf(y), 0.f), lev);
+// min/max of three floats.  In IEEE mode a quiet-NaN operand is ignored, so
+// elements left out of a group are set to NaN before the reduction.
+__device__ __forceinline__ float vmin3(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
-__device__ __forceinline__ uint32_t exact_code(float d, float scale, float lev) {
-  return (uint32_t)fminf(fmaxf(rintf(d / scale), 0.f), lev);
+// One DPP step of a min/max reduction over groups of consecutive lanes, in
+// place on N minima and N maxima.  The leading s_nop covers the DPP read-after-
+// write and exec-write hazards of whatever the compiler placed before the block.
+#define KVQ_DMIN(i, C) "v_min_f32_dpp %" #i ", %" #i ", %" #i " " C " row_mask:0xf bank_mask:0xf\n\t"
+#define KVQ_DMAX(i, C) "v_max_f32_dpp %" #i ", %" #i ", %" #i " " C " row_mask:0xf bank_mask:0xf\n\t"
+template <int N>
+struct DppMinMax;
+template <>
+struct DppMinMax<4> {
+  template <int S>
+  __device__ __forceinline__ static void step(float (&mn)[4], float (&mx)[4]) {
+#define KVQ_STEP4(C)                                                                                    \
+  asm("s_nop 4\n\t" KVQ_DMIN(0, C) KVQ_DMIN(1, C) KVQ_DMIN(2, C) KVQ_DMIN(3, C) KVQ_DMAX(4, C)          \
+          KVQ_DMAX(5, C) KVQ_DMAX(6, C) KVQ_DMAX(7, C)                                                  \
+      : "+v"(mn[0]), "+v"(mn[1]), "+v"(mn[2]), "+v"(mn[3]), "+v"(mx[0]), "+v"(mx[1]), "+v"(mx[2]),   \
+        "+v"(mx[3]))
+    if (S == 0) KVQ_STEP4("quad_perm:[1,0,3,2]");
+    if (S == 1) KVQ_STEP4("quad_perm:[2,3,0,1]");
+    if (S == 2) KVQ_STEP4("row_half_mirror");
+    if (S == 3) KVQ_STEP4("row_mirror");
+#undef KVQ_STEP4
+  }
+};
+template <>
+struct DppMinMax<2> {
+  template <int S>
+  __device__ __forceinline__ static void step(float (&mn)[2], float (&mx)[2]) {
+#define KVQ_STEP2(C)                                                                  \
+  asm("s_nop 4\n\t" KVQ_DMIN(0, C) KVQ_DMIN(1, C) KVQ_DMAX(2, C) KVQ_DMAX(3, C)       \
+      : "+v"(mn[0]), "+v"(mn[1]), "+v"(mx[0]), "+v"(mx[1]))
+    if (S == 0) KVQ_STEP2("quad_perm:[1,0,3,2]");
+    if (S == 1) KVQ_STEP2("quad_perm:[2,3,0,1]");
+    if (S == 2) KVQ_STEP2("row_half_mirror");
+    if (S == 3) KVQ_STEP2("row_mirror");
+#undef KVQ_STEP2
+  }
+};
+#undef KVQ_DMIN
+#undef KVQ_DMAX
+
+// x | (x of lane i ^ 8 within each 16-lane row)
+__device__ __forceinline__ uint32_t or_lane_xor8(uint32_t x) {
+  uint32_t r;
+  asm("s_nop 4\n\tv_or_b32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  return r;
 }
+
+// Orders LDS traffic between the lanes of one wave (same-wave LDS accesses
+// execute in order; this only keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T>
+__device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
+
+// scale and zero of a group from its minimum and maximum (NaN when the group
+// has no member), and the reciprocal the fast path multiplies by
+struct GroupParams {
+  float scale, zero, rcp;
+  bool bad;   // scale outside [2^-100, 2^100]: codes need the exact path
+};
+template <int B>
+__device__ __forceinline__ GroupParams group_params(float mn, float mx, bool valid) {
+  constexpr float LEV = (float)((1 << B) - 1);
+  GroupParams p;
+  const bool any = valid && mn <= mx;
+  p.scale = any ? (mx - mn) / LEV + 0.0f : 0.0f;
+  p.zero = any ? mn + 0.0f : 0.0f;
+  p.bad = p.scale != 0.f && !(p.scale >= 0x1p-100f && p.scale <= 0x1p+100f);
+  p.rcp = p.scale == 0.f ? 0.f : __builtin_amdgcn_rcpf(p.scale);
+  return p;
+}
+
+// The plain definition, branch-free (the division is done for scale == 0 too,
+// by 1, and its result dropped).
+__device__ __forceinline__ float exact_code(float d, float scale, float lev) {
+  const float q = fminf(fmaxf(rintf(d / (scale == 0.f ? 1.f : scale)), 0.f), lev);
+  return scale == 0.f ? 0.f : q;
+}
+
+constexpr float kNearHalf = 0.5f - 0x1p-17f;
 
 template <int KB, int VB, int D, bool F32IN>
-__global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
+__global__ __launch_bounds__(256, F32IN ? 3 : 4) void commit_kernel(const CommitArgs a, int ntasks) {
   constexpr int HC = D / 2;              // channels per key wave
   constexpr int NCGK = HC / 8;           // 8-channel groups per key wave
   constexpr int NTQK = 64 / NCGK;        // key lanes along the token axis
@@ -54,220 +156,413 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a) {
   constexpr int NCGV = D / 8;            // 8-channel groups of a value row
   constexpr int NTQV = 64 / NCGV;        // value lanes along the token axis
   constexpr int TPLV = (kSlot / 2) / NTQV;   // tokens per value lane
+  constexpr int TPL = TPLK > TPLV ? TPLK : TPLV;
+  constexpr int ES = F32IN ? 4 : 2;      // input element bytes
+  constexpr int PPR = F32IN ? 2 : 1;     // 16-byte pieces per 8-channel row piece
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
   constexpr uint32_t KM = kmeta_bytes(D);
   constexpr uint32_t REC_MAX = record_bytes(D, KB, VB, 32);
-  static_assert(TPLK * 8 <= 32 && TPLV * 8 <= 32, "per-lane element masks are 32 bits");
-  static_assert((kSlot / 2) % TPLV == 0 && TPLV % 2 == 0 && TPLV <= 4, "value token chunks");
-  __shared__ __align__(16) uint8_t rec[REC_MAX];
+  constexpr int TST = 9 * NTQK;          // padded row of the key statistics exchange
+  static_assert(NTQK == 8 || NTQK == 16, "key lanes per channel group");
+  static_assert(TPLK == 2 || TPLK == 4, "key tokens per lane");
+  static_assert(TPLV == 2 || TPLV == 4, "value tokens per lane");
+  static_assert(TPLK == TPLV, "key and value lanes hold the same number of rows");
+  __shared__ __align__(16) uint8_t recbuf[2][REC_MAX];
+  __shared__ __align__(16) float kx[2][2][NCGK * TST];      // key partial min/max: [wave][min|max][cgl][channel][tq]
+  __shared__ __align__(16) float krcp[D];                   // key reciprocals per channel
+  __shared__ __align__(16) float vrcp[D / 32][kSlot];       // value reciprocals per (group, token)
 
-  const CommitTask task = a.use_inline ? a.inline_tasks[blockIdx.x] : a.tasks[blockIdx.x];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool keys = wave < 2;
   const uint32_t rbytes = a.record_bytes;
   const uint32_t raw_end = KC + VC + KM + (uint32_t)(D >> a.gv_log2) * 256u;
-  // value codes are OR-ed in below: clear them, and the record's padding
-  for (uint32_t off = KC + tid * 4; off < KC + VC; off += 256 * 4) *reinterpret_cast<uint32_t*>(rec + off) = 0u;
-  for (uint32_t off = raw_end + tid * 4; off < rbytes; off += 256 * 4) *reinterpret_cast<uint32_t*>(rec + off) = 0u;
-  __syncthreads();
+  // lane geometry: a key lane holds tokens tq*TPLK + k of channel group cg
+  // (the NTQK lanes of a channel group are consecutive); a value lane holds
+  // tokens t0 + k of channel group cg (the lanes of a value group are consecutive)
+  const int cg = keys ? wave * NCGK + lane / NTQK : lane % NCGV;
+  const int tq = keys ? lane % NTQK : lane / NCGV;
+  const int t0 = keys ? tq * TPLK : (wave - 2) * (kSlot / 2) + tq * TPLV;
+  const int nrows = keys ? TPLK : TPLV;
+  const void* src = keys ? a.k : a.v;
+  const int G = gridDim.x;
 
-  if (wave < 2) {
-    // ================= keys: channels [wave*D/2, +D/2), groups along the 32 tokens
-    constexpr float LEV = (float)((1 << KB) - 1);
-    const int cgl = lane % NCGK, tq = lane / NCGK;
-    const int cg = wave * NCGK + cgl;          // 8-channel group within the row
-    float x[TPLK][8];
+  // the record bytes past the last field stay zero in both buffers
+  for (uint32_t off = raw_end + tid * 4; off < rbytes; off += 256 * 4) {
+    *reinterpret_cast<uint32_t*>(recbuf[0] + off) = 0u;
+    *reinterpret_cast<uint32_t*>(recbuf[1] + off) = 0u;
+  }
+
+  // Task descriptors are read with scalar loads (the kernel-argument copy, or
+  // the device table through the constant address space): they then count on
+  // a different counter from the row loads and never make a wait for a
+  // descriptor wait for the row prefetch as well.
+  typedef const __attribute__((address_space(4))) int32_t* ConstWords;
+  auto task_at = [&](int i) __attribute__((always_inline)) {
+    CommitTask t;
+    if (a.use_inline) {
+      t = a.inline_tasks[i];
+    } else {
+      const ConstWords w = (ConstWords)(uintptr_t)(a.tasks + i);
+      t.b = w[0]; t.dst_slot = w[1]; t.src_tok = w[2]; t.nvalid = w[3];
+      t.mask = (uint32_t)w[4]; t.rank_base = w[5]; t.token_base = w[6]; t.pad = 0;
+    }
+    return t;
+  };
+  // This lane's row pieces of task i (buffer loads: rows past the task's
+  // valid tokens, and tasks past the end, read as zeros without traffic).
+  struct Raw { uint4 p[TPL][PPR]; };
+  auto fetch = [&](int i, const CommitTask& task, Raw& raw) __attribute__((always_inline)) {
+    const bool live = i < ntasks;
+    const uint8_t* base = static_cast<const uint8_t*>(src) +
+                          (((size_t)task.b * a.n_max + task.src_tok) * a.hkv) * D * ES;
+    const int nbytes = live ? task.nvalid * a.hkv * D * ES : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < TPL; ++k)
+#pragma unroll
+      for (int j = 0; j < PPR; ++j) {
+        const int off = k < nrows ? ((t0 + k) * a.hkv + h) * D * ES + 8 * cg * ES + 16 * j : 0x7ff00000;
+        raw.p[k][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      }
+  };
+  auto unpack_row = [&](const Raw& raw, int k, float (&x)[8]) __attribute__((always_inline)) {
+    if (F32IN) {
+      const uint4 p0 = raw.p[k][0], p1 = raw.p[k][PPR - 1];
+      x[0] = __uint_as_float(p0.x); x[1] = __uint_as_float(p0.y); x[2] = __uint_as_float(p0.z); x[3] = __uint_as_float(p0.w);
+      x[4] = __uint_as_float(p1.x); x[5] = __uint_as_float(p1.y); x[6] = __uint_as_float(p1.z); x[7] = __uint_as_float(p1.w);
+    } else {
+      const uint4 w = raw.p[k][0];
+      x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+      x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    }
+  };
+
+  // ================= keys: protected rows go to the bf16 store as they are
+  auto store_protected = [&](const CommitTask& task, const float (&x)[TPL][8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < TPLK; ++k) {
-      const int t = tq * TPLK + k;
-      if (t < task.nvalid) {
-        const size_t row = ((size_t)task.b * a.n_max + task.src_tok + t) * a.hkv + h;
-        load8(a.k, row * D + 8 * cg, F32IN, x[k]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[k][c] = 0.f;
+      const int t = t0 + k;
+      if (t < task.nvalid && ((task.mask >> t) & 1u)) {
+        const int rank = task.rank_base + __popc(task.mask & ((1u << t) - 1u));
+        uint4 w;
+        w.x = f32_to_bf16_bits(x[k][0]) | (f32_to_bf16_bits(x[k][1]) << 16);
+        w.y = f32_to_bf16_bits(x[k][2]) | (f32_to_bf16_bits(x[k][3]) << 16);
+        w.z = f32_to_bf16_bits(x[k][4]) | (f32_to_bf16_bits(x[k][5]) << 16);
+        w.w = f32_to_bf16_bits(x[k][6]) | (f32_to_bf16_bits(x[k][7]) << 16);
+        const size_t prow = ((size_t)task.b * a.hkv + h) * a.seg.prot_cap + rank;
+        *reinterpret_cast<uint4*>(a.seg.prot_rows + prow * D + 8 * cg) = w;
+        if (h == 0 && cg == 0) a.seg.prot_pos[(size_t)task.b * a.seg.prot_cap + rank] = task.token_base + t;
       }
     }
+  };
+
+  // ================= keys: channels [wave*D/2, +D/2), groups along the 32 tokens
+  auto process_keys = [&](const CommitTask& task, float (&x)[TPL][8], uint8_t* rec) __attribute__((always_inline)) {
+    constexpr float LEV = (float)((1 << KB) - 1);
     uint32_t member = 0;
 #pragma unroll
     for (int k = 0; k < TPLK; ++k) {
-      const int t = tq * TPLK + k;
+      const int t = t0 + k;
       if (t < task.nvalid && !((task.mask >> t) & 1u)) member |= 1u << k;
     }
-    // protected rows: copy to the bf16 store
-    if (task.mask) {
+    if (task.mask != 0u || task.nvalid < kSlot) {
+      // tokens outside the group take no part in its statistics or codes
+#pragma unroll
+      for (int k = 0; k < TPLK; ++k)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[k][c] = ((member >> k) & 1u) ? x[k][c] : __builtin_nanf("");
+    }
+    // partial min/max over the lane's tokens, exchanged transposed through
+    // LDS: lane (cgl, tq) then reduces channel tq % 8 of its channel group
+    const int cgl = lane / NTQK;
+    float* kmn = kx[wave][0] + cgl * TST;
+    float* kmx = kx[wave][1] + cgl * TST;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float mn = vmin3(x[0][c], x[1][c], x[TPLK - 1][c]);
+      const float mx = vmax3(x[0][c], x[1][c], x[TPLK - 1][c]);
+      kmn[c * NTQK + tq] = TPLK == 4 ? vmin3(mn, x[TPLK - 2][c], x[TPLK - 2][c]) : mn;
+      kmx[c * NTQK + tq] = TPLK == 4 ? vmax3(mx, x[TPLK - 2][c], x[TPLK - 2][c]) : mx;
+    }
+    wave_lds_sync();
+    const int ch = tq & 7;
+    float gmn, gmx;
+    {
+      const float4* pn = reinterpret_cast<const float4*>(kmn + ch * NTQK);
+      const float4* px = reinterpret_cast<const float4*>(kmx + ch * NTQK);
+      float4 n = pn[0], m = px[0];
+      gmn = vmin3(n.x, n.y, n.z); gmn = vmin3(gmn, n.w, n.w);
+      gmx = vmax3(m.x, m.y, m.z); gmx = vmax3(gmx, m.w, m.w);
+#pragma unroll
+      for (int j = 1; j < NTQK / 4; ++j) {
+        n = pn[j]; m = px[j];
+        gmn = vmin3(gmn, n.x, n.y); gmn = vmin3(gmn, n.z, n.w);
+        gmx = vmax3(gmx, m.x, m.y); gmx = vmax3(gmx, m.z, m.w);
+      }
+    }
+    const GroupParams gp = group_params<KB>(gmn, gmx, true);
+    float* kscale = reinterpret_cast<float*>(rec + KC + VC);
+    if (tq < 8) {
+      kscale[8 * cg + ch] = gp.scale;
+      kscale[D + 8 * cg + ch] = gp.zero;
+      krcp[8 * cg + ch] = gp.rcp;
+    }
+    wave_lds_sync();
+    // scales stay in LDS: only the rare exact path reads them
+    float zero[8], rcp[8];
+    {
+      const float4 z0 = *reinterpret_cast<const float4*>(kscale + D + 8 * cg);
+      const float4 z1 = *reinterpret_cast<const float4*>(kscale + D + 8 * cg + 4);
+      const float4 r0 = *reinterpret_cast<const float4*>(krcp + 8 * cg);
+      const float4 r1 = *reinterpret_cast<const float4*>(krcp + 8 * cg + 4);
+      zero[0] = z0.x; zero[1] = z0.y; zero[2] = z0.z; zero[3] = z0.w;
+      zero[4] = z1.x; zero[5] = z1.y; zero[6] = z1.z; zero[7] = z1.w;
+      rcp[0] = r0.x; rcp[1] = r0.y; rcp[2] = r0.z; rcp[3] = r0.w;
+      rcp[4] = r1.x; rcp[5] = r1.y; rcp[6] = r1.z; rcp[7] = r1.w;
+    }
+    // codes of token k: channel c in bits [KB*c, KB*c + KB) of its word
+    uint32_t word[TPLK];
+#pragma unroll
+    for (int k = 0; k < TPLK; ++k) {
+      uint32_t p[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float d = x[k][c] - zero[c];
+        const float y = d * rcp[c];
+        float r = rintf(y);
+        if (fabsf(y - r) >= kNearHalf) r = exact_code(d, kscale[8 * cg + c], LEV);   // rare: near a boundary
+        if (KB == 4) p[c & 1] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 1, p[c & 1]);
+        else         p[c & 3] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 2, p[c & 3]);
+      }
+      const uint32_t w = KB == 4 ? (p[0] | (p[1] << 4)) : (p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6));
+      word[k] = ((member >> k) & 1u) ? w : 0u;
+    }
+    if (__any(gp.bad)) {
 #pragma unroll
       for (int k = 0; k < TPLK; ++k) {
-        const int t = tq * TPLK + k;
-        if (t < task.nvalid && ((task.mask >> t) & 1u)) {
-          const int rank = task.rank_base + __popc(task.mask & ((1u << t) - 1u));
-          uint4 w;
-          w.x = f32_to_bf16_bits(x[k][0]) | (f32_to_bf16_bits(x[k][1]) << 16);
-          w.y = f32_to_bf16_bits(x[k][2]) | (f32_to_bf16_bits(x[k][3]) << 16);
-          w.z = f32_to_bf16_bits(x[k][4]) | (f32_to_bf16_bits(x[k][5]) << 16);
-          w.w = f32_to_bf16_bits(x[k][6]) | (f32_to_bf16_bits(x[k][7]) << 16);
-          const size_t prow = ((size_t)task.b * a.hkv + h) * a.seg.prot_cap + rank;
-          *reinterpret_cast<uint4*>(a.seg.prot_rows + prow * D + 8 * cg) = w;
-          if (h == 0 && cg == 0) a.seg.prot_pos[(size_t)task.b * a.seg.prot_cap + rank] = task.token_base + t;
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float q = exact_code(x[k][c] - zero[c], kscale[8 * cg + c], LEV);
+          w |= (uint32_t)q << (KB * c);
+        }
+        word[k] = ((member >> k) & 1u) ? w : 0u;
+      }
+    }
+    // word-major: the word holding channel group cg of token t.  4-bit: the
+    // lane's TPLK tokens are consecutive words, written at once (a wide write
+    // also avoids the bank conflicts of lanes 32 words apart)
+    if (KB == 4) {
+      if (TPLK == 4) *reinterpret_cast<uint4*>(rec + (cg * 32 + t0) * 4) = make_uint4(word[0], word[1], word[TPLK - 2], word[TPLK - 1]);
+      else           *reinterpret_cast<uint2*>(rec + (cg * 32 + t0) * 4) = make_uint2(word[0], word[TPLK - 1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < TPLK; ++k)
+        *reinterpret_cast<uint16_t*>(rec + ((cg >> 1) * 32 + t0 + k) * 4 + 2 * (cg & 1)) = (uint16_t)word[k];
+    }
+  };
+
+  // ================= values: tokens [16*(wave-2), +16), groups along G_v channels
+  auto process_values = [&](const CommitTask& task, float (&x)[TPL][8], uint8_t* rec) __attribute__((always_inline)) {
+    constexpr float LEV = (float)((1 << VB) - 1);
+    const int lpg = (1 << a.gv_log2) / 8;     // lanes per value group (4, 8 or 16)
+    float mn[TPLV], mx[TPLV];
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k) {
+      float n = vmin3(x[k][0], x[k][1], x[k][2]), m = vmax3(x[k][0], x[k][1], x[k][2]);
+      n = vmin3(n, x[k][3], x[k][4]); m = vmax3(m, x[k][3], x[k][4]);
+      n = vmin3(n, x[k][5], x[k][6]); m = vmax3(m, x[k][5], x[k][6]);
+      mn[k] = vmin3(n, x[k][7], x[k][7]); mx[k] = vmax3(m, x[k][7], x[k][7]);
+    }
+    DppMinMax<TPLV>::template step<0>(mn, mx);
+    DppMinMax<TPLV>::template step<1>(mn, mx);
+    if (lpg >= 8) DppMinMax<TPLV>::template step<2>(mn, mx);
+    if (lpg >= 16) DppMinMax<TPLV>::template step<3>(mn, mx);
+    // lane gl of a group computes token gl % TPLV of the lane's tokens
+    const int gl = cg & (lpg - 1);
+    const int g = cg / lpg;
+    const int kk = gl & (TPLV - 1);
+    float smn, smx;
+    if (TPLV == 4) {
+      const float n01 = pick((kk & 1) != 0, mn[1], mn[0]), n23 = pick((kk & 1) != 0, mn[TPLV - 1], mn[TPLV - 2]);
+      const float m01 = pick((kk & 1) != 0, mx[1], mx[0]), m23 = pick((kk & 1) != 0, mx[TPLV - 1], mx[TPLV - 2]);
+      smn = pick((kk & 2) != 0, n23, n01);
+      smx = pick((kk & 2) != 0, m23, m01);
+    } else {
+      smn = pick((kk & 1) != 0, mn[TPLV - 1], mn[0]);
+      smx = pick((kk & 1) != 0, mx[TPLV - 1], mx[0]);
+    }
+    const GroupParams gp = group_params<VB>(smn, smx, t0 + kk < task.nvalid);
+    float* vs = reinterpret_cast<float*>(rec + KC + VC + KM + g * 256);
+    if (gl < TPLV) {
+      vs[t0 + kk] = gp.scale;
+      vs[32 + t0 + kk] = gp.zero;
+      vrcp[g][t0 + kk] = gp.rcp;
+    }
+    wave_lds_sync();
+    // scales stay in LDS: only the rare exact path reads them
+    float zero[TPLV], rcp[TPLV];
+    if (TPLV == 4) {
+      const float4 z = *reinterpret_cast<const float4*>(vs + 32 + t0);
+      const float4 r = *reinterpret_cast<const float4*>(&vrcp[g][t0]);
+      zero[0] = z.x; zero[1] = z.y; zero[TPLV - 2] = z.z; zero[TPLV - 1] = z.w;
+      rcp[0] = r.x; rcp[1] = r.y; rcp[TPLV - 2] = r.z; rcp[TPLV - 1] = r.w;
+    } else {
+      const float2 z = *reinterpret_cast<const float2*>(vs + 32 + t0);
+      const float2 r = *reinterpret_cast<const float2*>(&vrcp[g][t0]);
+      zero[0] = z.x; zero[TPLV - 1] = z.y;
+      rcp[0] = r.x; rcp[TPLV - 1] = r.y;
+    }
+    // The lane's TPLV consecutive tokens land next to each other in one code
+    // word of each channel: token t goes to
+    //   mm = t / 16, hh = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2)
+    //   4-bit: word 2*mm + hh, bits 4e;  2-bit: word hh, bits 2*(8*mm + e)
+    // bits[c] holds the lane's codes of channel c from bit 0 on.
+    // 4-bit: tokens k = 0, 2 go to bytes 0, 1 of pe and k = 1, 3 to those
+    // of po (v_cvt_pk_u8_f32), so pe | po << 4 has token k at bits 4k
+    uint32_t bits[8], pe[8], po[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) bits[c] = pe[c] = po[c] = 0u;
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float d = x[k][c] - zero[k];
+        const float y = d * rcp[k];
+        float r = rintf(y);
+        if (fabsf(y - r) >= kNearHalf) r = exact_code(d, vs[t0 + k], LEV);   // rare: near a boundary
+        if (VB == 4) {
+          if (k & 1) po[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, po[c]);
+          else       pe[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, pe[c]);
+        } else {
+          bits[c] |= (uint32_t)r << (VB * k);
         }
       }
     }
-    float scale[8], zero[8], rcp[8];
-    uint32_t redo = 0;                         // bit 8k + c: element (token k, channel c)
+    if (VB == 4) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float mn = __builtin_inff(), mx = -__builtin_inff();
-#pragma unroll
-      for (int k = 0; k < TPLK; ++k)
-        if ((member >> k) & 1u) { mn = fminf(mn, x[k][c]); mx = fmaxf(mx, x[k][c]); }
-#pragma unroll
-      for (int m = NCGK; m < 64; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m));
-        mx = fmaxf(mx, __shfl_xor(mx, m));
-      }
-      const bool any = mn <= mx;
-      scale[c] = any ? (mx - mn) / LEV + 0.0f : 0.0f;
-      zero[c] = any ? mn + 0.0f : 0.0f;
-      rcp[c] = __builtin_amdgcn_rcpf(scale[c]);
-      if (scale[c] != 0.f && !(scale[c] >= 0x1p-100f && scale[c] <= 0x1p+100f)) {
-#pragma unroll
-        for (int k = 0; k < TPLK; ++k) redo |= ((member >> k) & 1u) << (8 * k + c);
-      }
+      for (int c = 0; c < 8; ++c) bits[c] = pe[c] | (po[c] << 4);
     }
-    if (tq == 0) {
-      float* ks = reinterpret_cast<float*>(rec + KC + VC) + 8 * cg;
-      *reinterpret_cast<float4*>(ks) = make_float4(scale[0], scale[1], scale[2], scale[3]);
-      *reinterpret_cast<float4*>(ks + 4) = make_float4(scale[4], scale[5], scale[6], scale[7]);
-      *reinterpret_cast<float4*>(ks + D) = make_float4(zero[0], zero[1], zero[2], zero[3]);
-      *reinterpret_cast<float4*>(ks + D + 4) = make_float4(zero[4], zero[5], zero[6], zero[7]);
-    }
-    uint32_t code[TPLK][8];
-#pragma unroll
-    for (int k = 0; k < TPLK; ++k)
+    if (__any(gp.bad)) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        bool r;
-        const uint32_t q = fast_code(x[k][c] - zero[c], scale[c], rcp[c], LEV, r);
-        const bool live = ((member >> k) & 1u) && scale[c] != 0.f;
-        code[k][c] = live ? q : 0u;
-        redo |= (uint32_t)(live && r) << (8 * k + c);
-      }
-    if (__any(redo != 0)) {
+        uint32_t b = 0;
 #pragma unroll
-      for (int k = 0; k < TPLK; ++k)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          if ((redo >> (8 * k + c)) & 1u) code[k][c] = exact_code(x[k][c] - zero[c], scale[c], LEV);
-    }
-#pragma unroll
-    for (int k = 0; k < TPLK; ++k) {
-      const int t = tq * TPLK + k;
-      uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) word |= code[k][c] << (KB * c);
-      // word-major: the word holding channel group cg of token t
-      if (KB == 4) *reinterpret_cast<uint32_t*>(rec + (cg * 32 + t) * 4) = word;
-      else         *reinterpret_cast<uint16_t*>(rec + ((cg >> 1) * 32 + t) * 4 + 2 * (cg & 1)) = (uint16_t)word;
-    }
-  } else {
-    // ================= values: tokens [16*(wave-2), +16), groups along G_v channels
-    constexpr float LEV = (float)((1 << VB) - 1);
-    const int cg = lane % NCGV, tq = lane / NCGV;
-    const int t0 = (wave - 2) * (kSlot / 2) + tq * TPLV;   // first token of this lane
-    const int lanes_per_group = (1 << a.gv_log2) / 8;
-    float x[TPLV][8];
-#pragma unroll
-    for (int k = 0; k < TPLV; ++k) {
-      const int t = t0 + k;
-      if (t < task.nvalid) {
-        const size_t row = ((size_t)task.b * a.n_max + task.src_tok + t) * a.hkv + h;
-        load8(a.v, row * D + 8 * cg, F32IN, x[k]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[k][c] = 0.f;
+        for (int k = 0; k < TPLV; ++k) b |= (uint32_t)exact_code(x[k][c] - zero[k], vs[t0 + k], LEV) << (VB * k);
+        bits[c] = b;
       }
     }
-    float scale[TPLV], zero[TPLV], rcp[TPLV];
-    uint32_t redo = 0;                         // bit 8k + c
-#pragma unroll
-    for (int k = 0; k < TPLV; ++k) {
-      float mn = x[k][0], mx = x[k][0];
-#pragma unroll
-      for (int c = 1; c < 8; ++c) { mn = fminf(mn, x[k][c]); mx = fmaxf(mx, x[k][c]); }
-      for (int m = 1; m < lanes_per_group; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m));
-        mx = fmaxf(mx, __shfl_xor(mx, m));
-      }
-      const bool valid = t0 + k < task.nvalid;
-      scale[k] = valid ? (mx - mn) / LEV + 0.0f : 0.0f;
-      zero[k] = valid ? mn + 0.0f : 0.0f;
-      rcp[k] = __builtin_amdgcn_rcpf(scale[k]);
-      if (scale[k] != 0.f && !(scale[k] >= 0x1p-100f && scale[k] <= 0x1p+100f)) redo |= 0xFFu << (8 * k);
-    }
-    if ((cg & (lanes_per_group - 1)) == 0) {
-      float* vs = reinterpret_cast<float*>(rec + KC + VC + KM + (cg / lanes_per_group) * 256);
-#pragma unroll
-      for (int k = 0; k < TPLV; k += 2) {
-        *reinterpret_cast<float2*>(vs + t0 + k) = make_float2(scale[k], scale[k + 1]);
-        *reinterpret_cast<float2*>(vs + 32 + t0 + k) = make_float2(zero[k], zero[k + 1]);
-      }
-    }
-    uint32_t code[TPLV][8];
-#pragma unroll
-    for (int k = 0; k < TPLV; ++k)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        bool r;
-        const uint32_t q = fast_code(x[k][c] - zero[k], scale[k], rcp[k], LEV, r);
-        const bool live = scale[k] != 0.f;
-        code[k][c] = live ? q : 0u;
-        redo |= (uint32_t)(live && r) << (8 * k + c);
-      }
-    if (__any(redo != 0)) {
-#pragma unroll
-      for (int k = 0; k < TPLV; ++k)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          if ((redo >> (8 * k + c)) & 1u) code[k][c] = exact_code(x[k][c] - zero[k], scale[k], LEV);
-    }
-    // The lane's TPLV tokens (even-aligned, within one run of four) land in
-    // one code word of each channel: token t goes to
-    //   mm = t / 16, hh = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2)
-    //   4-bit: word 2*mm + hh, bits 4e;  2-bit: word hh, bits 2*(8*mm + e)
-    // Lanes sharing a word OR their bits into it.
     const int mm = t0 / 16, hh = (t0 / 4) % 2;
+    const int e0 = (t0 % 4) + 4 * ((t0 / 8) % 2);
     const int j = VB == 4 ? 2 * mm + hh : hh;
+    const int p0 = VB == 4 ? 4 * e0 : 2 * (8 * mm + e0);   // bit of the lane's first token
+    uint8_t* vw = rec + KC + (j * D + 8 * cg) * 4 + p0 / 8;
+    if (VB == 4 && TPLV == 4) {
+      // lane L (< 32) and lane L + 32 hold the two 16-bit halves of the same
+      // words (tokens t0 and t0 + 8); one swap per channel pair c, c + 4 gives
+      // the lower lane words c and the upper lane words c + 4 as r[0] | r[1] << 16
+      uint32_t wv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const auto r = __builtin_amdgcn_permlane32_swap(bits[c], bits[c + 4], false, false);
+        wv[c] = r[0] | (r[1] << 16);
+      }
+      const int hi = lane >= 32;
+      *reinterpret_cast<uint4*>(rec + KC + (j * D + 8 * cg + 4 * hi) * 4) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      uint32_t bits = 0;
-#pragma unroll
-      for (int k = 0; k < TPLV; ++k) {
-        const int t = t0 + k;
-        const int e = (t % 4) + 4 * ((t / 8) % 2);
-        const int pos = VB == 4 ? 4 * e : 2 * (8 * mm + e);
-        bits |= code[k][c] << pos;
+      if (VB * TPLV == 16) {
+        *reinterpret_cast<uint16_t*>(vw + 4 * c) = (uint16_t)bits[c];
+      } else if (VB * TPLV == 8) {
+        vw[4 * c] = (uint8_t)bits[c];
+      } else {
+        // two 2-bit codes per lane: a byte holds the codes of this lane and
+        // of the lane with the neighbouring token pair (lane ^ 8 in the row)
+        const uint32_t both = or_lane_xor8(bits[c] << (p0 % 8));
+        if (p0 % 8 == 0) vw[4 * c] = (uint8_t)both;
       }
-      atomicOr(reinterpret_cast<uint32_t*>(rec + KC) + j * D + 8 * cg + c, bits);
     }
-  }
-  __syncthreads();
+    }
+  };
 
-  uint8_t* dst = a.seg.records + (((size_t)task.b * a.hkv + h) * a.seg.slot_cap + task.dst_slot) * rbytes;
-  for (uint32_t off = tid * 16; off < rbytes; off += 256 * 16)
-    *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(rec + off);
-  if (h == 0 && tid == 0) {
-    int4 hd = make_int4(task.nvalid, (int)task.mask, task.rank_base, task.token_base);
-    *reinterpret_cast<int4*>(a.seg.headers + ((size_t)task.b * a.seg.slot_cap + task.dst_slot) * kHeaderBytes) = hd;
-  }
+  // ---- task loop: the next slot's rows are fetched before the current slot
+  // is processed; the record buffers alternate, so a slot's stores into one
+  // buffer never race the previous slot's copy-out of the other.  Key and
+  // value waves run separate copies of the loop (same barrier count, the
+  // branch is uniform per wave), so neither holds the other's registers.
+  // Every thread issues the same number of stores (buffer stores: lanes past
+  // the record, and the header store of all but one thread, fall outside the
+  // resource and are dropped), so the wait for the next slot's rows, which
+  // were loaded before these stores, is a fixed count.
+  constexpr int NST = (REC_MAX + 256 * 16 - 1) / (256 * 16);
+  auto copy_out = [&](const CommitTask& task, const uint8_t* rec) __attribute__((always_inline)) {
+    uint8_t* dst = a.seg.records + (((size_t)task.b * a.hkv + h) * a.seg.slot_cap + task.dst_slot) * rbytes;
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(dst, 0, rbytes, 0x00020000);
+#pragma unroll
+    for (int r = 0; r < NST; ++r) {
+      const uint32_t off = (r * 256 + tid) * 16;
+      const uint4 val = *reinterpret_cast<const uint4*>(rec + (off < REC_MAX ? off : REC_MAX - 16));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rr, off < rbytes ? off : 0x7ff00000u, 0, 0);
+    }
+    uint8_t* hdst = a.seg.headers + ((size_t)task.b * a.seg.slot_cap + task.dst_slot) * kHeaderBytes;
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(hdst, 0, kHeaderBytes, 0x00020000);
+    const int4 hd = make_int4(task.nvalid, (int)task.mask, task.rank_base, task.token_base);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, hd), hr,
+                                           (h == 0 && tid == 0) ? 0u : 0x7ff00000u, 0, 0);
+  };
+  auto run = [&](const bool role_keys) __attribute__((always_inline)) {
+    Raw raw;
+    fetch(blockIdx.x, task_at(blockIdx.x), raw);
+    {
+      // stores that fall outside their resource, in the shape of copy_out:
+      // the loop is then entered with the same pending loads and stores as
+      // from its back edge, and its waits stay at the fixed store count
+      const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.seg.headers, 0, 0, 0x00020000);
+      const __attribute__((ext_vector_type(4))) unsigned int z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < NST + 1; ++r) __builtin_amdgcn_raw_buffer_store_b128(z, none, 0x7ff00000u + 16u * r, 0, 0);
+    }
+    int it = 0;
+    for (int i = blockIdx.x; i < ntasks; i += G, ++it) {
+      // unpack this slot's rows, then reuse their registers for the next
+      // slot's loads
+      float x[TPL][8];
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) unpack_row(raw, k, x[k]);
+      const CommitTask task = task_at(i);
+      // stores of data-dependent count go before the next loads (see copy_out)
+      if (role_keys && task.mask != 0u) store_protected(task, x);
+      fetch(i + G, task_at(i + G < ntasks ? i + G : i), raw);
+      uint8_t* rec = recbuf[it & 1];
+      if (role_keys) process_keys(task, x, rec);
+      else           process_values(task, x, rec);
+      lds_barrier();
+      copy_out(task, rec);
+    }
+  };
+  if (keys) run(true);
+  else      run(false);
 }
 
+// Persistent grid: as many workgroups as the device holds at once (the
+// kernel's occupancy per CU times the CU count), spread over the kv heads;
+// each workgroup loops over its share of the slots.
 template <int KB, int VB, int D, bool F32IN>
 hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s) {
-  dim3 grid(ntasks, a.hkv);
-  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN>), grid, dim3(256), 0, s, a);
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN>, 256, 0) != hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  const int per_head = std::max(1, per_cu * a.num_cus / std::max(1, a.hkv));
+  dim3 grid(std::min(ntasks, per_head), a.hkv);
+  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN>), grid, dim3(256), 0, s, a, ntasks);
   return hipGetLastError();
 }
 

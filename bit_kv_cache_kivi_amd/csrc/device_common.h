@@ -119,4 +119,12 @@ __device__ __forceinline__ void unpack8(uint32_t w, float (&c)[8]) {
   }
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads and stores in
+// flight stay in flight across it (__syncthreads also waits for all of them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace kvq

@@ -349,6 +349,7 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     }
     a.k = d_k;
     a.v = d_v;
+    a.num_cus = c->num_cus;
     a.seg = seg_ptrs(c, segment);
     a.n_max = n_max;
     a.hkv = cfg.num_kv_heads;

@@ -45,7 +45,7 @@ struct CommitArgs {
   int32_t gv_log2;
   uint32_t record_bytes;
   int32_t use_inline;
-  int32_t pad_;
+  int32_t num_cus;          // compute units of the device (sizes the persistent grid)
   CommitTask inline_tasks[kInlineTasks];
 };
 
