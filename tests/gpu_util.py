@@ -5,6 +5,7 @@ import sys
 import numpy as np
 
 import oracle as O
+import workloads as W
 
 
 def announce(*msg):
@@ -68,3 +69,27 @@ def attention_error(out, ref, out_dtype="f32"):
     err = np.abs(o - ref)[mask]
     gate = 2e-3 if out_dtype == "f32" else 2e-3 + 0.5 * ulp_bf16(ref[mask])
     return float(err.max()), float((err - gate).max())
+
+
+def build_case(cfg, T=None, B=None, extra_slots=4):
+    """Seeded workload, a device cache and an oracle cache, both holding the
+    committed prefix (and suffix).  Shared by the GPU parity tests."""
+    from bit_kv_cache_kivi_amd import kvq
+    w = W.make(cfg, T=T, B=B)
+    c = w.cfg
+    nprot_p = max([len(p) for p in w.prot_prefix] + [0]) + 64
+    nprot_s = max([len(p) for p in (w.prot_suffix or [])] + [0]) + 64
+    cache = kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
+                        prefix_tokens=int(w.lengths.max()) + 32 * extra_slots,
+                        suffix_tokens=c.suffix + (32 if c.suffix else 0),
+                        prefix_protected=nprot_p, suffix_protected=nprot_s if c.suffix else 0,
+                        max_q_heads=c.Hq)
+    ora = O.OracleCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group)
+    prot = w.prot_prefix if c.prot_frac > 0 else None
+    cache.commit(dev(w.k_prefix, c.dtype), dev(w.v_prefix, c.dtype), ntok=w.lengths, protected=prot)
+    ora.commit(0, w.k_prefix, w.v_prefix, ntok=w.lengths, prot=prot)
+    if c.suffix:
+        sprot = w.prot_suffix if c.prot_frac > 0 else None
+        cache.commit(dev(w.k_suffix, c.dtype), dev(w.v_suffix, c.dtype), protected=sprot, segment=kvq.KVQ_SUFFIX)
+        ora.commit(1, w.k_suffix, w.v_suffix, prot=sprot)
+    return w, cache, ora

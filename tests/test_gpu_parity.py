@@ -20,28 +20,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from bit_kv_cache_kivi_amd import kvq  # noqa: E402
-from gpu_util import announce, attention_error, compare_commit, dev  # noqa: E402
-
-
-def build_case(cfg, T=None, B=None, extra_slots=4):
-    w = W.make(cfg, T=T, B=B)
-    c = w.cfg
-    nprot_p = max([len(p) for p in w.prot_prefix] + [0]) + 64
-    nprot_s = max([len(p) for p in (w.prot_suffix or [])] + [0]) + 64
-    cache = kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
-                        prefix_tokens=int(w.lengths.max()) + 32 * extra_slots,
-                        suffix_tokens=c.suffix + (32 if c.suffix else 0),
-                        prefix_protected=nprot_p, suffix_protected=nprot_s if c.suffix else 0,
-                        max_q_heads=c.Hq)
-    ora = O.OracleCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group)
-    prot = w.prot_prefix if c.prot_frac > 0 else None
-    cache.commit(dev(w.k_prefix, c.dtype), dev(w.v_prefix, c.dtype), ntok=w.lengths, protected=prot)
-    ora.commit(0, w.k_prefix, w.v_prefix, ntok=w.lengths, prot=prot)
-    if c.suffix:
-        sprot = w.prot_suffix if c.prot_frac > 0 else None
-        cache.commit(dev(w.k_suffix, c.dtype), dev(w.v_suffix, c.dtype), protected=sprot, segment=kvq.KVQ_SUFFIX)
-        ora.commit(1, w.k_suffix, w.v_suffix, prot=sprot)
-    return w, cache, ora
+from gpu_util import announce, attention_error, build_case, compare_commit, dev  # noqa: E402
 
 
 SMALL = [("tiny", None, None), ("llada8b", 512, None), ("dream7b_2bit", 384, 2), ("dream7b_4bit", 384, 2),
