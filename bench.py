@@ -35,6 +35,34 @@ import workloads as W  # noqa: E402
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
+# HBM bytes of one attention launch on this workload, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE passes (median KiB per dispatch over the rotation),
+# scaled by what the same counters read for a plain copy of 256 MiB
+# (bench.py --calibrate-copy 256: FETCH_SIZE reads 131084 KiB for 262144 KiB
+# moved, WRITE_SIZE 262144).  Valid only for the kernel source they were taken
+# on (its SHA-256); any other source reports null.
+_FETCH_SCALE = 262144.0 / 131084.0
+_WRITE_SCALE = 1.0
+MEASURED_TRAFFIC = {
+    "dream7b_4bit": {
+        "attn_source_sha256": "b38c355fa45b87889e6780f499b1616d0b0a30e627d8a812609052aa2a4ef670",
+        "kib": {"attn_kernel": {"fetch": 33495, "write": 29120},
+                "combine_kernel": {"fetch": 14594, "write": 1792}},
+    },
+}
+
+
+def measured_traffic(workload):
+    """Bytes per attention launch, or None if not measured for this source."""
+    import hashlib
+    m = MEASURED_TRAFFIC.get(workload)
+    if m is None:
+        return None
+    with open(os.path.join(ROOT, "bit_kv_cache_kivi_amd", "csrc", "attn.hip"), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != m["attn_source_sha256"]:
+            return None
+    return sum((k["fetch"] * _FETCH_SCALE + k["write"] * _WRITE_SCALE) * 1024.0 for k in m["kib"].values())
+
 
 def attn_algorithmic(cfg, ntok_per_seq, nslots_per_seq, nprot_per_seq, record_bytes):
     """Bytes the method must move and flops it must do for one attention call."""
@@ -92,7 +120,20 @@ def main():
     ap.add_argument("--layers", type=int, default=28, help="per-layer caches the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a device buffer of MIB MiB five times (a reference kernel of known "
+                         "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only: there is no multi-GPU path; "
                                    "run with --gpus 1"}), flush=True)
@@ -231,7 +272,8 @@ def main():
         "commit_gbs": commit_bytes / (commit_ms * 1e-3) / 1e9,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_F16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_F16_TFLOPS,
+                     "traffic": measured_traffic(c.name),
                      "kernel": "attention launch (attn_kernel + combine_kernel)",
                      "hbm_frac": a_bytes / attn_s / 1e9 / PEAK_HBM_GBS},
     }

@@ -548,15 +548,19 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   }
 }
 
-// One workgroup per (query head, sequence): merges the splits of all 32 rows.
-// Thread -> (4 consecutive query tokens, channels c, c+32, ...): every split's
-// partial is read with 16-byte loads, many in flight, and the result is
-// transposed through LDS for row-contiguous output stores.
+// One workgroup per (query head, sequence, 32-channel chunk): merges the
+// splits of all 32 rows for those channels.  Thread -> (query tokens
+// 4jq..4jq+3, one channel), jq fastest, so each 16-byte load of a wave covers
+// whole 128-byte rows of the partials.  The partial-O loads of the first
+// kBatch splits are issued before the merge weights are computed, and the
+// result is transposed through LDS for row-contiguous output stores.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
+  constexpr int CW = 32;        // channels per workgroup
+  constexpr int kBatch = 8;     // splits loaded at once
   __shared__ __align__(16) float w_lds[kMaxSplitsLds][kSlot];
-  __shared__ __align__(16) float out_lds[kSlot][D + 4];
-  const int hq = blockIdx.x, b = blockIdx.y;
+  __shared__ __align__(16) float out_lds[kSlot][CW + 4];
+  const int hq = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * CW;
   const int np = a.nslots[0][b];
   const int ns = a.use_suffix ? a.nslots[1][b] : 0;
   const int U = np + ns + 1;
@@ -566,6 +570,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
   const size_t pstride = (size_t)r * (D + 2) * kSlot;           // one split's partial
   const float* p0 = a.partial + ((((size_t)b * a.hkv + kvh) * a.max_splits) * r + hl) * (size_t)(D + 2) * kSlot;
+  const int jq = tid & 7, c = tid >> 3;
+  const float* pc = p0 + (size_t)(c0 + c) * kSlot + 4 * jq;
+  float4 v[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    if (u < nsplit) v[u] = *reinterpret_cast<const float4*>(pc + u * pstride);
   if (tid < kSlot) {
     float mstar = -__builtin_inff();
     for (int sp = 0; sp < nsplit; ++sp) mstar = fmaxf(mstar, p0[sp * pstride + D * kSlot + tid]);
@@ -579,60 +589,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
     for (int sp = 0; sp < nsplit; ++sp) w_lds[sp][tid] *= inv;
   }
   __syncthreads();
-  const int jq = tid & 7, c0 = tid >> 3;      // tokens 4jq..4jq+3, channels c0 + 32k
-  constexpr int NC = D / 32;
-  float4 acc[NC];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp0 = 0; sp0 < nsplit; sp0 += kBatch) {
+    if (sp0 > 0) {
 #pragma unroll
-  for (int k = 0; k < NC; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  int sp = 0;
-  for (; sp + 4 <= nsplit; sp += 4) {
-    float4 v[4][NC];
+      for (int u = 0; u < kBatch; ++u)
+        if (sp0 + u < nsplit) v[u] = *reinterpret_cast<const float4*>(pc + (sp0 + u) * pstride);
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int k = 0; k < NC; ++k)
-        v[u][k] = *reinterpret_cast<const float4*>(p0 + (sp + u) * pstride + (c0 + 32 * k) * kSlot + 4 * jq);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 wv = *reinterpret_cast<const float4*>(&w_lds[sp + u][4 * jq]);
-#pragma unroll
-      for (int k = 0; k < NC; ++k) {
-        acc[k].x = fmaf(v[u][k].x, wv.x, acc[k].x); acc[k].y = fmaf(v[u][k].y, wv.y, acc[k].y);
-        acc[k].z = fmaf(v[u][k].z, wv.z, acc[k].z); acc[k].w = fmaf(v[u][k].w, wv.w, acc[k].w);
+    for (int u = 0; u < kBatch; ++u) {
+      if (sp0 + u < nsplit) {
+        const float4 wv = *reinterpret_cast<const float4*>(&w_lds[sp0 + u][4 * jq]);
+        acc.x = fmaf(v[u].x, wv.x, acc.x); acc.y = fmaf(v[u].y, wv.y, acc.y);
+        acc.z = fmaf(v[u].z, wv.z, acc.z); acc.w = fmaf(v[u].w, wv.w, acc.w);
       }
     }
   }
-  for (; sp < nsplit; ++sp) {
-    const float4 wv = *reinterpret_cast<const float4*>(&w_lds[sp][4 * jq]);
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(p0 + sp * pstride + (c0 + 32 * k) * kSlot + 4 * jq);
-      acc[k].x = fmaf(v.x, wv.x, acc[k].x); acc[k].y = fmaf(v.y, wv.y, acc[k].y);
-      acc[k].z = fmaf(v.z, wv.z, acc[k].z); acc[k].w = fmaf(v.w, wv.w, acc[k].w);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    const int c = c0 + 32 * k;
-    out_lds[4 * jq + 0][c] = acc[k].x;
-    out_lds[4 * jq + 1][c] = acc[k].y;
-    out_lds[4 * jq + 2][c] = acc[k].z;
-    out_lds[4 * jq + 3][c] = acc[k].w;
-  }
+  out_lds[4 * jq + 0][c] = acc.x;
+  out_lds[4 * jq + 1][c] = acc.y;
+  out_lds[4 * jq + 2][c] = acc.z;
+  out_lds[4 * jq + 3][c] = acc.w;
   __syncthreads();
-  // row j of this head: D contiguous outputs, 4 per thread
-  for (int idx = tid; idx < kSlot * D / 4; idx += 256) {
-    const int jj = idx / (D / 4), c = 4 * (idx % (D / 4));
-    const size_t o = (((size_t)b * kSlot + jj) * a.hq + hq) * D + c;
-    const float4 v = *reinterpret_cast<const float4*>(&out_lds[jj][c]);
-    if (a.out_f32) {
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = v;
-    } else {
-      uint2 w;
-      w.x = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
-      w.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
-    }
+  // row jj of this head: channels c0 + 4*(tid % 8) .. +3
+  const int jj = tid >> 3, cc = 4 * (tid & 7);
+  const size_t o = (((size_t)b * kSlot + jj) * a.hq + hq) * D + c0 + cc;
+  const float4 res = *reinterpret_cast<const float4*>(&out_lds[jj][cc]);
+  if (a.out_f32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = res;
+  } else {
+    uint2 w;
+    w.x = f32_to_bf16_bits(res.x) | (f32_to_bf16_bits(res.y) << 16);
+    w.y = f32_to_bf16_bits(res.z) | (f32_to_bf16_bits(res.w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
   }
 }
 
@@ -644,7 +632,7 @@ hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) 
   else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8>), grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
