@@ -73,7 +73,8 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 
   __shared__ __align__(16) uint8_t rawbuf[2][S::STAGE];      // packed slot records / the block
   __shared__ __align__(16) uint4 prtbuf[2][GPT][NPT];        // a producer thread's protected-row chunks
-  __shared__ __align__(16) half8 kop[2][2][KS][64];          // [buffer][hi, lo][k-step][lane]
+  __shared__ __align__(16) half8 kop[2][KS][64];             // key hi tiles: [buffer][k-step][lane]
+  __shared__ __align__(16) uint2 klo[2][D / 64][64][4];      // key lo tiles (bf8): [buffer][64-channel block][lane][8-byte part]
   __shared__ __align__(16) half8 vop[3][CT][2][64];          // [buffer][channel tile][k-half][lane]
   __shared__ __align__(16) int4 hdr[kMaxUnits];
 
@@ -114,6 +115,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // ---------------- prologues (run inside the role branches below): headers
   // and the block's raw rows (producers), Q operands (consumers)
   half8 qop[KS];
+  v8i_t q8[D / 64];
 
   // ---------------- producers: register prefetch of one unit -- the slot
   // record (16-byte chunks, as laid out in memory) and this thread's chunks of
@@ -242,7 +244,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 
   // ---------------- producers: dequantize unit q into K buffer q & 1 and
   // V buffer q % 3
-  const float neg_one = opaque_neg_one();
+  const float neg4096 = opaque_neg_4096();
   auto dequant = [&](int q, uint32_t mask) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
@@ -273,7 +275,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], ksc[e], kzr[e]);
         }
-        store_hi_lo(kop[kb][0][ks][t + 32 * khh], kop[kb][1][ks][t + 32 * khh], x, neg_one);
+        store_hi_lo8(kop[kb][ks][t + 32 * khh], klo[kb][kcg >> 3][t + 32 * ((kcg >> 2) & 1)][kcg & 3], x, neg4096);
       }
       // V: channels vc0 + vi of token octet (mm, hh); 4-bit: word 2mm+hh of the
       // channel; 2-bit: half mm of word hh.
@@ -308,7 +310,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         const float4 x1 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg + 4);
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         const int hh = cg / (D / 16), s = cg % (D / 16);
-        store_hi_lo(kop[kb][0][s][t + 32 * hh], kop[kb][1][s][t + 32 * hh], x, neg_one);
+        store_hi_lo8(kop[kb][s][t + 32 * hh], klo[kb][cg >> 3][t + 32 * ((cg >> 2) & 1)][cg & 3], x, neg4096);
       }
 #pragma unroll
       for (int vi = 0; vi < VPT; ++vi) {
@@ -333,25 +335,36 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // The operand tiles are read from LDS a few k-steps ahead of the MFMAs
   // that use them (the scheduling barriers pin the interleave; left alone
   // the compiler issues each read right before its MFMA and waits for it).
+  // S^T = K_hi Q^T (fp16, v_mfma_f32_32x32x16_f16) + 2^-12 K_lo' Q8^T (bf8 x
+  // e4m3, v_mfma_scale_f32_32x32x64_f8f6f4 with an E8M0 scale of 2^-12 on K_lo')
+  constexpr int KB8 = D / 64;
   auto scores = [&](int q) __attribute__((always_inline)) {
     const int kb = q & 1;
-    half8 kh[KS], kl[KS];
+    half8 kh[KS];
+    v8i_t kl[KB8];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) { kh[s] = kop[kb][0][s][lane]; kl[s] = kop[kb][1][s][lane]; }
+    for (int s = 0; s < KS; ++s) kh[s] = kop[kb][s][lane];
+#pragma unroll
+    for (int k = 0; k < KB8; ++k) {
+      const uint4 l0 = *reinterpret_cast<const uint4*>(&klo[kb][k][lane][0]);
+      const uint4 l1 = *reinterpret_cast<const uint4*>(&klo[kb][k][lane][2]);
+      kl[k] = v8i_t{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[s], qop[s], sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl[s], qop[s], sacc, 0, 0, 0);
-    }
+    for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[s], qop[s], sacc, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < KB8; ++k)
+      sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl[k], q8[k], sacc, 1, 0, 0, 127 - 12, 0, 127);
+    constexpr int NR = KS + 2 * KB8, NM = KS + KB8;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // 4 LDS reads ahead
 #pragma unroll
-    for (int k = 0; k < 2 * KS - 4; ++k) {
+    for (int k = 0; k < NR - 4; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - 4), 0);
   };
   // nvalid (valid tokens of the unit) is read from the header one phase
   // ahead by the caller, so its LDS latency stays off the softmax path.
@@ -478,6 +491,39 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         const float x[8] = {bf16_lo(raw[s].x), bf16_hi(raw[s].x), bf16_lo(raw[s].y), bf16_hi(raw[s].y),
                             bf16_lo(raw[s].z), bf16_hi(raw[s].z), bf16_lo(raw[s].w), bf16_hi(raw[s].w)};
         qop[s] = to_half8(x);
+      }
+    }
+  }
+  {
+    // Q8: Q in e4m3 for the key lo product; lane = query token j, block k
+    // holds channels 64k + 32*hh + [0, 32) (the lo-tile layout)
+    const int j = lane & 31, hh = lane >> 5;
+    const size_t row = (((size_t)b * kSlot + j) * hq_all + kvh * r + min(ci, r - 1)) * D;
+#pragma unroll
+    for (int k = 0; k < KB8; ++k) {
+      const int c0 = 64 * k + 32 * hh;
+      float x[32];
+      if (q_f32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q_ptr) + row + c0);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float4 t = p[v];
+          x[4 * v] = t.x; x[4 * v + 1] = t.y; x[4 * v + 2] = t.z; x[4 * v + 3] = t.w;
+        }
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_ptr) + row + c0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 t = p[v];
+          x[8 * v] = bf16_lo(t.x); x[8 * v + 1] = bf16_hi(t.x); x[8 * v + 2] = bf16_lo(t.y); x[8 * v + 3] = bf16_hi(t.y);
+          x[8 * v + 4] = bf16_lo(t.z); x[8 * v + 5] = bf16_hi(t.z); x[8 * v + 6] = bf16_lo(t.w); x[8 * v + 7] = bf16_hi(t.w);
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w], x[4 * w + 1], 0u, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], d, true);
+        q8[k][w] = (int)d;
       }
     }
   }

@@ -9,6 +9,7 @@ namespace kvq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -91,6 +92,34 @@ __device__ __forceinline__ void store_hi_lo(half8& hi, half8& lo, const float (&
   }
   hi = h;
   lo = l;
+}
+
+// x -> hi = fp16(x) and lo = bf8(2^12 * (x - hi)) (two words, byte e =
+// element e; e5m2, round to nearest even).  hi + 2^-12 * lo keeps x to about
+// 2^-14 of its magnitude.  neg4096 is -4096 in a register the compiler cannot
+// see through, so that 2^12 * x - 2^12 * hi is one mixed-precision fma.
+__device__ __forceinline__ void store_hi_lo8(half8& hi, uint2& lo, const float (&x)[8], float neg4096) {
+  half8 h;
+  float l[8];
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const half2_t p = to_half2(x[i], x[i + 1]);
+    h[i] = p.x; h[i + 1] = p.y;
+    l[i] = fmaf(static_cast<float>(p.x), neg4096, x[i] * 4096.0f);
+    l[i + 1] = fmaf(static_cast<float>(p.y), neg4096, x[i + 1] * 4096.0f);
+  }
+  uint32_t w0 = __builtin_amdgcn_cvt_pk_bf8_f32(l[0], l[1], 0u, false);
+  w0 = __builtin_amdgcn_cvt_pk_bf8_f32(l[2], l[3], w0, true);
+  uint32_t w1 = __builtin_amdgcn_cvt_pk_bf8_f32(l[4], l[5], 0u, false);
+  w1 = __builtin_amdgcn_cvt_pk_bf8_f32(l[6], l[7], w1, true);
+  hi = h;
+  lo = make_uint2(w0, w1);
+}
+
+__device__ __forceinline__ float opaque_neg_4096() {
+  float m = -4096.0f;
+  asm("" : "+s"(m));
+  return m;
 }
 
 // Eight b-bit codes of a u32 as floats.  b = 4: code e at bits [4e, 4e+4);
