@@ -536,7 +536,12 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   if (late) {
     int nv = 0;
     for (int i = 0; i < n_int; ++i) {
+      // The late consumers' softmax and PV are the longest path of an
+      // interval (their V tiles and MFMAs queue behind the early consumers'
+      // scores); a higher issue priority on the SIMD for that phase shortens it.
+      __builtin_amdgcn_s_setprio(2);
       if (i >= 2 && i - 2 < NU) softmax_pv(i - 2, nv);
+      __builtin_amdgcn_s_setprio(0);
       if (i >= 1 && i - 1 < NU) {
         nv = hdr[i - 1].x;
         scores(i - 1);
