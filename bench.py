@@ -45,9 +45,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "b38c355fa45b87889e6780f499b1616d0b0a30e627d8a812609052aa2a4ef670",
-        "kib": {"attn_kernel": {"fetch": 33495, "write": 29120},
-                "combine_kernel": {"fetch": 14594, "write": 1792}},
+        "attn_source_sha256": "5903561654693f578efb8edf294033466ecd9e7dec71c317b3c888d419e02992",
+        "kib": {"attn_kernel": {"fetch": 33510, "write": 29120},
+                "combine_kernel": {"fetch": 14597, "write": 1792}},
     },
 }
 
