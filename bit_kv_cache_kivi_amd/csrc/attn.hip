@@ -11,11 +11,12 @@
 // and a contiguous range of units, and is split into two roles:
 //   * 4 producer waves (one per SIMD) stream the packed slot records and the
 //     protected bf16 key rows from HBM (buffer loads into registers, three
-//     units ahead), stage them in LDS, and dequantize each unit into fp16 MFMA
-//     operand tiles: K as an fp16 hi + lo pair (the scores keep about 22 bits
-//     of the dequantized keys), V as fp16;
+//     units ahead), stage them in LDS, and dequantize each unit into MFMA
+//     operand tiles: K as hi = fp16(x) plus an e5m2 lo part holding
+//     2^12 (x - hi), V as fp16;
 //   * one consumer wave per query head of the kv head (32 query tokens = one
-//     32-wide MFMA tile) runs S^T = K Q^T on v_mfma_f32_32x32x16_f16, an online
+//     32-wide MFMA tile) runs S^T = K Q^T (hi on v_mfma_f32_32x32x16_f16, lo
+//     against an e4m3 copy of Q on the scaled fp8 MFMA), an online
 //     softmax in fp32 (exp2 with the scale folded in; the reference maximum is
 //     raised only when the running maximum exceeds it by more than 2^8, so O is
 //     rarely rescaled) and O^T += V^T P^T.  The transposed products let the S
@@ -23,10 +24,12 @@
 //     lane).
 // A slot is dequantized once per workgroup and shared by all query heads
 // through LDS.  One barrier per unit: in interval i producers store unit i+1,
-// dequantize unit i and issue the loads of unit i+3, while consumers work on
-// unit i-1.  Consumers 4..7 run half a unit behind (softmax and PV of unit
-// i-2, then the scores of unit i-1), so on each SIMD one consumer's MFMA work
-// overlaps the other consumer's softmax and the producer's dequantization.
+// issue the loads of unit i+3 and dequantize unit i, while consumers work on
+// units i-2 and i-1.  Consumers 0..3 first issue the PV of unit i-2 and the
+// scores of unit i-1 to the MFMA pipe, then run the softmax of unit i-1;
+// consumers 4..7 first run the softmax of unit i-2, then its PV and the
+// scores of unit i-1.  On each SIMD one consumer's MFMA work thus overlaps
+// the other consumer's softmax and the producer's dequantization.
 // A split's partial (reference maximum, sum, unnormalised O) goes to the
 // workspace and the combine kernel merges splits with log-sum-exp weights; a
 // single split writes the normalised output itself.
@@ -74,7 +77,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   __shared__ __align__(16) uint8_t rawbuf[2][S::STAGE];      // packed slot records / the block
   __shared__ __align__(16) uint4 prtbuf[2][GPT][NPT];        // a producer thread's protected-row chunks
   __shared__ __align__(16) half8 kop[2][KS][64];             // key hi tiles: [buffer][k-step][lane]
-  __shared__ __align__(16) uint2 klo[2][D / 64][64][4];      // key lo tiles (bf8): [buffer][64-channel block][lane][8-byte part]
+  __shared__ __align__(16) uint4 klo[2][D / 64][2][64];      // key lo tiles (bf8): [buffer][64-channel block][16-byte half][lane]
   __shared__ __align__(16) half8 vop[3][CT][2][64];          // [buffer][channel tile][k-half][lane]
   __shared__ __align__(16) int4 hdr[kMaxUnits];
 
@@ -145,12 +148,19 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // Producer thread -> work mapping.  K: the thread's GPT (token, 8-channel
   // group) pairs share the group (tokens kt0 + KTT*gi of group kcg), so the
   // group's scales and zeros are read once.  V: the thread's VPT (channel,
-  // token octet) pairs share the octet and the channel group (channels
-  // vc0 + vi of octet vcombo), so the tokens' scales and zeros are read once.
+  // token octet) pairs share the octet vcombo and the channel group, so the
+  // tokens' scales and zeros are read once.  With value groups of 64 or more
+  // channels, lane j takes channels j%32 + 32*(vi + VPT*(j/32)), so that
+  // consecutive lanes write consecutive operand rows (no LDS bank conflicts);
+  // with 32-channel groups, channels VPT*j + vi.
   constexpr int KTT = kSlot / GPT;
-  constexpr int VCT = D / VPT;
+  static_assert(D / VPT == 64, "one V channel set per lane");
   const int kt0 = tid % KTT, kcg = tid / KTT;
-  const int vc0 = VPT * (tid % VCT), vcombo = tid / VCT;
+  const int vcombo = tid / 64;
+  int vch[VPT];
+#pragma unroll
+  for (int vi = 0; vi < VPT; ++vi)
+    vch[vi] = gv_log2 >= 6 ? (lane & 31) + 32 * (vi + VPT * (lane >> 5)) : VPT * lane + vi;
   constexpr int kOutOfRange = 0x7ff00000;
   bool rec_chunk[RPT];
 #pragma unroll
@@ -163,7 +173,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   const uint8_t* vblk_base = static_cast<const uint8_t*>(v_blk) + ((size_t)b * kSlot * hkv + kvh) * D * 2;
   const int blk_n = kSlot * hkv * D * 2;
   const int blk_row = hkv * D * 2;                 // bytes between the block's token rows
-  auto load_unit = [&](int q, Pre& pr) __attribute__((always_inline)) {
+  auto load_unit = [&](int q, Pre& pr, const int4 h) __attribute__((always_inline)) {
     const bool valid = q < nq;
     const bool blk_unit = has_block && q == nq && !blk_f32;
     const int u = u0 + (valid ? q : 0), sg = valid ? seg_of(u) : 0;
@@ -183,9 +193,8 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       const int off = blk_unit ? boff : (valid && rec_chunk[j]) ? rbase + idx * 16 : kOutOfRange;
       pr.rec[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
     }
-    // header read unconditionally (clamped index) and masked by a select, so
-    // no branch splits the loads of a unit
-    const int4 h = hdr[min(q, kMaxUnits - 1)];
+    // header read by the caller (clamped index) and masked by a select, so no
+    // branch splits the loads of a unit
     const uint32_t mask = valid ? (uint32_t)h.y : 0u;
     pr.mask = mask;
 #pragma unroll
@@ -243,62 +252,82 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   };
 
   // ---------------- producers: dequantize unit q into K buffer q & 1 and
-  // V buffer q % 3
-  const float neg4096 = opaque_neg_4096();
-  auto dequant = [&](int q, uint32_t mask) __attribute__((always_inline)) {
+  // V buffer q % 3.  dq_fetch issues every LDS read of a unit (code words,
+  // scales and zeros, the protected chunks) at the start of an interval, so
+  // that their latency overlaps the stores and loads of other units;
+  // dequant does the arithmetic.  The reads are unconditional (the addresses
+  // stay inside the stage whatever it holds); values a unit does not use are
+  // ignored.
+  const float neg_one = opaque_neg_one();
+  const int khh = kcg / (D / 16), kks = kcg % (D / 16);
+  const int vmm = vcombo >> 1, vhh = vcombo & 1;
+  const int vta = 16 * vmm + 4 * vhh;       // value tokens vta..vta+3, vta+8..vta+11
+  // the 8-byte lo part of channel group cg, token t: byte j of lane l of
+  // 64-channel block k holds channel 64k + 32(l/32) + j of token l%32
+  auto klo_part = [&](int kb, int cg, int t) __attribute__((always_inline)) -> uint2& {
+    return reinterpret_cast<uint2*>(&klo[kb][cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1];
+  };
+  struct DqIn { uint32_t kw[GPT]; uint4 kp[GPT]; float4 ks[2], kz[2]; uint32_t vw[VPT]; float4 vs[2], vz[2]; };
+  auto dq_fetch = [&](int q, DqIn& d) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
+    // K: tokens kt0 + KTT*gi of channel group kcg; their codes are word kcg
+    // (4-bit) or half kcg % 2 of word kcg / 2 (2-bit) of the token's word column.
+    const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC) + 8 * kcg;
+    d.ks[0] = *reinterpret_cast<const float4*>(kmeta);
+    d.ks[1] = *reinterpret_cast<const float4*>(kmeta + 4);
+    d.kz[0] = *reinterpret_cast<const float4*>(kmeta + D);
+    d.kz[1] = *reinterpret_cast<const float4*>(kmeta + D + 4);
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int t = kt0 + KTT * gi;
+      d.kw[gi] = KB == 4 ? words[kcg * 32 + t] : words[(kcg >> 1) * 32 + t];
+      d.kp[gi] = prtbuf[q & 1][gi][tid];
+    }
+    // V: channels vch[vi] of token octet (vmm, vhh); 4-bit: word 2vmm+vhh of
+    // the channel; 2-bit: half vmm of word vhh.
+    const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (vch[0] >> gv_log2) * 256);
+    d.vs[0] = *reinterpret_cast<const float4*>(vs + vta);
+    d.vs[1] = *reinterpret_cast<const float4*>(vs + vta + 8);
+    d.vz[0] = *reinterpret_cast<const float4*>(vs + 32 + vta);
+    d.vz[1] = *reinterpret_cast<const float4*>(vs + 32 + vta + 8);
+#pragma unroll
+    for (int vi = 0; vi < VPT; ++vi)
+      d.vw[vi] = VB == 4 ? words[KC / 4 + (2 * vmm + vhh) * D + vch[vi]] : words[KC / 4 + vhh * D + vch[vi]];
+  };
+  auto dequant = [&](int q, uint32_t mask, const DqIn& d) __attribute__((always_inline)) {
+    const uint8_t* rawS = rawbuf[q & 1];
     const int kb = q & 1, vbuf = q % 3;
     if (q < nq) {
-      // K: tokens kt0 + KTT*gi of channel group kcg; their codes are word kcg
-      // (4-bit) or half kcg % 2 of word kcg / 2 (2-bit) of the token's word column.
-      const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC) + 8 * kcg;
-      const float4 ks0 = *reinterpret_cast<const float4*>(kmeta);
-      const float4 ks1 = *reinterpret_cast<const float4*>(kmeta + 4);
-      const float4 kz0 = *reinterpret_cast<const float4*>(kmeta + D);
-      const float4 kz1 = *reinterpret_cast<const float4*>(kmeta + D + 4);
-      const float ksc[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
-      const float kzr[8] = {kz0.x, kz0.y, kz0.z, kz0.w, kz1.x, kz1.y, kz1.z, kz1.w};
-      const int khh = kcg / (D / 16), ks = kcg % (D / 16);
+      const float ksc[8] = {d.ks[0].x, d.ks[0].y, d.ks[0].z, d.ks[0].w, d.ks[1].x, d.ks[1].y, d.ks[1].z, d.ks[1].w};
+      const float kzr[8] = {d.kz[0].x, d.kz[0].y, d.kz[0].z, d.kz[0].w, d.kz[1].x, d.kz[1].y, d.kz[1].z, d.kz[1].w};
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
         const int t = kt0 + KTT * gi;
         float x[8];
         if ((mask >> t) & 1u) {
-          const uint4 w = prtbuf[q & 1][gi][tid];
+          const uint4 w = d.kp[gi];
           x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
           x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
         } else {
-          const uint32_t w = KB == 4 ? words[kcg * 32 + t] : words[(kcg >> 1) * 32 + t] >> (16 * (kcg & 1));
           float code[8];
-          unpack8<KB>(w, code);
+          unpack8<KB>(KB == 4 ? d.kw[gi] : d.kw[gi] >> (16 * (kcg & 1)), code);
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], ksc[e], kzr[e]);
         }
-        store_hi_lo8(kop[kb][ks][t + 32 * khh], klo[kb][kcg >> 3][t + 32 * ((kcg >> 2) & 1)][kcg & 3], x, neg4096);
+        store_hi_lo8(kop[kb][kks][t + 32 * khh], klo_part(kb, kcg, t), x, neg_one);
       }
-      // V: channels vc0 + vi of token octet (mm, hh); 4-bit: word 2mm+hh of the
-      // channel; 2-bit: half mm of word hh.
-      const int mm = vcombo >> 1, hh = vcombo & 1;
-      const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (vc0 >> gv_log2) * 256);
-      const int ta = 16 * mm + 4 * hh;        // tokens ta..ta+3, ta+8..ta+11
-      const float4 vs0 = *reinterpret_cast<const float4*>(vs + ta);
-      const float4 vs1 = *reinterpret_cast<const float4*>(vs + ta + 8);
-      const float4 vz0 = *reinterpret_cast<const float4*>(vs + 32 + ta);
-      const float4 vz1 = *reinterpret_cast<const float4*>(vs + 32 + ta + 8);
-      const float vsc[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
-      const float vzr[8] = {vz0.x, vz0.y, vz0.z, vz0.w, vz1.x, vz1.y, vz1.z, vz1.w};
+      const float vsc[8] = {d.vs[0].x, d.vs[0].y, d.vs[0].z, d.vs[0].w, d.vs[1].x, d.vs[1].y, d.vs[1].z, d.vs[1].w};
+      const float vzr[8] = {d.vz[0].x, d.vz[0].y, d.vz[0].z, d.vz[0].w, d.vz[1].x, d.vz[1].y, d.vz[1].z, d.vz[1].w};
 #pragma unroll
       for (int vi = 0; vi < VPT; ++vi) {
-        const int c = vc0 + vi;
-        const uint32_t w = VB == 4 ? words[KC / 4 + (2 * mm + hh) * D + c]
-                                   : words[KC / 4 + hh * D + c] >> (16 * mm);
+        const int c = vch[vi];
         float code[8];
-        unpack8<VB>(w, code);
+        unpack8<VB>(VB == 4 ? d.vw[vi] : d.vw[vi] >> (16 * vmm), code);
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], vsc[e], vzr[e]);
-        vop[vbuf][c >> 5][mm][(c & 31) + 32 * hh] = to_half8(x);
+        vop[vbuf][c >> 5][vmm][(c & 31) + 32 * vhh] = to_half8(x);
       }
     } else if (q == nq && has_block) {
       const float* kst = reinterpret_cast<const float*>(rawS);
@@ -309,16 +338,15 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         const float4 x0 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg);
         const float4 x1 = *reinterpret_cast<const float4*>(kst + t * D + 8 * cg + 4);
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        const int hh = cg / (D / 16), s = cg % (D / 16);
-        store_hi_lo8(kop[kb][s][t + 32 * hh], klo[kb][cg >> 3][t + 32 * ((cg >> 2) & 1)][cg & 3], x, neg4096);
+        store_hi_lo8(kop[kb][kks][t + 32 * khh], klo_part(kb, cg, t), x, neg_one);
       }
 #pragma unroll
       for (int vi = 0; vi < VPT; ++vi) {
-        const int c = vc0 + vi, mm = vcombo >> 1, hh = vcombo & 1;
+        const int c = vch[vi];
         half8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = vst[(16 * mm + 4 * hh + (e & 3) + 8 * (e >> 2)) * D + c];
-        vop[vbuf][c >> 5][mm][(c & 31) + 32 * hh] = v;
+        for (int e = 0; e < 8; ++e) v[e] = vst[(vta + (e & 3) + 8 * (e >> 2)) * D + c];
+        vop[vbuf][c >> 5][vmm][(c & 31) + 32 * vhh] = v;
       }
     }
   };
@@ -346,8 +374,8 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     for (int s = 0; s < KS; ++s) kh[s] = kop[kb][s][lane];
 #pragma unroll
     for (int k = 0; k < KB8; ++k) {
-      const uint4 l0 = *reinterpret_cast<const uint4*>(&klo[kb][k][lane][0]);
-      const uint4 l1 = *reinterpret_cast<const uint4*>(&klo[kb][k][lane][2]);
+      const uint4 l0 = klo[kb][k][0][lane];
+      const uint4 l1 = klo[kb][k][1][lane];
       kl[k] = v8i_t{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
     }
 #pragma unroll
@@ -357,22 +385,20 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 #pragma unroll
     for (int k = 0; k < KB8; ++k)
       sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl[k], q8[k], sacc, 1, 0, 0, 127 - 12, 0, 127);
-    constexpr int NR = KS + 2 * KB8, NM = KS + KB8;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // 4 LDS reads ahead
+    constexpr int NR = KS + 2 * KB8, NM = KS + KB8, AHEAD = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);    // LDS reads ahead
 #pragma unroll
-    for (int k = 0; k < NR - 4; ++k) {
+    for (int k = 0; k < NR - AHEAD; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - 4), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - AHEAD), 0);
   };
   // nvalid (valid tokens of the unit) is read from the header one phase
   // ahead by the caller, so its LDS latency stays off the softmax path.
-  auto softmax_pv = [&](int q, int nvalid) __attribute__((always_inline)) {
-    const int vbuf = q % 3;
-    half8 va[CT][2];                     // first k-half of the V operands, read before the softmax
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) va[ct][0] = vop[vbuf][ct][0][lane];
+  // softmax of the scores in sacc: P (fp16, the PV B operand) into pop; the
+  // running maximum, sum and O are updated.
+  auto softmax = [&](int nvalid, half8 (&pop)[2]) __attribute__((always_inline)) {
     // sacc[i] = S[query lane%32][token 8*(i/4) + 4*(lane/32) + i%4]
     if (nvalid < kSlot) {
 #pragma unroll
@@ -401,7 +427,6 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     // P is rounded to fp16 for the PV product; the row sum takes the same
     // rounded values (v_dot2_f32_f16 against (1, 1)), so numerator and
     // denominator see identical weights.
-    half8 pop[2];
     float psum = l_run;
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
@@ -413,8 +438,8 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       psum = __builtin_amdgcn_fdot2(pp, ones, psum, false);
     }
     l_run = psum;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) va[ct][1] = vop[vbuf][ct][1][lane];
+  };
+  auto pv = [&](const half8 (&va)[CT][2], const half8 (&pop)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
       o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ct][0], pop[0], o[ct], 0, 0, 0);
@@ -422,17 +447,25 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     for (int ct = 0; ct < CT; ++ct)
       o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ct][1], pop[1], o[ct], 0, 0, 0);
   };
+  // V operands of unit q, k-half kh
+  auto read_v = [&](int q, int kh, half8 (&va)[CT][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) va[ct][kh] = vop[q % 3][ct][kh][lane];
+  };
 
   // ---------------- pipeline.  Interval i: producers store unit i+1 (register
-  // set (i+1) & 1), dequantize unit i and load unit i+3 into the freed set;
-  // early consumers take unit i-1; late consumers finish unit i-2 and score
+  // set (i+1) & 1), load unit i+3 into the freed set and dequantize unit i;
+  // early consumers run the PV of unit i-2 and the scores and softmax of unit
+  // i-1; late consumers run the softmax and PV of unit i-2 and the scores of
   // unit i-1.  Producers and consumers run separate loops with the same
   // barrier count (the branch is uniform per wave), so neither role holds the
   // other's loop-carried registers.
-  // intervals, rounded up to even so that the producer loop (unrolled by two
-  // for its two register sets) has no conditional half: a conditional half
-  // would merge register states at the latch and force waits on in-flight loads
-  const int n_int = (NU + (NC > 4 ? 2 : 1) + 1) & ~1;
+  // intervals: unit q is dequantized in interval q and its PV runs in
+  // interval q + 2, so NU + 2 intervals, rounded up to even so that the
+  // producer loop (unrolled by two for its two register sets) has no
+  // conditional half: a conditional half would merge register states at the
+  // latch and force waits on in-flight loads
+  const int n_int = (NU + 3) & ~1;
   if (producer) {
       for (int i = tid; i < nq; i += NPT) {
         const int u = u0 + i, seg = seg_of(u);
@@ -442,24 +475,36 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       }
       if (tid == 0 && has_block) hdr[nq] = make_int4(kSlot, 0, 0, 0);
     __syncthreads();                         // headers in LDS
+    auto hdr_at = [&](int q) { return hdr[min(q, kMaxUnits - 1)]; };
     Pre pre0, pre1;
-    load_unit(0, pre0);
-    load_unit(1, pre1);
+    load_unit(0, pre0, hdr_at(0));
+    load_unit(1, pre1, hdr_at(1));
     store_unit(0, pre0);
     uint32_t dmask = pre0.mask;              // protected mask of the unit dequantized next
-    load_unit(2, pre0);
+    load_unit(2, pre0, hdr_at(2));
     __syncthreads();
+    // Interval order: LDS reads of the header of the unit to load (first, so
+    // that waiting for it does not wait for the rest) and of the unit to
+    // dequantize; store the next unit (its loads have landed); issue the loads
+    // three units ahead; then the dequantization arithmetic.
     for (int i = 0; i < n_int; i += 2) {
+      const int4 h3 = hdr_at(i + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      DqIn d;
+      dq_fetch(i, d);
       store_unit(i + 1, pre1);
       const uint32_t m1 = pre1.mask;
-      if (i < NU) dequant(i, dmask);
-      load_unit(i + 3, pre1);
+      load_unit(i + 3, pre1, h3);
+      if (i < NU) dequant(i, dmask, d);
       __syncthreads();
+      const int4 h4 = hdr_at(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_fetch(i + 1, d);
       store_unit(i + 2, pre0);
       const uint32_t m0 = pre0.mask;
-      if (i + 1 < NU) dequant(i + 1, m1);
+      load_unit(i + 4, pre0, h4);
+      if (i + 1 < NU) dequant(i + 1, m1, d);
       dmask = m0;
-      load_unit(i + 4, pre0);
       __syncthreads();
     }
     return;
@@ -533,14 +578,21 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     for (int i = 0; i < n_int; ++i) __syncthreads();
     return;
   }
+  half8 pop[2], va[CT][2];
   if (late) {
+    // Interval i: softmax and PV of unit i-2, then the scores of unit i-1.
     int nv = 0;
     for (int i = 0; i < n_int; ++i) {
       // The late consumers' softmax and PV are the longest path of an
       // interval (their V tiles and MFMAs queue behind the early consumers'
       // scores); a higher issue priority on the SIMD for that phase shortens it.
       __builtin_amdgcn_s_setprio(2);
-      if (i >= 2 && i - 2 < NU) softmax_pv(i - 2, nv);
+      if (i >= 2 && i - 2 < NU) {
+        read_v(i - 2, 0, va);
+        softmax(nv, pop);
+        read_v(i - 2, 1, va);
+        pv(va, pop);
+      }
       __builtin_amdgcn_s_setprio(0);
       if (i >= 1 && i - 1 < NU) {
         nv = hdr[i - 1].x;
@@ -549,11 +601,24 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       __syncthreads();
     }
   } else {
+    // Interval i: PV of unit i-2 (P kept from the previous interval) and the
+    // scores of unit i-1 go to the MFMA pipe back to back, then the softmax
+    // of unit i-1; the late consumer on the same SIMD runs its softmax first
+    // and its MFMAs second, so the two alternate between vector ALU and MFMA.
     for (int i = 0; i < n_int; ++i) {
+      if (i >= 2 && i - 2 < NU) {
+        read_v(i - 2, 0, va);
+        read_v(i - 2, 1, va);
+        pv(va, pop);
+        // every V read, then the MFMAs (left alone, the compiler issues each
+        // read right before its MFMA and waits for it)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * CT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * CT, 0);
+      }
       if (i >= 1 && i - 1 < NU) {
         const int nv = hdr[i - 1].x;
         scores(i - 1);
-        softmax_pv(i - 1, nv);
+        softmax(nv, pop);
       }
       __syncthreads();
     }

@@ -78,48 +78,34 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// x -> (hi, lo) fp16 pair with hi = fp16(x), lo = fp16(x - hi): hi + lo keeps
-// about 22 significant bits of x.
-__device__ __forceinline__ void store_hi_lo(half8& hi, half8& lo, const float (&x)[8], float neg_one) {
-  half8 h, l;
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const half2_t p = to_half2(x[i], x[i + 1]);
-    const half2_t q = to_half2(fmaf(static_cast<float>(p.x), neg_one, x[i]),
-                               fmaf(static_cast<float>(p.y), neg_one, x[i + 1]));
-    h[i] = p.x; h[i + 1] = p.y;
-    l[i] = q.x; l[i + 1] = q.y;
-  }
-  hi = h;
-  lo = l;
-}
+typedef short short2_t __attribute__((ext_vector_type(2)));
 
 // x -> hi = fp16(x) and lo = bf8(2^12 * (x - hi)) (two words, byte e =
 // element e; e5m2, round to nearest even).  hi + 2^-12 * lo keeps x to about
-// 2^-14 of its magnitude.  neg4096 is -4096 in a register the compiler cannot
-// see through, so that 2^12 * x - 2^12 * hi is one mixed-precision fma.
-__device__ __forceinline__ void store_hi_lo8(half8& hi, uint2& lo, const float (&x)[8], float neg4096) {
+// 2^-14 of its magnitude.  x - hi is exact in fp32 and is one mixed-precision
+// fma against neg_one (-1 in a register the compiler cannot see through); the
+// 2^12 comes from the scaled conversion, which divides its inputs by the scale
+// operand (here 2^-12).
+__device__ __forceinline__ void store_hi_lo8(half8& hi, uint2& lo, const float (&x)[8], float neg_one) {
+  constexpr float kLoScale = 1.0f / 4096.0f;
   half8 h;
   float l[8];
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
     const half2_t p = to_half2(x[i], x[i + 1]);
     h[i] = p.x; h[i + 1] = p.y;
-    l[i] = fmaf(static_cast<float>(p.x), neg4096, x[i] * 4096.0f);
-    l[i + 1] = fmaf(static_cast<float>(p.y), neg4096, x[i + 1] * 4096.0f);
+    l[i] = fmaf(static_cast<float>(p.x), neg_one, x[i]);
+    l[i + 1] = fmaf(static_cast<float>(p.y), neg_one, x[i + 1]);
   }
-  uint32_t w0 = __builtin_amdgcn_cvt_pk_bf8_f32(l[0], l[1], 0u, false);
-  w0 = __builtin_amdgcn_cvt_pk_bf8_f32(l[2], l[3], w0, true);
-  uint32_t w1 = __builtin_amdgcn_cvt_pk_bf8_f32(l[4], l[5], 0u, false);
-  w1 = __builtin_amdgcn_cvt_pk_bf8_f32(l[6], l[7], w1, true);
+  // the first conversion of each word writes its low half and the second its
+  // high half, so the old value of the first is arbitrary: an input that dies
+  // there, which spares a register copy
+  short2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(__builtin_bit_cast(short2_t, l[0]), l[0], l[1], kLoScale, false);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w0, l[2], l[3], kLoScale, true);
+  short2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(__builtin_bit_cast(short2_t, l[4]), l[4], l[5], kLoScale, false);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w1, l[6], l[7], kLoScale, true);
   hi = h;
-  lo = make_uint2(w0, w1);
-}
-
-__device__ __forceinline__ float opaque_neg_4096() {
-  float m = -4096.0f;
-  asm("" : "+s"(m));
-  return m;
+  lo = make_uint2(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1));
 }
 
 // Eight b-bit codes of a u32 as floats.  b = 4: code e at bits [4e, 4e+4);

@@ -80,6 +80,23 @@ def test_adversarial_groups():
         compare_commit(cache, ora, 0, B)
 
 
+@pytest.mark.parametrize("kb,vb,gv", [(4, 4, 32), (2, 2, 32), (4, 2, 128), (2, 4, 128)])
+def test_attention_value_groups_d128(kb, vb, gv):
+    """Head dim 128 with every value-group size and bit width: the producer
+    thread mapping differs between 32-channel groups and wider ones."""
+    announce("value groups d128", kb, vb, gv)
+    import dataclasses
+    cfg = dataclasses.replace(W.CONFIGS["dream7b_4bit"], k_bits=kb, v_bits=vb, v_group=gv)
+    w, cache, ora = build_case(cfg, T=300, B=2)
+    c = w.cfg
+    compare_commit(cache, ora, 0, c.B)
+    ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk)
+    out = cache.block_attn(dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype), out_dtype=torch.float32)
+    e, x = attention_error(out, ref, "f32")
+    print(f"kb={kb} vb={vb} gv={gv}: fp32-out err={e:.2e}")
+    assert x <= 0, f"fp32 output error {e}"
+
+
 def test_reset_suffix_and_dual():
     announce("suffix reset")
     cfg = W.CONFIGS["dual_long"]
