@@ -607,20 +607,28 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     // and its MFMAs second, so the two alternate between vector ALU and MFMA.
     for (int i = 0; i < n_int; ++i) {
       if (i >= 2 && i - 2 < NU) {
-        read_v(i - 2, 0, va);
         read_v(i - 2, 1, va);
         pv(va, pop);
-        // every V read, then the MFMAs (left alone, the compiler issues each
-        // read right before its MFMA and waits for it)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * CT, 0);
+        // the second-half reads, then the MFMAs (left alone, the compiler
+        // issues each read right before its MFMA and waits for it)
+        __builtin_amdgcn_sched_group_barrier(0x100, CT, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * CT, 0);
       }
       if (i >= 1 && i - 1 < NU) {
         const int nv = hdr[i - 1].x;
         scores(i - 1);
         softmax(nv, pop);
+        // first V k-half of unit i-1 for the next interval's PV, in flight
+        // across the barrier
+        __builtin_amdgcn_sched_barrier(0);
+        read_v(i - 1, 0, va);
       }
-      __syncthreads();
+      // A consumer only reads LDS, so its barrier needs no release fence and
+      // the reads above stay in flight across it (a unit's V tile is rewritten
+      // three intervals after it is produced); the acquire fence keeps the
+      // next interval's reads below the barrier.
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     }
   }
 
