@@ -45,9 +45,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "5903561654693f578efb8edf294033466ecd9e7dec71c317b3c888d419e02992",
-        "kib": {"attn_kernel": {"fetch": 33510, "write": 29120},
-                "combine_kernel": {"fetch": 14597, "write": 1792}},
+        "attn_source_sha256": "b21517dab616fea7fabae1a9da105537f3c58dec54a8b480581e5bbaa90ca78c",
+        "kib": {"attn_kernel": {"fetch": 33512, "write": 29120},
+                "combine_kernel": {"fetch": 14590, "write": 1792}},
     },
 }
 
