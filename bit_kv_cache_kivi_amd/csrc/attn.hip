@@ -485,8 +485,10 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     __syncthreads();
     // Interval order: LDS reads of the header of the unit to load (first, so
     // that waiting for it does not wait for the rest) and of the unit to
-    // dequantize; store the next unit (its loads have landed); issue the loads
-    // three units ahead; then the dequantization arithmetic.
+    // dequantize; store the next unit (its loads have landed); the
+    // dequantization arithmetic, as soon as its reads land (it then runs while
+    // the early consumers' MFMAs do, and is done before their softmax); last,
+    // the loads three units ahead.
     for (int i = 0; i < n_int; i += 2) {
       const int4 h3 = hdr_at(i + 3);
       __builtin_amdgcn_sched_barrier(0);
@@ -494,17 +496,17 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       dq_fetch(i, d);
       store_unit(i + 1, pre1);
       const uint32_t m1 = pre1.mask;
-      load_unit(i + 3, pre1, h3);
       if (i < NU) dequant(i, dmask, d);
+      load_unit(i + 3, pre1, h3);
       __syncthreads();
       const int4 h4 = hdr_at(i + 4);
       __builtin_amdgcn_sched_barrier(0);
       dq_fetch(i + 1, d);
       store_unit(i + 2, pre0);
       const uint32_t m0 = pre0.mask;
-      load_unit(i + 4, pre0, h4);
       if (i + 1 < NU) dequant(i + 1, m1, d);
       dmask = m0;
+      load_unit(i + 4, pre0, h4);
       __syncthreads();
     }
     return;
