@@ -91,8 +91,9 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   const void* const k_blk = a.k_blk;
   const void* const v_blk = a.v_blk;
   const SegPtrs seg0 = a.seg[0], seg1 = a.seg[1];
-  const int np = a.nslots[0][b];
-  const int ns = a.use_suffix ? a.nslots[1][b] : 0;
+  // both counts read unconditionally, so the two loads overlap
+  const int np = a.nslots[0][b], ns_all = a.nslots[1][b];
+  const int ns = a.use_suffix ? ns_all : 0;
   const int U = np + ns + 1;                 // slots + the block itself
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (split >= nsplit) return;
@@ -687,8 +688,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   __shared__ __align__(16) float w_lds[kMaxSplitsLds][kSlot];
   __shared__ __align__(16) float out_lds[kSlot][CW + 4];
   const int hq = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * CW;
-  const int np = a.nslots[0][b];
-  const int ns = a.use_suffix ? a.nslots[1][b] : 0;
+  // both counts read unconditionally, so the two loads overlap
+  const int np = a.nslots[0][b], ns_all = a.nslots[1][b];
+  const int ns = a.use_suffix ? ns_all : 0;
   const int U = np + ns + 1;
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (nsplit <= 1) return;
@@ -703,13 +705,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   for (int u = 0; u < kBatch; ++u)
     if (u < nsplit) v[u] = *reinterpret_cast<const float4*>(pc + u * pstride);
   if (tid < kSlot) {
+    // The maxima and sums of kBatch splits are loaded together (indices
+    // clamped, values masked), so each batch costs one memory latency.
     float mstar = -__builtin_inff();
-    for (int sp = 0; sp < nsplit; ++sp) mstar = fmaxf(mstar, p0[sp * pstride + D * kSlot + tid]);
+    for (int sp0 = 0; sp0 < nsplit; sp0 += kBatch) {
+      float mv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) mv[u] = p0[min(sp0 + u, nsplit - 1) * pstride + D * kSlot + tid];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) mstar = fmaxf(mstar, mv[u]);   // clamped repeats change no maximum
+    }
     float l = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float w = __builtin_amdgcn_exp2f(p0[sp * pstride + D * kSlot + tid] - mstar);
-      l = fmaf(p0[sp * pstride + (D + 1) * kSlot + tid], w, l);
-      w_lds[sp][tid] = w;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += kBatch) {
+      float mv[kBatch], lv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float* pm = p0 + min(sp0 + u, nsplit - 1) * pstride + D * kSlot + tid;
+        mv[u] = pm[0];
+        lv[u] = pm[kSlot];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (sp0 + u < nsplit) {
+          const float w = __builtin_amdgcn_exp2f(mv[u] - mstar);
+          l = fmaf(lv[u], w, l);
+          w_lds[sp0 + u][tid] = w;
+        }
+      }
     }
     const float inv = 1.0f / l;
     for (int sp = 0; sp < nsplit; ++sp) w_lds[sp][tid] *= inv;
