@@ -160,13 +160,49 @@ def main():
 
     max_prefix = int(w.lengths.max())
     prot_cap = max(len(p) for p in w.prot_prefix) + c.step_protect * commits_per_layer + 8
+    sprot_cap = max([len(p) for p in (w.prot_suffix or [])] + [0]) + 8
     caches = []
     for _ in range(L):
-        cache = kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
-                            prefix_tokens=max_prefix + 32 * (commits_per_layer + 1),
-                            prefix_protected=prot_cap, max_q_heads=c.Hq)
-        cache.commit(kp, vp, ntok=w.lengths, protected=w.prot_prefix if c.prot_frac else None)
-        caches.append(cache)
+        caches.append(kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
+                                  prefix_tokens=max_prefix + 32 * (commits_per_layer + 1),
+                                  suffix_tokens=c.suffix, prefix_protected=prot_cap,
+                                  suffix_protected=sprot_cap if c.suffix else 0, max_q_heads=c.Hq))
+    torch.cuda.synchronize()
+    # Prefill: one commit of the whole prefix into each layer cache, through
+    # prebuilt C-ABI arguments.  After an untimed first round (a handle's first
+    # device call also sets up its host-side ring and events), every layer's
+    # prefix is committed again with the segment reset, timed with events
+    # around all L commits.
+    stream0 = torch.cuda.current_stream()
+    s0 = ctypes.c_void_p(stream0.cuda_stream)
+    dt0 = kvq.KVQ_BF16 if c.dtype == "bf16" else kvq.KVQ_F32
+    h_ntok = (ctypes.c_int32 * c.B)(*[int(n) for n in w.lengths])
+    if c.prot_frac:
+        offs = np.concatenate([[0], np.cumsum([len(p) for p in w.prot_prefix])]).astype(np.int32)
+        h_off = (ctypes.c_int32 * (c.B + 1))(*[int(x) for x in offs])
+        h_idx = (ctypes.c_int32 * max(int(offs[-1]), 1))(*[int(x) for p in w.prot_prefix for x in p])
+    else:
+        h_off = h_idx = None
+    n_max = int(kp.shape[1])
+
+    def prefill(cache, reset):
+        kvq.check(kvq.lib.kvq_commit(cache.handle, 0, reset, ctypes.c_void_p(kp.data_ptr()),
+                                     ctypes.c_void_p(vp.data_ptr()), dt0, n_max, h_ntok, h_off, h_idx, s0))
+    for cache in caches:
+        prefill(cache, 0)
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream0)
+    for cache in caches:
+        prefill(cache, 1)
+    p1.record(stream0)
+    torch.cuda.synchronize()
+    prefill_ms = p0.elapsed_time(p1) / L
+    if c.suffix:
+        ks, vs = to(w.k_suffix), to(w.v_suffix)
+        for cache in caches:
+            cache.commit(ks, vs, protected=w.prot_suffix if c.prot_frac else None, segment=kvq.KVQ_SUFFIX)
+        del ks, vs
     del kp, vp
     torch.cuda.synchronize()
     R = caches[0].layout["record_bytes"]
@@ -196,14 +232,16 @@ def main():
 
     def do_attn(i):
         qp, kbp, vbp, op = attn_args
-        kvq.check(lib.kvq_block_attn(caches[i % L].handle, 0, qp, c.Hq, dtc, kbp, vbp, dtc, 32, scale,
-                                     op, kvq.KVQ_BF16, sptr))
+        kvq.check(lib.kvq_block_attn(caches[i % L].handle, 1 if c.suffix else 0, qp, c.Hq, dtc, kbp, vbp, dtc,
+                                     32, scale, op, kvq.KVQ_BF16, sptr))
 
     def attn_counts(layer):
         """Algorithmic bytes/flops of one attention call on a layer's cache as it stands."""
-        ntok = [int(n) + 32 * commits[layer] for n in w.lengths]
-        nslots = [-(-int(n) // 32) + commits[layer] for n in w.lengths]
+        ntok = [int(n) + 32 * commits[layer] + c.suffix for n in w.lengths]
+        nslots = [-(-int(n) // 32) + commits[layer] + -(-c.suffix // 32) for n in w.lengths]
         nprot = [len(p) + c.step_protect * commits[layer] for p in w.prot_prefix]
+        if c.suffix and c.prot_frac:
+            nprot = [n + len(p) for n, p in zip(nprot, w.prot_suffix)]
         return attn_algorithmic(c, ntok, nslots, nprot, R)
 
     def timed(fn, n, first):
@@ -246,6 +284,16 @@ def main():
     qtok = c.B * 32
     attn_s = attn_ms * 1e-3
     achieved_tflops = a_flops / attn_s / 1e12
+    achieved_gbs = a_bytes / attn_s / 1e9
+    # the roofline that binds at this workload: MFMA time against HBM time of
+    # the algorithmic flops and bytes
+    if a_flops / (PEAK_F16_TFLOPS * 1e12) >= a_bytes / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved_tflops / PEAK_F16_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS}
+    prefill_bytes = commit_algorithmic(c, [int(n) for n in w.lengths], sum(len(p) for p in w.prot_prefix), R)
     res = {
         "metric": "block-attn query-tokens/s + achieved HBM GB/s, 4-bit KV, Dream-7B shape",
         "value": qtok / (ms_per_step * 1e-3),
@@ -266,16 +314,18 @@ def main():
         "attn_ms": attn_ms,
         "commit_ms": commit_ms,
         "attn_query_tokens_per_s": qtok / attn_s,
-        "attn_hbm_gbs": a_bytes / attn_s / 1e9,
+        "attn_hbm_gbs": achieved_gbs,
         "attn_tflops": achieved_tflops,
         "commit_tokens_per_s": c.B * 32 / (commit_ms * 1e-3),
         "commit_gbs": commit_bytes / (commit_ms * 1e-3) / 1e9,
+        "prefill_commit_ms": prefill_ms,
+        "prefill_commit_tokens_per_s": float(np.sum(w.lengths)) / (prefill_ms * 1e-3),
+        "prefill_commit_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
+        "prefill_commit_hbm_frac": prefill_bytes / (prefill_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
-        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_F16_TFLOPS,
-                     "traffic": measured_traffic(c.name),
+        "roofline": {**roof, "traffic": measured_traffic(c.name),
                      "kernel": "attention launch (attn_kernel + combine_kernel)",
-                     "hbm_frac": a_bytes / attn_s / 1e9 / PEAK_HBM_GBS},
+                     "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(c, w, blocks, args.cpu_budget)

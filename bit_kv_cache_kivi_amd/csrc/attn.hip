@@ -81,7 +81,14 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   __shared__ __align__(16) half8 vop[3][CT][2][64];          // [buffer][channel tile][k-half][lane]
   __shared__ __align__(16) int4 hdr[kMaxUnits];
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  int split_i, kvh_i, b_i;
+  if (a.num_wg) {
+    const uint32_t e = a.wg[blockIdx.x];
+    split_i = e & 0xff; kvh_i = (e >> 8) & 0xff; b_i = e >> 16;
+  } else {
+    split_i = blockIdx.x; kvh_i = blockIdx.y; b_i = blockIdx.z;
+  }
+  const int split = split_i, kvh = kvh_i, b = b_i;
   // Kernel-argument fields as locals: lambdas below capture these, never the
   // argument struct itself (capturing it by reference would copy the whole
   // struct to scratch memory).
@@ -774,7 +781,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
 
 template <int KB, int VB, int D>
 hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
-  dim3 grid(grid_splits, a.hkv, B);
+  const dim3 grid = a.num_wg ? dim3(a.num_wg) : dim3(grid_splits, a.hkv, B);
   const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
   if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4>), grid, block, 0, s, a);
   else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8>), grid, block, 0, s, a);

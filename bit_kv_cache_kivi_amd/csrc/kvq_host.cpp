@@ -82,10 +82,6 @@ void compute_layout(const kvq_config* c, kvq_layout* L) {
     L->prot_rows_offset[s] = off; off += align256(B * pcap * H * D * 2);
     L->prot_pos_offset[s] = off;  off += align256(B * pcap * 4);
   }
-  const uint64_t maxcap = c->prefix_slots > c->suffix_slots ? c->prefix_slots : c->suffix_slots;
-  L->staging_offset = off;
-  L->staging_bytes = align256(B * maxcap * sizeof(CommitTask));
-  off += 2 * L->staging_bytes;
   const uint64_t splits = c->max_splits ? c->max_splits : 32;
   const uint64_t rmax = c->max_q_heads / c->num_kv_heads;
   L->workspace_offset = off;
@@ -106,9 +102,13 @@ struct kvq_cache {
   uint8_t* dbuf;
   SegMirror seg[2];
   int32_t split_slots = 0;
-  // pinned staging ring (created on first device use)
+  // Ring of two task tables in pinned host memory (created on first device
+  // use): a large commit's kernel reads its table straight from host memory,
+  // so no copy operation sits on the stream ahead of the kernel.  ev[k] marks
+  // the end of the last kernel that read table k.
   bool hip_ready = false;
   uint8_t* h_stage = nullptr;
+  size_t task_bytes = 0;           // one table: B * max(slot capacity) tasks
   hipEvent_t ev[2] = {nullptr, nullptr};
   bool ev_used[2] = {false, false};
   int next_stage = 0;
@@ -120,7 +120,9 @@ namespace {
 
 kvq_status ensure_hip(kvq_cache* c) {
   if (c->hip_ready) return KVQ_OK;
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), 2 * c->lay.staging_bytes, hipHostMallocDefault);
+  const size_t maxcap = std::max(c->cfg.prefix_slots, c->cfg.suffix_slots);
+  c->task_bytes = ((size_t)c->cfg.batch * maxcap * sizeof(CommitTask) + 255) & ~(size_t)255;
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), 2 * c->task_bytes, hipHostMallocDefault);
   if (e != hipSuccess) { c->h_stage = nullptr; return fail(KVQ_EHIP, "hipHostMalloc: %s", hipGetErrorString(e)); }
   for (int i = 0; i < 2; ++i) {
     e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
@@ -334,18 +336,10 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
         e = hipEventSynchronize(c->ev[k]);
         if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
       }
-      const size_t bytes = tasks.size() * sizeof(CommitTask);
-      uint8_t* hs = c->h_stage + k * c->lay.staging_bytes;
-      uint8_t* ds = c->dbuf + c->lay.staging_offset + k * c->lay.staging_bytes;
-      memcpy(hs, tasks.data(), bytes);
-      e = hipMemcpyAsync(ds, hs, bytes, hipMemcpyHostToDevice, st);
-      if (e != hipSuccess) return fail(KVQ_EHIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-      e = hipEventRecord(c->ev[k], st);
-      if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-      c->ev_used[k] = true;
-      c->next_stage = k ^ 1;
+      uint8_t* hs = c->h_stage + k * c->task_bytes;
+      memcpy(hs, tasks.data(), tasks.size() * sizeof(CommitTask));
       a.use_inline = 0;
-      a.tasks = reinterpret_cast<const CommitTask*>(ds);
+      a.tasks = reinterpret_cast<const CommitTask*>(hs);   // device-accessible pinned memory
     }
     a.k = d_k;
     a.v = d_v;
@@ -357,6 +351,13 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     a.record_bytes = (uint32_t)c->lay.record_bytes;
     e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st);
     if (e != hipSuccess) return fail(KVQ_EHIP, "commit launch: %s", hipGetErrorString(e));
+    if (!a.use_inline) {
+      const int k = c->next_stage;
+      e = hipEventRecord(c->ev[k], st);
+      if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+      c->ev_used[k] = true;
+      c->next_stage = k ^ 1;
+    }
   }
 
   // ---- host mirror
@@ -406,11 +407,31 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
   if (c->split_slots > 0) {
     split_units = c->split_slots;
   } else {
-    // one workgroup per compute unit over the whole grid: the kernel holds one
-    // workgroup per CU, and fewer splits mean fewer partials to merge
-    const int64_t target = c->num_cus;
-    const int64_t pairs_units = total_units * H;
-    split_units = (int)std::max<int64_t>(8, (pairs_units + target - 1) / target);
+    // The kernel holds one workgroup per compute unit, so the grid should fit
+    // in one round: the smallest split length (at least 8 units) whose
+    // workgroups, summed over every (sequence, kv head) pair, do not exceed
+    // the CU count.  Ragged batches need this count per sequence: a length
+    // from the total alone leaves a second, mostly idle round.  When even one
+    // split per pair exceeds the CUs, split the total evenly instead.
+    std::vector<int> units(B);
+    for (int b = 0; b < B; ++b)
+      units[b] = c->seg[0].nslots[b] + (use_suffix ? c->seg[1].nslots[b] : 0) + 1;
+    auto groups = [&](int su) {
+      int64_t n = 0;
+      for (int b = 0; b < B; ++b) n += (units[b] + su - 1) / su;
+      return n * H;
+    };
+    const int64_t cus = c->num_cus;
+    if (groups(std::max(max_units, 8)) > cus) {
+      split_units = (int)std::max<int64_t>(8, (total_units * H + cus - 1) / cus);
+    } else {
+      int lo = 8, hi = std::max(max_units, 8);      // groups(hi) <= cus; find the smallest such length
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (groups(mid) <= cus) hi = mid; else lo = mid + 1;
+      }
+      split_units = lo;
+    }
   }
   split_units = std::max(split_units, (max_units + max_splits - 1) / max_splits);
   split_units = std::min(split_units, kMaxSplitUnits);
@@ -438,6 +459,28 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
   a.split_units = split_units;
   a.max_splits = max_splits;
   a.use_suffix = use_suffix ? 1 : 0;
+  // One-dimensional grid of exactly the workgroups that hold units, when they
+  // fit the launch-argument list: with one workgroup per CU, workgroups that
+  // exit at once still take dispatch slots, and an uneven spread of the
+  // working ones over the XCDs can leave some of them for a second round.
+  {
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b) {
+      const int U = a.nslots[0][b] + a.nslots[1][b] + 1;
+      n += (int64_t)H * ((U + split_units - 1) / split_units);
+    }
+    a.num_wg = 0;
+    if (n <= kvq::kMaxWgTable && grid_splits <= 256 && H <= 256) {
+      int i = 0;
+      for (int b = 0; b < B; ++b) {
+        const int U = a.nslots[0][b] + a.nslots[1][b] + 1;
+        const int ns = (U + split_units - 1) / split_units;
+        for (int h = 0; h < H; ++h)
+          for (int sp = 0; sp < ns; ++sp) a.wg[i++] = (uint32_t)sp | ((uint32_t)h << 8) | ((uint32_t)b << 16);
+      }
+      a.num_wg = i;
+    }
+  }
   hipError_t e = kvq::launch_attention(a, grid_splits, B, cfg.head_dim, cfg.k_bits, cfg.v_bits,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "attention launch: %s", hipGetErrorString(e));

@@ -49,6 +49,8 @@ struct CommitArgs {
   CommitTask inline_tasks[kInlineTasks];
 };
 
+constexpr int kMaxWgTable = 512;  // attention workgroups listed in the launch arguments
+
 struct AttnArgs {
   const void* q;        // [B, 32, Hq, D]
   const void* k_blk;    // [B, 32, Hkv, D]
@@ -65,7 +67,14 @@ struct AttnArgs {
   int32_t max_splits;
   int32_t use_suffix;
   uint16_t nslots[2][KVQ_MAX_BATCH];   // per-sequence slot counts of both segments
+  // Workgroup list of a one-dimensional grid: entry i = split | kvh << 8 |
+  // b << 16 for workgroup i, only splits that hold units.  num_wg == 0: a
+  // (splits, Hkv, B) grid instead, whose workgroups past a sequence's splits
+  // exit at once.
+  int32_t num_wg;
+  uint32_t wg[kMaxWgTable];
 };
+static_assert(sizeof(AttnArgs) <= 4096, "attention launch arguments fit the kernel-argument segment");
 
 // Record field offsets for (D, kb, vb, G_v): see include/kvq.h.
 __host__ __device__ constexpr uint32_t kc_bytes(int D, int kb) { return kSlot * D * kb / 8; }

@@ -36,7 +36,6 @@ class KvqLayout(ctypes.Structure):
         ("records_offset", c_uint64 * 2), ("headers_offset", c_uint64 * 2),
         ("prot_rows_offset", c_uint64 * 2), ("prot_pos_offset", c_uint64 * 2),
         ("slot_cap", c_int32 * 2), ("prot_cap", c_int32 * 2),
-        ("staging_offset", c_uint64), ("staging_bytes", c_uint64),
         ("workspace_offset", c_uint64), ("workspace_bytes", c_uint64),
     ]
 

@@ -46,7 +46,8 @@
  *  - The caller owns all device memory: the cache buffer handed to kvq_create
  *    (kvq_required_bytes bytes, 256-byte aligned), inputs and outputs.  The
  *    library never allocates device memory.  It allocates a small pinned host
- *    staging ring and two events on first device use; kvq_destroy frees them.
+ *    ring of two commit task tables (read by the commit kernel directly from
+ *    host memory) and two events on first device use; kvq_destroy frees them.
  *  - Pointers named d_* are device pointers; h_* are host pointers read only
  *    during the call.  `stream` is a hipStream_t (NULL = default stream).
  *  - Calls are asynchronous and stream-ordered.  All calls on one handle must be
@@ -150,7 +151,6 @@ typedef struct {
   uint64_t prot_pos_offset[2];
   int32_t slot_cap[2];
   int32_t prot_cap[2];
-  uint64_t staging_offset, staging_bytes;     /* commit task tables (2 buffers)   */
   uint64_t workspace_offset, workspace_bytes; /* attention split-K partials       */
 } kvq_layout;
 
@@ -168,8 +168,8 @@ kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out);
  * starts empty; nothing in d_buf needs initialising. */
 kvq_status kvq_create(const kvq_config* cfg, void* d_buf, size_t buf_bytes, kvq_cache** out);
 
-/* Frees the host-side handle and its pinned staging ring.  Waits for the
- * handle's outstanding staging copies.  NULL is accepted. */
+/* Frees the host-side handle and its pinned task-table ring.  Waits for the
+ * handle's outstanding commit kernels that read the ring.  NULL is accepted. */
 kvq_status kvq_destroy(kvq_cache* c);
 
 /* Quantize-on-commit.  Appends, for every sequence b, the first h_ntok[b]

@@ -53,7 +53,7 @@ def test_layout_matches_documented_record(kvq):
                         (L["headers_offset"][s], 3 * L["slot_cap"][s] * 16),
                         (L["prot_rows_offset"][s], 3 * L["prot_cap"][s] * 2 * D * 2),
                         (L["prot_pos_offset"][s], 3 * L["prot_cap"][s] * 4)]
-        regions += [(L["staging_offset"], 2 * L["staging_bytes"]), (L["workspace_offset"], L["workspace_bytes"])]
+        regions += [(L["workspace_offset"], L["workspace_bytes"])]
         regions.sort()
         for (o1, n1), (o2, _) in zip(regions, regions[1:]):
             assert o1 % 256 == 0 and o1 + n1 <= o2
