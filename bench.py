@@ -45,9 +45,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "b21517dab616fea7fabae1a9da105537f3c58dec54a8b480581e5bbaa90ca78c",
-        "kib": {"attn_kernel": {"fetch": 33512, "write": 29120},
-                "combine_kernel": {"fetch": 14590, "write": 1792}},
+        "attn_source_sha256": "c0cb36e4261a4c16b8f5343c96b0e142d9a817fde8eac6da2b7a569c0094e32d",
+        "kib": {"attn_kernel": {"fetch": 33522, "write": 29120},
+                "combine_kernel": {"fetch": 14606, "write": 1792}},
     },
 }
 
