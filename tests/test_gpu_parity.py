@@ -179,3 +179,33 @@ def test_per_step_commit_then_attend():
         e, x = attention_error(out, ref)
         assert x <= 0, (step, e)
     compare_commit(cache, ora, 0, c.B)
+
+
+def test_many_pairs_grid_and_ragged_splits():
+    """More (sequence, kv head) workgroups than the launch-argument list holds
+    (the three-dimensional grid, whose idle splits exit at once), and a ragged
+    batch on the listed grid; both against the oracle."""
+    announce("grid shapes")
+    import dataclasses
+    g = np.random.default_rng(11)
+    D, H, r = 64, 4, 2
+    for B, lengths in [(140, None), (6, [40, 300, 700, 31, 256, 1]), (3, [0, 64, 96])]:
+        T = 96 if lengths is None else max(max(lengths), 1)
+        ntok = np.full(B, T) if lengths is None else np.array(lengths)
+        k = g.standard_normal((B, T, H, D)).astype(np.float32)
+        v = g.standard_normal((B, T, H, D)).astype(np.float32)
+        q = g.standard_normal((B, 32, H * r, D)).astype(np.float32)
+        kb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+        vb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+        cache = kvq.KVCache(B, H, D, 4, 4, 64, prefix_tokens=T + 32, max_q_heads=H * r)
+        ora = O.OracleCache(B, H, D, 4, 4, 64)
+        cache.commit(dev(k, "f32"), dev(v, "f32"), ntok=ntok)
+        ora.commit(0, k, v, ntok=ntok)
+        ref = O.block_attention(ora, q, kb, vb)
+        for split in (0, 2):
+            cache.set_split_slots(split)
+            out = cache.block_attn(dev(q, "f32"), dev(kb, "f32"), dev(vb, "f32"), out_dtype=torch.float32)
+            e, x = attention_error(out, ref)
+            print(f"B={B} split={split}: err={e:.2e}")
+            assert x <= 0, (B, split, e)
+        cache.close()
