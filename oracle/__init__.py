@@ -30,9 +30,10 @@ from .layout import (record_layout, pack_record, unpack_record, v_token_position
                      HEADER_BYTES)
 from .cache import OracleCache
 from .attention import block_attention, attention_rows
+from .rotation import rotate_f32, unrotate, rotation_matrix, hadamard
 
 __all__ = [
     "asym_quantize", "dequantize", "to_bf16_f32", "record_layout", "pack_record",
     "unpack_record", "v_token_position", "HEADER_BYTES", "OracleCache",
-    "block_attention", "attention_rows",
+    "block_attention", "attention_rows", "rotate_f32", "unrotate", "rotation_matrix", "hadamard",
 ]

@@ -13,10 +13,17 @@ dequantized values (Q-MaskAhead: attention directly from low-bit KV).
 Readings: scores are q.k times a softmax scale (1/sqrt(D) unless given); no
 causal or positional mask (keys arrive already position-encoded); grouped-query
 heads map query head hq to kv head hq // (Hq / Hkv).
+
+With a value rotation R on the cache (oracle/rotation.py; SoloQ summary page:
+values follow the rotated activation path), the cached values are R v: the
+block's own values are rotated the same way (fp32, as at commit), attention
+yields R o, and the output is R^T (R o).
 """
 from __future__ import annotations
 
 import numpy as np
+
+from .rotation import rotate_f32, unrotate
 
 
 def attention_rows(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float) -> np.ndarray:
@@ -44,6 +51,9 @@ def block_attention(cache, q: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
         scale = 1.0 / np.sqrt(D)
     out = np.full((B, L, Hq, D), np.nan)
     want = None if pairs is None else set(pairs)
+    rot = getattr(cache, "v_rot", None)
+    if rot is not None:
+        v_blk = rotate_f32(v_blk, *rot)
     for b in range(B):
         for h in range(Hkv):
             heads = [hq for hq in range(h * r, (h + 1) * r) if want is None or (b, hq) in want]
@@ -59,5 +69,6 @@ def block_attention(cache, q: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
             keys = np.concatenate(ks)
             vals = np.concatenate(vs)
             for hq in heads:
-                out[b, :, hq] = attention_rows(q[b, :, hq], keys, vals, scale)
+                o = attention_rows(q[b, :, hq], keys, vals, scale)
+                out[b, :, hq] = o if rot is None else unrotate(o, *rot)
     return out

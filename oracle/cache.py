@@ -18,7 +18,9 @@ Readings where the pages are silent (each listed in the design notes):
     take no part in their group's key statistics and get code 0; their values
     are quantized like any other token;
   * V groups are G_v consecutive channels of one token;
-  * a suffix segment is replaced wholesale when it is reset.
+  * a suffix segment is replaced wholesale when it is reset;
+  * with a value rotation set (oracle/rotation.py), every committed value row
+    is rotated before it is quantized, and the cache holds rotated values.
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ import numpy as np
 
 from .layout import SLOT, pack_record, pack_header, record_layout
 from .quant import asym_quantize, dequantize, to_bf16_f32
+from .rotation import rotate_f32
 
 
 @dataclasses.dataclass
@@ -44,8 +47,10 @@ class _SeqSeg:
 class OracleCache:
     """Host model of one layer's cache: B sequences, Hkv kv heads, head dim D."""
 
-    def __init__(self, B: int, Hkv: int, D: int, k_bits: int, v_bits: int, v_group: int):
+    def __init__(self, B: int, Hkv: int, D: int, k_bits: int, v_bits: int, v_group: int, v_rot=None):
+        """v_rot: None, or (perm, mix, block) of the K-RPBH value rotation."""
         assert D % v_group == 0
+        self.v_rot = v_rot
         self.B, self.Hkv, self.D = B, Hkv, D
         self.kb, self.vb, self.gv = k_bits, v_bits, v_group
         self.layout = record_layout(D, k_bits, v_bits, v_group) if k_bits <= 4 and v_bits <= 4 else None
@@ -59,6 +64,8 @@ class OracleCache:
         prot[b]: sorted positions (relative to this commit) of protected tokens."""
         k = np.asarray(k, dtype=np.float32)
         v = np.asarray(v, dtype=np.float32)
+        if self.v_rot is not None:
+            v = rotate_f32(v, *self.v_rot)
         B, n_max, Hkv, D = k.shape
         assert (B, Hkv, D) == (self.B, self.Hkv, self.D) and v.shape == k.shape
         if reset:

@@ -216,3 +216,17 @@ def to_csr(pos: List[np.ndarray]):
         off[i + 1] = off[i] + len(p)
     idx = np.concatenate(pos).astype(np.int32) if off[-1] else np.zeros(0, np.int32)
     return off, idx
+
+
+def krpbh_params(D: int, block: int, seed: int = 0):
+    """Random inputs of the K-RPBH value rotation: a permutation of 0..D-1 and a
+    Haar-distributed k x k orthogonal mix (k = D / block), fp32.  QR of a
+    Gaussian matrix with the signs of R's diagonal moved into Q gives the Haar
+    measure.  These are drawn here, as inputs; neither side of the comparison
+    draws them."""
+    g = np.random.default_rng([0xB07A7E, D, block, seed])
+    k = D // block
+    a = g.standard_normal((k, k))
+    q, r = np.linalg.qr(a)
+    q = q * np.sign(np.diag(r))[None, :]
+    return g.permutation(D).astype(np.int32), q.astype(np.float32)
