@@ -20,6 +20,8 @@ SOURCES = {
     # the quantizer must round exactly as written: no fused multiply-add contraction
     "commit.hip": ["-ffp-contract=off"],
     "attn.hip": [],
+    # the value rotation must round exactly as written too
+    "rotate.hip": ["-ffp-contract=off"],
     "kvq_host.cpp": [],
 }
 

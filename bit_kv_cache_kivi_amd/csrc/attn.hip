@@ -64,7 +64,15 @@ struct Shape {
   static_assert(RPT >= GPT, "the block's K rows use the record prefetch slots");
 };
 
-template <int KB, int VB, int D, int NC>
+// CEN (values stored in a rotated basis): a value is dequantized as
+// (code - cm) * scale with cm the middle code, (2^vb - 1) / 2, and the offset
+// zero + cm * scale of each (token, channel group) is summed apart in fp32,
+// weighted by the same fp16 probabilities as the PV product.  A dequantized
+// value then rounds to fp16 with an error that is odd in the code around cm,
+// instead of one shared by every channel with the same code; those shared
+// errors would line up with the constant vector that the transposed
+// Hadamard transform concentrates into one channel per block.
+template <int KB, int VB, int D, int NC, bool CEN>
 __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const AttnArgs a) {
   using S = Shape<D>;
   constexpr int KS = S::KS, CT = S::CT, GPT = S::GPT, VPT = S::VPT, RPT = S::RPT;
@@ -80,6 +88,11 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   __shared__ __align__(16) uint4 klo[2][D / 64][2][64];      // key lo tiles (bf8): [buffer][64-channel block][16-byte half][lane]
   __shared__ __align__(16) half8 vop[3][CT][2][64];          // [buffer][channel tile][k-half][lane]
   __shared__ __align__(16) int4 hdr[kMaxUnits];
+  __shared__ __align__(16) float zoff[CEN ? 3 : 1][CEN ? D / 32 : 1][kSlot];   // value offsets (CEN)
+  // CEN: per consumer lane, the sum of P times the value offsets of each
+  // channel group (kept in LDS: the consumers have no registers to spare)
+  __shared__ __align__(16) float zsum[CEN ? NC : 1][CEN ? D / 32 : 1][64];
+  constexpr float kCm = 0.5f * (float)((1 << VB) - 1);
 
   int split_i, kvh_i, b_i;
   if (a.num_wg) {
@@ -326,7 +339,16 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         store_hi_lo8(kop[kb][kks][t + 32 * khh], klo_part(kb, kcg, t), x, neg_one);
       }
       const float vsc[8] = {d.vs[0].x, d.vs[0].y, d.vs[0].z, d.vs[0].w, d.vs[1].x, d.vs[1].y, d.vs[1].z, d.vs[1].w};
-      const float vzr[8] = {d.vz[0].x, d.vz[0].y, d.vz[0].z, d.vz[0].w, d.vz[1].x, d.vz[1].y, d.vz[1].z, d.vz[1].w};
+      float vzr[8] = {d.vz[0].x, d.vz[0].y, d.vz[0].z, d.vz[0].w, d.vz[1].x, d.vz[1].y, d.vz[1].z, d.vz[1].w};
+      if constexpr (CEN) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vzr[e] = -kCm * vsc[e];
+        if (tid < (D >> gv_log2) * kSlot) {
+          const int g = tid / kSlot, t = tid % kSlot;
+          const float* vm = reinterpret_cast<const float*>(rawS + KC + VC + KM + g * 256);
+          zoff[vbuf][g][t] = fmaf(kCm, vm[t], vm[kSlot + t]);
+        }
+      }
 #pragma unroll
       for (int vi = 0; vi < VPT; ++vi) {
         const int c = vch[vi];
@@ -355,6 +377,9 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = vst[(vta + (e & 3) + 8 * (e >> 2)) * D + c];
         vop[vbuf][c >> 5][vmm][(c & 31) + 32 * vhh] = v;
+      }
+      if constexpr (CEN) {
+        if (tid < (D / 32) * kSlot) zoff[vbuf][tid / kSlot][tid % kSlot] = 0.f;   // the block is not quantized
       }
     }
   };
@@ -430,6 +455,11 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[ct][i] *= alpha;
+      if constexpr (CEN) {
+#pragma unroll
+        for (int g = 0; g < D / 32; ++g)
+          if (g < (D >> gv_log2)) zsum[ci][g][lane] *= alpha;
+      }
     }
     const float mneg = -m_ref;
     // P is rounded to fp16 for the PV product; the row sum takes the same
@@ -446,6 +476,32 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       psum = __builtin_amdgcn_fdot2(pp, ones, psum, false);
     }
     l_run = psum;
+  };
+  // CEN: zsum[g] += sum over the lane's 16 tokens of P (fp16, as in the PV
+  // product) times the offset of the token's group g; token of P entry i is
+  // 8*(i/4) + 4*(lane/32) + i%4
+  auto zacc = [&](int q, const half8 (&pop)[2]) __attribute__((always_inline)) {
+    if constexpr (CEN) {
+      const int ng = D >> gv_log2;
+#pragma unroll
+      for (int g = 0; g < D / 32; ++g) {
+        if (g < ng) {
+          const float* zp = &zoff[q % 3][g][4 * (lane >> 5)];
+          float acc = zsum[ci][g][lane];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float4 z = *reinterpret_cast<const float4*>(zp + 8 * m);
+            const half8& pp = pop[m >> 1];
+            const int i0 = (4 * m) & 7;
+            acc = fmaf((float)pp[i0], z.x, acc);
+            acc = fmaf((float)pp[i0 + 1], z.y, acc);
+            acc = fmaf((float)pp[i0 + 2], z.z, acc);
+            acc = fmaf((float)pp[i0 + 3], z.w, acc);
+          }
+          zsum[ci][g][lane] = acc;
+        }
+      }
+    }
   };
   auto pv = [&](const half8 (&va)[CT][2], const half8 (&pop)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -582,6 +638,12 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       }
     }
   }
+  if constexpr (CEN) {
+    if (ci < r) {
+#pragma unroll
+      for (int g = 0; g < D / 32; ++g) zsum[ci][g][lane] = 0.f;
+    }
+  }
   __syncthreads();
   __syncthreads();
   if (ci >= r) {
@@ -598,8 +660,16 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       // scores); a higher issue priority on the SIMD for that phase shortens it.
       __builtin_amdgcn_s_setprio(2);
       if (i >= 2 && i - 2 < NU) {
-        read_v(i - 2, 0, va);
-        softmax(nv, pop);
+        if constexpr (CEN) {
+          // the offset sums first: with the V tiles in flight as well, the
+          // wave would run out of registers
+          softmax(nv, pop);
+          zacc(i - 2, pop);
+          read_v(i - 2, 0, va);
+        } else {
+          read_v(i - 2, 0, va);
+          softmax(nv, pop);
+        }
         read_v(i - 2, 1, va);
         pv(va, pop);
       }
@@ -628,6 +698,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         const int nv = hdr[i - 1].x;
         scores(i - 1);
         softmax(nv, pop);
+        zacc(i - 1, pop);
         // first V k-half of unit i-1 for the next interval's PV, in flight
         // across the barrier
         __builtin_amdgcn_sched_barrier(0);
@@ -646,6 +717,21 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   const int hq = kvh * r + ci;
   const float l_tot = sum_halves(l_run);
   const int j = lane & 31, hh = lane >> 5;
+  if constexpr (CEN) {
+    // the offsets' contribution, common to every channel of a group
+    float zt[D / 32];
+#pragma unroll
+    for (int g = 0; g < D / 32; ++g) zt[g] = g < (D >> gv_log2) ? sum_halves(zsum[ci][g][lane]) : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int gct = (32 * ct) >> gv_log2;
+      float z = zt[0];
+#pragma unroll
+      for (int g = 1; g < D / 32; ++g) z = gct == g ? zt[g] : z;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[ct][i] += z;
+    }
+  }
   if (nsplit == 1) {
     const float inv = 1.0f / l_tot;
     const size_t row = ((size_t)b * kSlot + j) * hq_all + hq;
@@ -783,8 +869,13 @@ template <int KB, int VB, int D>
 hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
   const dim3 grid = a.num_wg ? dim3(a.num_wg) : dim3(grid_splits, a.hkv, B);
   const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
-  if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4>), grid, block, 0, s, a);
-  else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8>), grid, block, 0, s, a);
+  if (a.v_centred) {
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, true>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, true>), grid, block, 0, s, a);
+  } else {
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false>), grid, block, 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);

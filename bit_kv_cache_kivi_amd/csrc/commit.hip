@@ -42,6 +42,7 @@
 // identical to the plain definition.  This file is compiled with
 // -ffp-contract=off.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kvq_internal.h"
@@ -147,8 +148,14 @@ __device__ __forceinline__ float exact_code(float d, float scale, float lev) {
 
 constexpr float kNearHalf = 0.5f - 0x1p-17f;
 
-template <int KB, int VB, int D, bool F32IN>
-__global__ __launch_bounds__(256, F32IN ? 3 : 4) void commit_kernel(const CommitArgs a, int ntasks) {
+// x of lane (lane ^ M) within each 32-lane half (ds_swizzle, bit-mask mode)
+template <int M>
+__device__ __forceinline__ float swz_xor(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (M << 10)));
+}
+
+template <int KB, int VB, int D, bool F32IN, bool ROT>
+__global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(const CommitArgs a, int ntasks) {
   constexpr int HC = D / 2;              // channels per key wave
   constexpr int NCGK = HC / 8;           // 8-channel groups per key wave
   constexpr int NTQK = 64 / NCGK;        // key lanes along the token axis
@@ -172,6 +179,10 @@ __global__ __launch_bounds__(256, F32IN ? 3 : 4) void commit_kernel(const Commit
   __shared__ __align__(16) float kx[2][2][NCGK * TST];      // key partial min/max: [wave][min|max][cgl][channel][tq]
   __shared__ __align__(16) float krcp[D];                   // key reciprocals per channel
   __shared__ __align__(16) float vrcp[D / 32][kSlot];       // value reciprocals per (group, token)
+  // rotation only: the value rows of each value wave, the permutation and the mix
+  __shared__ __align__(16) float vrow[2][ROT ? kSlot / 2 : 1][ROT ? D : 4];
+  __shared__ __align__(16) int32_t rperm[ROT ? D : 4];
+  __shared__ __align__(16) float rmix[ROT ? 64 : 4];
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -194,6 +205,12 @@ __global__ __launch_bounds__(256, F32IN ? 3 : 4) void commit_kernel(const Commit
   for (uint32_t off = raw_end + tid * 4; off < rbytes; off += 256 * 4) {
     *reinterpret_cast<uint32_t*>(recbuf[0] + off) = 0u;
     *reinterpret_cast<uint32_t*>(recbuf[1] + off) = 0u;
+  }
+
+  if constexpr (ROT) {
+    for (int e = tid; e < D; e += 256) rperm[e] = a.rot.perm[e];
+    for (int e = tid; e < 64; e += 256) rmix[e] = a.rot.mix[e];
+    __syncthreads();
   }
 
   // Task descriptors are read with scalar loads (the kernel-argument copy, or
@@ -366,9 +383,110 @@ __global__ __launch_bounds__(256, F32IN ? 3 : 4) void commit_kernel(const Commit
     }
   };
 
+  // ================= values: K-RPBH rotation of the lane's rows (SoloQ summary
+  // page, rotation paragraphs), in the fp32 order
+  //   y = x[perm]; Hadamard stages h = 1, 2, ..., b/2, each pair (i, i + h)
+  //   with i & h == 0 becoming (y_i + y_{i+h}, y_i - y_{i+h}); y <- y / sqrt(b);
+  //   z[i*b + j] = sum over l = 0..k-1 in order of mix[i][l] * y[l*b + j]
+  // (products rounded, then added: no contraction in this file).  A lane holds
+  // positions 8*cg .. 8*cg + 7 of its rows; stages h < 8 stay in the lane,
+  // stages h >= 8 pair it with the lane whose cg differs in bit h / 8 (the
+  // lanes of one row are consecutive), and the mix reads the rows back from LDS.
+  auto rotate_values = [&](float (&x)[TPL][8]) __attribute__((always_inline)) {
+    float* rows = &vrow[wave - 2][0][0];
+    const int lr0 = tq * TPLV;
+    const int block = a.rot.block, nb = D / block;
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k) {
+      float4* p = reinterpret_cast<float4*>(rows + (lr0 + k) * D + 8 * cg);
+      p[0] = make_float4(x[k][0], x[k][1], x[k][2], x[k][3]);
+      p[1] = make_float4(x[k][4], x[k][5], x[k][6], x[k][7]);
+    }
+    wave_lds_sync();
+    int pm[8];
+    {
+      const int4 q0 = *reinterpret_cast<const int4*>(rperm + 8 * cg);
+      const int4 q1 = *reinterpret_cast<const int4*>(rperm + 8 * cg + 4);
+      pm[0] = q0.x; pm[1] = q0.y; pm[2] = q0.z; pm[3] = q0.w;
+      pm[4] = q1.x; pm[5] = q1.y; pm[6] = q1.z; pm[7] = q1.w;
+    }
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[k][c] = rows[(lr0 + k) * D + pm[c]];
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+      for (int k = 0; k < TPLV; ++k)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if ((c & h) == 0) {
+            const float u = x[k][c], w = x[k][c + h];
+            x[k][c] = u + w;
+            x[k][c + h] = u - w;
+          }
+    auto cross = [&](auto m) __attribute__((always_inline)) {
+      constexpr int M = decltype(m)::value;
+      const bool upper = (cg & M) != 0;
+#pragma unroll
+      for (int k = 0; k < TPLV; ++k)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float o = swz_xor<M>(x[k][c]);
+          x[k][c] = upper ? o - x[k][c] : x[k][c] + o;
+        }
+    };
+    cross(std::integral_constant<int, 1>());
+    if (block == 64) {
+      cross(std::integral_constant<int, 2>());
+      cross(std::integral_constant<int, 4>());
+    }
+    const float inv_sqrt_b = block == 16 ? 0.25f : 0.125f;
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[k][c] = x[k][c] * inv_sqrt_b;
+    if (nb == 1) {
+      const float m0 = rmix[0];
+#pragma unroll
+      for (int k = 0; k < TPLV; ++k)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[k][c] = m0 * x[k][c];
+      return;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k) {
+      float4* p = reinterpret_cast<float4*>(rows + (lr0 + k) * D + 8 * cg);
+      p[0] = make_float4(x[k][0], x[k][1], x[k][2], x[k][3]);
+      p[1] = make_float4(x[k][4], x[k][5], x[k][6], x[k][7]);
+    }
+    wave_lds_sync();
+    const int bi = (8 * cg) / block;               // the lane's block
+    const int col = (8 * cg) % block;              // its first position inside the block
+    const float* mrow = rmix + bi * nb;
+#pragma unroll
+    for (int k = 0; k < TPLV; ++k) {
+      const float* rw = rows + (lr0 + k) * D + col;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int l = 0; l < nb; ++l) {
+        const float4 y0 = *reinterpret_cast<const float4*>(rw + l * block);
+        const float4 y1 = *reinterpret_cast<const float4*>(rw + l * block + 4);
+        const float ml = mrow[l];
+        const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = l == 0 ? ml * y[c] : acc[c] + ml * y[c];
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[k][c] = acc[c];
+    }
+  };
+
   // ================= values: tokens [16*(wave-2), +16), groups along G_v channels
   auto process_values = [&](const CommitTask& task, float (&x)[TPL][8], uint8_t* rec) __attribute__((always_inline)) {
     constexpr float LEV = (float)((1 << VB) - 1);
+    if constexpr (ROT) rotate_values(x);
     const int lpg = (1 << a.gv_log2) / 8;     // lanes per value group (4, 8 or 16)
     float mn[TPLV], mx[TPLV];
 #pragma unroll
@@ -552,23 +670,26 @@ __global__ __launch_bounds__(256, F32IN ? 3 : 4) void commit_kernel(const Commit
 // Persistent grid: as many workgroups as the device holds at once (the
 // kernel's occupancy per CU times the CU count), spread over the kv heads;
 // each workgroup loops over its share of the slots.
-template <int KB, int VB, int D, bool F32IN>
+template <int KB, int VB, int D, bool F32IN, bool ROT>
 hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s) {
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN>, 256, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN, ROT>, 256, 0) != hipSuccess ||
+        n < 1)
       n = 1;
     return n;
   }();
   const int per_head = std::max(1, per_cu * a.num_cus / std::max(1, a.hkv));
   dim3 grid(std::min(ntasks, per_head), a.hkv);
-  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN>), grid, dim3(256), 0, s, a, ntasks);
+  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT>), grid, dim3(256), 0, s, a, ntasks);
   return hipGetLastError();
 }
 
 template <int KB, int VB, int D>
 hipError_t launch_d(const CommitArgs& a, int ntasks, bool f32, hipStream_t s) {
-  return f32 ? launch_t<KB, VB, D, true>(a, ntasks, s) : launch_t<KB, VB, D, false>(a, ntasks, s);
+  if (a.rot.block != 0)
+    return f32 ? launch_t<KB, VB, D, true, true>(a, ntasks, s) : launch_t<KB, VB, D, false, true>(a, ntasks, s);
+  return f32 ? launch_t<KB, VB, D, true, false>(a, ntasks, s) : launch_t<KB, VB, D, false, false>(a, ntasks, s);
 }
 
 template <int KB, int VB>

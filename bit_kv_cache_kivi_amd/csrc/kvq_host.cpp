@@ -59,6 +59,10 @@ kvq_status check_config(const kvq_config* c) {
   if (c->max_q_heads / c->num_kv_heads > 8)
     return fail(KVQ_EUNSUPPORTED, "query heads per kv head %d (supported: <= 8)", c->max_q_heads / c->num_kv_heads);
   if (c->max_splits < 0 || c->max_splits > 256) return fail(KVQ_EINVAL, "max_splits %d outside 0..256", c->max_splits);
+  if (c->v_rotation_block != 0 && c->v_rotation_block != 16 && c->v_rotation_block != 64)
+    return fail(KVQ_EUNSUPPORTED, "v_rotation_block %d (supported: 0, 16, 64)", c->v_rotation_block);
+  if (c->v_rotation_block > c->head_dim)
+    return fail(KVQ_EUNSUPPORTED, "v_rotation_block %d exceeds head_dim %d", c->v_rotation_block, c->head_dim);
   return KVQ_OK;
 }
 
@@ -87,6 +91,11 @@ void compute_layout(const kvq_config* c, kvq_layout* L) {
   L->workspace_offset = off;
   L->workspace_bytes = align256(B * H * splits * rmax * (D + 2) * kvq::kSlot * 4);
   off += L->workspace_bytes;
+  L->rotation_offset = off;
+  L->rotation_bytes = c->v_rotation_block
+                          ? align256(2 * B * kvq::kSlot * H * D * 4) + align256(B * kvq::kSlot * (uint64_t)c->max_q_heads * D * 4)
+                          : 0;
+  off += L->rotation_bytes;
   L->total_bytes = off;
 }
 
@@ -114,6 +123,7 @@ struct kvq_cache {
   int next_stage = 0;
   int num_cus = 0;                 // compute units of the device (sizes the attention grid)
   std::vector<CommitTask> tasks;
+  kvq::RotParams rot{};            // value rotation (rot.block == 0 until set)
 };
 
 namespace {
@@ -234,6 +244,37 @@ kvq_status kvq_segment_info(const kvq_cache* c, int32_t segment, int32_t* h_ntok
   return KVQ_OK;
 }
 
+kvq_status kvq_set_v_rotation(kvq_cache* c, const int32_t* h_perm, const float* h_mix) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  const int b = c->cfg.v_rotation_block, D = c->cfg.head_dim;
+  if (b == 0) return fail(KVQ_EINVAL, "cache was created without value rotation (v_rotation_block = 0)");
+  if (!h_perm || !h_mix) return fail(KVQ_EINVAL, "permutation and mix must be non-NULL");
+  for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < c->cfg.batch; ++i)
+      if (c->seg[s].nslots[i] != 0) return fail(KVQ_EINVAL, "the rotation can only change while both segments are empty");
+  std::vector<int> seen(D, 0);
+  for (int e = 0; e < D; ++e) {
+    const int p = h_perm[e];
+    if (p < 0 || p >= D || seen[p]) return fail(KVQ_EINVAL, "h_perm is not a permutation of 0..%d", D - 1);
+    seen[p] = 1;
+  }
+  const int k = D / b;
+  for (int i = 0; i < k * k; ++i)
+    if (!std::isfinite(h_mix[i])) return fail(KVQ_EINVAL, "h_mix has a non-finite entry");
+  for (int i = 0; i < k; ++i)
+    for (int j = 0; j < k; ++j) {
+      double g = 0.0;
+      for (int l = 0; l < k; ++l) g += (double)h_mix[l * k + i] * h_mix[l * k + j];
+      if (std::fabs(g - (i == j ? 1.0 : 0.0)) > 1e-4) return fail(KVQ_EINVAL, "h_mix is not orthogonal");
+    }
+  kvq::RotParams r{};
+  r.block = b;
+  for (int e = 0; e < D; ++e) r.perm[e] = h_perm[e];
+  for (int i = 0; i < k * k; ++i) r.mix[i] = h_mix[i];
+  c->rot = r;
+  return KVQ_OK;
+}
+
 kvq_status kvq_set_split_slots(kvq_cache* c, int32_t slots_per_split) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   if (slots_per_split < 0) return fail(KVQ_EINVAL, "slots_per_split %d", slots_per_split);
@@ -251,6 +292,7 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
   if (segment == KVQ_SUFFIX && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
   if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return fail(KVQ_EINVAL, "in_dtype %d", in_dtype);
   if (n_max < 0) return fail(KVQ_EINVAL, "n_max %d", n_max);
+  if (cfg.v_rotation_block != 0 && c->rot.block == 0) return fail(KVQ_EINVAL, "value rotation is not set");
   if (h_prot_idx && !h_prot_off) return fail(KVQ_EINVAL, "protected index list given without offsets");
   std::vector<int32_t> ntok(B);
   int64_t total = 0;
@@ -344,6 +386,7 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     a.k = d_k;
     a.v = d_v;
     a.num_cus = c->num_cus;
+    a.rot = c->rot;
     a.seg = seg_ptrs(c, segment);
     a.n_max = n_max;
     a.hkv = cfg.num_kv_heads;
@@ -387,6 +430,7 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
   if (!aligned16(d_q) || !aligned16(d_k_blk) || !aligned16(d_v_blk) || !aligned16(d_out))
     return fail(KVQ_EINVAL, "q, k_blk, v_blk and out must be 16-byte aligned");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
+  if (cfg.v_rotation_block != 0 && c->rot.block == 0) return fail(KVQ_EINVAL, "value rotation is not set");
 
   const int max_splits = cfg.max_splits ? cfg.max_splits : 32;
   int max_units = 0;
@@ -481,9 +525,47 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
       a.num_wg = i;
     }
   }
-  hipError_t e = kvq::launch_attention(a, grid_splits, B, cfg.head_dim, cfg.k_bits, cfg.v_bits,
-                                       static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int D = cfg.head_dim;
+  float* rot_o = nullptr;
+  if (c->rot.block != 0) {
+    // rotated values: the block's values join the cache's basis (keys are
+    // converted alongside, so that both block operands are fp32), attention
+    // writes R o in fp32, and the transposed rotation gives o
+    float* ws = reinterpret_cast<float*>(c->dbuf + c->lay.rotation_offset);
+    const size_t blk = (size_t)B * kvq::kSlot * H * D;
+    kvq::BlkPrepArgs p;
+    memset(&p, 0, sizeof(p));
+    p.k = d_k_blk;
+    p.v = d_v_blk;
+    p.k_out = ws;
+    p.v_out = ws + blk;
+    p.rows = (int64_t)B * kvq::kSlot * H;
+    p.in_f32 = blk_dtype == KVQ_F32;
+    p.rot = c->rot;
+    hipError_t e = kvq::launch_blk_prep(p, D, st);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "block rotation launch: %s", hipGetErrorString(e));
+    rot_o = reinterpret_cast<float*>(c->dbuf + c->lay.rotation_offset + align256(2 * blk * 4));
+    a.k_blk = p.k_out;
+    a.v_blk = p.v_out;
+    a.blk_f32 = 1;
+    a.v_centred = 1;
+    a.out = rot_o;
+    a.out_f32 = 1;
+  }
+  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st);
   if (e != hipSuccess) return fail(KVQ_EHIP, "attention launch: %s", hipGetErrorString(e));
+  if (rot_o) {
+    kvq::UnrotArgs u;
+    memset(&u, 0, sizeof(u));
+    u.src = rot_o;
+    u.out = d_out;
+    u.rows = (int64_t)B * kvq::kSlot * num_q_heads;
+    u.out_f32 = out_dtype == KVQ_F32;
+    u.rot = c->rot;
+    e = kvq::launch_unrotate(u, D, st);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "output rotation launch: %s", hipGetErrorString(e));
+  }
   return KVQ_OK;
 }
 

@@ -35,6 +35,15 @@ struct SegPtrs {
 
 constexpr int kInlineTasks = 64;  // commits with at most this many new slots pass their tasks by value
 
+// K-RPBH value rotation: permutation of the D channels, Hadamard transform on
+// blocks of `block` channels, k x k mix (k = D / block, row-major) across the
+// blocks.  block == 0: no rotation.
+struct RotParams {
+  int32_t block;
+  int32_t perm[128];
+  float mix[64];
+};
+
 struct CommitArgs {
   const void* k;        // [B, n_max, Hkv, D]
   const void* v;
@@ -46,8 +55,10 @@ struct CommitArgs {
   uint32_t record_bytes;
   int32_t use_inline;
   int32_t num_cus;          // compute units of the device (sizes the persistent grid)
+  RotParams rot;            // values are rotated before quantization when rot.block != 0
   CommitTask inline_tasks[kInlineTasks];
 };
+static_assert(sizeof(CommitArgs) <= 4096, "commit launch arguments fit the kernel-argument segment");
 
 constexpr int kMaxWgTable = 512;  // attention workgroups listed in the launch arguments
 
@@ -66,6 +77,7 @@ struct AttnArgs {
   int32_t split_units;  // units (slots + block) per split
   int32_t max_splits;
   int32_t use_suffix;
+  int32_t v_centred;    // values in a rotated basis: dequantized around the middle code
   uint16_t nslots[2][KVQ_MAX_BATCH];   // per-sequence slot counts of both segments
   // Workgroup list of a one-dimensional grid: entry i = split | kvh << 8 |
   // b << 16 for workgroup i, only splits that hold units.  num_wg == 0: a
@@ -75,6 +87,28 @@ struct AttnArgs {
   uint32_t wg[kMaxWgTable];
 };
 static_assert(sizeof(AttnArgs) <= 4096, "attention launch arguments fit the kernel-argument segment");
+
+// The current block's keys converted to fp32 and its values rotated, rows
+// [B * 32 * Hkv] of D (the attention then sees the rotated value basis).
+struct BlkPrepArgs {
+  const void* k;
+  const void* v;
+  float* k_out;
+  float* v_out;
+  int64_t rows;
+  int32_t in_f32;
+  RotParams rot;
+};
+
+// Transposed rotation of attention output rows [B * 32 * Hq] of D (fp32) into
+// the caller's output.
+struct UnrotArgs {
+  const float* src;
+  void* out;
+  int64_t rows;
+  int32_t out_f32;
+  RotParams rot;
+};
 
 // Record field offsets for (D, kb, vb, G_v): see include/kvq.h.
 __host__ __device__ constexpr uint32_t kc_bytes(int D, int kb) { return kSlot * D * kb / 8; }
@@ -90,5 +124,7 @@ hipError_t launch_commit(const CommitArgs& a, int ntasks, int D, int kb, int vb,
                          hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
                             hipStream_t stream);
+hipError_t launch_blk_prep(const BlkPrepArgs& a, int D, hipStream_t stream);
+hipError_t launch_unrotate(const UnrotArgs& a, int D, hipStream_t stream);
 
 }  // namespace kvq

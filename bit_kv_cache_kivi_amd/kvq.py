@@ -25,7 +25,7 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "batch", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group_tokens",
         "v_group_channels", "prefix_slots", "suffix_slots", "prefix_protected",
-        "suffix_protected", "max_q_heads", "max_splits")]
+        "suffix_protected", "max_q_heads", "max_splits", "v_rotation_block")]
 
 
 class KvqLayout(ctypes.Structure):
@@ -37,6 +37,7 @@ class KvqLayout(ctypes.Structure):
         ("prot_rows_offset", c_uint64 * 2), ("prot_pos_offset", c_uint64 * 2),
         ("slot_cap", c_int32 * 2), ("prot_cap", c_int32 * 2),
         ("workspace_offset", c_uint64), ("workspace_bytes", c_uint64),
+        ("rotation_offset", c_uint64), ("rotation_bytes", c_uint64),
     ]
 
 
@@ -63,6 +64,7 @@ def _load():
                                      c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_segment_info": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_int32)]),
         "kvq_set_split_slots": (c_int32, [c_void_p, c_int32]),
+        "kvq_set_v_rotation": (c_int32, [c_void_p, P(c_int32), P(c_float)]),
         "kvq_status_str": (c_char_p, [c_int32]),
         "kvq_last_error": (c_char_p, []),
         "kvq_abi_version": (c_int32, []),
@@ -94,10 +96,11 @@ def _int_array(vals):
 
 
 def make_config(batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128, prefix_slots=1,
-                suffix_slots=0, prefix_protected=0, suffix_protected=0, max_q_heads=None, max_splits=0):
+                suffix_slots=0, prefix_protected=0, suffix_protected=0, max_q_heads=None, max_splits=0,
+                v_rotation_block=0):
     return KvqConfig(batch, num_kv_heads, head_dim, k_bits, v_bits, SLOT, v_group, prefix_slots,
                      suffix_slots, prefix_protected, suffix_protected,
-                     max_q_heads if max_q_heads is not None else num_kv_heads, max_splits)
+                     max_q_heads if max_q_heads is not None else num_kv_heads, max_splits, v_rotation_block)
 
 
 def get_layout(cfg: KvqConfig) -> dict:
@@ -130,11 +133,12 @@ class KVCache:
 
     def __init__(self, batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128,
                  prefix_tokens=32, suffix_tokens=0, prefix_protected=0, suffix_protected=0,
-                 max_q_heads=None, max_splits=0, device="cuda"):
+                 max_q_heads=None, max_splits=0, v_rotation_block=0, device="cuda"):
         import torch
         self.cfg = make_config(batch, num_kv_heads, head_dim, k_bits, v_bits, v_group,
                                -(-prefix_tokens // SLOT), -(-suffix_tokens // SLOT),
-                               prefix_protected, suffix_protected, max_q_heads, max_splits)
+                               prefix_protected, suffix_protected, max_q_heads, max_splits,
+                               v_rotation_block)
         self.layout = get_layout(self.cfg)
         nbytes = self.layout["total_bytes"]
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -204,6 +208,17 @@ class KVCache:
 
     def set_split_slots(self, n: int):
         check(lib.kvq_set_split_slots(self._h, int(n)))
+
+    def set_v_rotation(self, perm, mix):
+        """perm: D channel indices (a permutation); mix: k x k orthogonal matrix,
+        k = head_dim / v_rotation_block (any nested sequence or array)."""
+        perm = [int(x) for x in perm]
+        flat = [float(x) for row in mix for x in row]
+        D, blk = self.cfg.head_dim, self.cfg.v_rotation_block
+        k = D // blk if blk else 0
+        if len(perm) != D or len(flat) != k * k:
+            raise ValueError(f"perm needs {D} entries and mix {k}x{k} (v_rotation_block={blk})")
+        check(lib.kvq_set_v_rotation(self._h, (c_int32 * len(perm))(*perm), (c_float * len(flat))(*flat)))
 
     # ---- raw views of the buffer (for inspection and tests)
     def records(self, segment, b):

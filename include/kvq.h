@@ -111,7 +111,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
 #define KVQ_MAX_BATCH 256
 
@@ -139,6 +139,8 @@ typedef struct {
   int32_t suffix_protected;  /* >= 0                                                */
   int32_t max_q_heads;       /* largest Hq passed to kvq_block_attn (Hq % Hkv == 0) */
   int32_t max_splits;        /* split-K partial capacity per (b, kv head); 0 = 32   */
+  int32_t v_rotation_block;  /* 0 = values stored as they are; 16 or 64 = K-RPBH      */
+                             /* rotated values (see kvq_set_v_rotation), D % b == 0 */
 } kvq_config;
 
 typedef struct {
@@ -152,6 +154,10 @@ typedef struct {
   int32_t slot_cap[2];
   int32_t prot_cap[2];
   uint64_t workspace_offset, workspace_bytes; /* attention split-K partials       */
+  uint64_t rotation_offset, rotation_bytes;   /* rotated-value attention staging:
+                                                 block K and V in fp32, then the
+                                                 rotated output; 0 bytes when
+                                                 v_rotation_block == 0            */
 } kvq_layout;
 
 typedef struct kvq_cache kvq_cache;
@@ -206,6 +212,30 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix,
 /* Host mirror of a segment's lengths: any of the [B] arrays may be NULL. */
 kvq_status kvq_segment_info(const kvq_cache* c, int32_t segment,
                             int32_t* h_ntok, int32_t* h_nslots, int32_t* h_nprot);
+
+/* K-RPBH value rotation (SoloQ summary page, rotation paragraphs: a random
+ * permutation of the channels, a Hadamard transform on blocks of b consecutive
+ * channels, then a k x k random orthogonal mix of the same channel across the
+ * k = D / b blocks; block-diffusion paragraph: values follow the activation path,
+ * so they are rotated before they are quantized).  Only for a cache created with
+ * v_rotation_block = b != 0, and only while both segments are empty (before the
+ * first commit, or after both were reset); every commit and attention call of
+ * such a cache fails with KVQ_EINVAL until the rotation is set.
+ *   h_perm: host int32 [D], a permutation of 0..D-1 (rotated channel e takes
+ *           input channel h_perm[e]);
+ *   h_mix:  host fp32 [k * k], row-major, orthogonal (|M^T M - I| <= 1e-4 in every
+ *           entry), finite.
+ * Both are copied into the handle.  With the rotation set, kvq_commit quantizes
+ * R v instead of v, computed in fp32 in this order:
+ *     y = v[perm];  Hadamard stages h = 1, 2, ..., b/2: each pair (i, i + h) with
+ *     i & h == 0 becomes (y_i + y_{i+h}, y_i - y_{i+h});  y <- y / sqrt(b);
+ *     z[i*b + j] = sum over l = 0..k-1, in that order, of mix[i][l] * y[l*b + j]
+ *     (each product rounded, then added; no fused multiply-add);
+ * and kvq_block_attn rotates the block's values the same way, attends in the
+ * rotated basis and returns R^T of the result, so its output approximates the
+ * attention over the unrotated values.  The Hadamard block is normalised by
+ * 1/sqrt(b); no length correction is applied. */
+kvq_status kvq_set_v_rotation(kvq_cache* c, const int32_t* h_perm, const float* h_mix);
 
 /* Attention work split: slots per split-K chunk (0 = automatic). */
 kvq_status kvq_set_split_slots(kvq_cache* c, int32_t slots_per_split);

@@ -71,9 +71,10 @@ def attention_error(out, ref, out_dtype="f32"):
     return float(err.max()), float((err - gate).max())
 
 
-def build_case(cfg, T=None, B=None, extra_slots=4):
+def build_case(cfg, T=None, B=None, extra_slots=4, v_rot_block=0):
     """Seeded workload, a device cache and an oracle cache, both holding the
-    committed prefix (and suffix).  Shared by the GPU parity tests."""
+    committed prefix (and suffix).  Shared by the GPU parity tests.
+    v_rot_block != 0: values are stored K-RPBH rotated (blocks of that size)."""
     from bit_kv_cache_kivi_amd import kvq
     w = W.make(cfg, T=T, B=B)
     c = w.cfg
@@ -83,8 +84,13 @@ def build_case(cfg, T=None, B=None, extra_slots=4):
                         prefix_tokens=int(w.lengths.max()) + 32 * extra_slots,
                         suffix_tokens=c.suffix + (32 if c.suffix else 0),
                         prefix_protected=nprot_p, suffix_protected=nprot_s if c.suffix else 0,
-                        max_q_heads=c.Hq)
-    ora = O.OracleCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group)
+                        max_q_heads=c.Hq, v_rotation_block=v_rot_block)
+    v_rot = None
+    if v_rot_block:
+        perm, mix = W.krpbh_params(c.D, v_rot_block)
+        cache.set_v_rotation(perm, mix)
+        v_rot = (perm, mix, v_rot_block)
+    ora = O.OracleCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group, v_rot=v_rot)
     prot = w.prot_prefix if c.prot_frac > 0 else None
     cache.commit(dev(w.k_prefix, c.dtype), dev(w.v_prefix, c.dtype), ntok=w.lengths, protected=prot)
     ora.commit(0, w.k_prefix, w.v_prefix, ntok=w.lengths, prot=prot)

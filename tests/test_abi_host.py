@@ -34,14 +34,15 @@ def test_exports_every_declared_symbol(kvq):
     lib = ctypes.CDLL(SO)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
-    assert kvq.lib.kvq_abi_version() == 1
+    assert kvq.lib.kvq_abi_version() == 2
 
 
 def test_layout_matches_documented_record(kvq):
     import oracle
-    for (D, kb, vb, gv) in [(128, 4, 4, 64), (128, 2, 2, 64), (128, 4, 4, 128), (64, 4, 4, 64), (64, 2, 4, 32)]:
+    for (D, kb, vb, gv, rb) in [(128, 4, 4, 64, 0), (128, 2, 2, 64, 16), (128, 4, 4, 128, 64), (64, 4, 4, 64, 64),
+                                (64, 2, 4, 32, 0)]:
         cfg = kvq.make_config(3, 2, D, kb, vb, gv, prefix_slots=10, suffix_slots=4, prefix_protected=7,
-                              suffix_protected=3, max_q_heads=6)
+                              suffix_protected=3, max_q_heads=6, v_rotation_block=rb)
         L = kvq.get_layout(cfg)
         ref = oracle.record_layout(D, kb, vb, gv)
         for k in ("record_bytes", "kc_offset", "vc_offset", "kmeta_offset", "vmeta_offset"):
@@ -54,6 +55,11 @@ def test_layout_matches_documented_record(kvq):
                         (L["prot_rows_offset"][s], 3 * L["prot_cap"][s] * 2 * D * 2),
                         (L["prot_pos_offset"][s], 3 * L["prot_cap"][s] * 4)]
         regions += [(L["workspace_offset"], L["workspace_bytes"])]
+        # rotation staging: block K and V (fp32), then the rotated output of up to max_q_heads heads
+        assert L["rotation_bytes"] == (0 if rb == 0 else
+                                       -(-2 * 3 * 32 * 2 * D * 4 // 256) * 256 + -(-3 * 32 * 6 * D * 4 // 256) * 256)
+        if rb:
+            regions += [(L["rotation_offset"], L["rotation_bytes"])]
         regions.sort()
         for (o1, n1), (o2, _) in zip(regions, regions[1:]):
             assert o1 % 256 == 0 and o1 + n1 <= o2
@@ -64,7 +70,8 @@ def test_layout_matches_documented_record(kvq):
     ("batch", 0, 1), ("batch", 257, 1), ("head_dim", 96, 2), ("k_bits", 3, 2), ("v_bits", 8, 2),
     ("k_group_tokens", 64, 2), ("v_group_channels", 48, 2), ("v_group_channels", 256, 2),
     ("prefix_slots", 0, 1), ("suffix_slots", -1, 1), ("max_q_heads", 3, 1), ("max_q_heads", 36, 2),
-    ("max_splits", 1000, 1), ("prefix_protected", -1, 1)])
+    ("max_splits", 1000, 1), ("prefix_protected", -1, 1), ("v_rotation_block", 32, 2),
+    ("v_rotation_block", -16, 2)])
 def test_bad_configs(kvq, field, value, status):
     cfg = kvq.make_config(2, 4, 128, 4, 4, 64, prefix_slots=8, max_q_heads=8)
     setattr(cfg, field, value)
@@ -150,3 +157,28 @@ def test_status_strings(kvq):
     for s in range(5):
         assert kvq.lib.kvq_status_str(s)
     assert kvq.lib.kvq_status_str(99) == b"unknown status"
+
+
+def test_value_rotation_validation(kvq):
+    """kvq_set_v_rotation: only on a cache made for it, with a true permutation and
+    an orthogonal mix; commits and attention fail until it is set."""
+    I = lambda v: (ctypes.c_int32 * len(v))(*v)   # noqa: E731
+    F = lambda v: (ctypes.c_float * len(v))(*v)   # noqa: E731
+    p = ctypes.c_void_p(1 << 33)
+    h = _handle(kvq)                                   # no rotation configured
+    assert kvq.lib.kvq_set_v_rotation(h, I(list(range(64))), F([1.0])) == 1
+    kvq.lib.kvq_destroy(h)
+    h = _handle(kvq, v_rotation_block=16)              # D = 64: k = 4 blocks
+    assert kvq.lib.kvq_commit(h, 0, 0, p, p, 1, 32, None, None, None, None) == 1
+    assert kvq.lib.kvq_block_attn(h, 0, p, 4, 1, p, p, 1, 32, 0.125, p, 1, None) == 1
+    assert "rotation" in kvq.last_error()
+    eye = [1.0 if i == j else 0.0 for i in range(4) for j in range(4)]
+    perm = list(range(64))[::-1]
+    assert kvq.lib.kvq_set_v_rotation(h, None, F(eye)) == 1
+    assert kvq.lib.kvq_set_v_rotation(h, I([0] * 64), F(eye)) == 1                  # not a permutation
+    assert kvq.lib.kvq_set_v_rotation(h, I(perm[:63] + [64]), F(eye)) == 1          # index out of range
+    assert kvq.lib.kvq_set_v_rotation(h, I(perm), F([2.0 * x for x in eye])) == 1  # not orthogonal
+    assert kvq.lib.kvq_set_v_rotation(h, I(perm), F(eye[:-1] + [float("nan")])) == 1
+    Q = np.linalg.qr(np.random.default_rng(0).standard_normal((4, 4)))[0].astype(np.float32)
+    assert kvq.lib.kvq_set_v_rotation(h, I(perm), F(Q.reshape(-1).tolist())) == 0
+    kvq.lib.kvq_destroy(h)
