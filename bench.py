@@ -45,9 +45,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "c0cb36e4261a4c16b8f5343c96b0e142d9a817fde8eac6da2b7a569c0094e32d",
+        "attn_source_sha256": "9fb781302bfb0a55430cf0b777a4d0449430eb42292ece0e9bb151ebebc8683d",
         "kib": {"attn_kernel": {"fetch": 33522, "write": 29120},
-                "combine_kernel": {"fetch": 14606, "write": 1792}},
+                "combine_kernel": {"fetch": 14608, "write": 1792}},
     },
 }
 
@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--layers", type=int, default=28, help="per-layer caches the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--v-rotation", type=int, default=0, choices=(0, 16, 64),
+                    help="store values K-RPBH rotated with this Hadamard block (0: plain values)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a device buffer of MIB MiB five times (a reference kernel of known "
                          "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
@@ -166,7 +168,10 @@ def main():
         caches.append(kvq.KVCache(c.B, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group,
                                   prefix_tokens=max_prefix + 32 * (commits_per_layer + 1),
                                   suffix_tokens=c.suffix, prefix_protected=prot_cap,
-                                  suffix_protected=sprot_cap if c.suffix else 0, max_q_heads=c.Hq))
+                                  suffix_protected=sprot_cap if c.suffix else 0, max_q_heads=c.Hq,
+                                  v_rotation_block=args.v_rotation))
+        if args.v_rotation:
+            caches[-1].set_v_rotation(*W.krpbh_params(c.D, args.v_rotation))
     torch.cuda.synchronize()
     # Prefill: one commit of the whole prefix into each layer cache, through
     # prebuilt C-ABI arguments.  After an untimed first round (a handle's first
@@ -310,7 +315,7 @@ def main():
         "config": {"workload": c.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D,
                    "prefix_tokens": int(max_prefix), "block": 32, "k_bits": c.k_bits, "v_bits": c.v_bits,
                    "v_group": c.v_group, "protected_frac": c.prot_frac, "layers_rotated": L,
-                   "parallelism": "none"},
+                   "v_rotation_block": args.v_rotation, "parallelism": "none"},
         "attn_ms": attn_ms,
         "commit_ms": commit_ms,
         "attn_query_tokens_per_s": qtok / attn_s,
@@ -323,8 +328,9 @@ def main():
         "prefill_commit_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
         "prefill_commit_hbm_frac": prefill_bytes / (prefill_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
-        "roofline": {**roof, "traffic": measured_traffic(c.name),
-                     "kernel": "attention launch (attn_kernel + combine_kernel)",
+        "roofline": {**roof, "traffic": None if args.v_rotation else measured_traffic(c.name),
+                     "kernel": "attention launch (attn_kernel + combine_kernel" +
+                               (", with blk_prep_kernel and unrotate_kernel)" if args.v_rotation else ")"),
                      "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS},
     }
     if not args.no_cpu_baseline:
