@@ -20,6 +20,9 @@ Sources (pages, cited by title and section):
   * MaskAhead / Q-MaskAhead abstract: attention computed directly from low-bit KV.
   * Elastic-Cache abstract, observation (1): masked tokens beyond the active
     window can be cached block-wise (the suffix of the dual cache).
+  * MaskAhead abstract: mask queries of the current block rank cached entries by
+    their estimated contribution to the attention output; the block attends to
+    the top-ranked ones (oracle/selection.py).
 
 Parity status: every function here is pinned by tests against closed forms,
 invariants or brute force; the pages themselves print no worked example, so no
@@ -31,9 +34,11 @@ from .layout import (record_layout, pack_record, unpack_record, v_token_position
 from .cache import OracleCache
 from .attention import block_attention, attention_rows
 from .rotation import rotate_f32, unrotate, rotation_matrix, hadamard
+from . import selection
 
 __all__ = [
     "asym_quantize", "dequantize", "to_bf16_f32", "record_layout", "pack_record",
     "unpack_record", "v_token_position", "HEADER_BYTES", "OracleCache",
     "block_attention", "attention_rows", "rotate_f32", "unrotate", "rotation_matrix", "hadamard",
+    "selection",
 ]
