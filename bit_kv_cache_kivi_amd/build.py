@@ -22,6 +22,7 @@ SOURCES = {
     "attn.hip": [],
     # the value rotation must round exactly as written too
     "rotate.hip": ["-ffp-contract=off"],
+    "select.hip": [],
     "kvq_host.cpp": [],
 }
 

@@ -114,7 +114,12 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // both counts read unconditionally, so the two loads overlap
   const int np = a.nslots[0][b], ns_all = a.nslots[1][b];
   const int ns = a.use_suffix ? ns_all : 0;
-  const int U = np + ns + 1;                 // slots + the block itself
+  // With a selection, the units are the listed cached units (prefix slots
+  // numbered first, then suffix slots) and each carries a token mask.
+  const int32_t* const sel_units = a.sel_units;
+  const uint32_t* const sel_mask = a.sel_mask;
+  const size_t sel_base = ((size_t)b * hkv + kvh) * a.sel_ucap;
+  const int U = (a.sel_count ? a.sel_count[b * hkv + kvh] : np + ns) + 1;   // cached units + the block
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (split >= nsplit) return;
   const int u0 = split * a.split_units;
@@ -133,8 +138,6 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   const uint32_t rbytes = a.record_bytes;
   const float c2 = a.scale_log2;
 
-  auto seg_of = [&](int u) { return u < np ? 0 : 1; };
-  auto slot_of = [&](int u) { return u < np ? u : u - np; };
 
   // ---------------- prologues (run inside the role branches below): headers
   // and the block's raw rows (producers), Q operands (consumers)
@@ -197,7 +200,9 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   auto load_unit = [&](int q, Pre& pr, const int4 h) __attribute__((always_inline)) {
     const bool valid = q < nq;
     const bool blk_unit = has_block && q == nq && !blk_f32;
-    const int u = u0 + (valid ? q : 0), sg = valid ? seg_of(u) : 0;
+    // header word 0: segment << 16 | slot (the same LDS word in every lane)
+    const int hx = __builtin_amdgcn_readfirstlane(h.x);
+    const int sg = valid ? (hx >> 16) : 0;
     // (selects on values: a conditional on the captured lvalues would select
     // their addresses and keep them in scratch memory)
     const __amdgpu_buffer_rsrc_t rr =
@@ -206,7 +211,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     const __amdgpu_buffer_rsrc_t prr =
         uniform_rsrc(pick(blk_unit, (const void*)vblk_base, pick(sg, (const void*)prot_base1, (const void*)prot_base0)),
                      pick(blk_unit, blk_n, pick(sg, prot_n1, prot_n0)));
-    const int rbase = slot_of(u) * (int)rbytes;
+    const int rbase = (hx & 0xffff) * (int)rbytes;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int idx = j * NPT + tid;
@@ -427,18 +432,20 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - AHEAD), 0);
   };
-  // nvalid (valid tokens of the unit) is read from the header one phase
-  // ahead by the caller, so its LDS latency stays off the softmax path.
+  // tmask (the unit's attended tokens: valid, and selected if a selection is
+  // used) is read from the header one phase ahead by the caller, so its LDS
+  // latency stays off the softmax path.
   // softmax of the scores in sacc: P (fp16, the PV B operand) into pop; the
   // running maximum, sum and O are updated.
-  auto softmax = [&](int nvalid, half8 (&pop)[2]) __attribute__((always_inline)) {
+  auto softmax = [&](uint32_t tmask, half8 (&pop)[2]) __attribute__((always_inline)) {
     // sacc[i] = S[query lane%32][token 8*(i/4) + 4*(lane/32) + i%4]
-    if (nvalid < kSlot) {
+    if (tmask != ~0u) {
+      // the lane's tokens 4*(lane/32) + {0..3, 8..11, 16..19, 24..27}: bits at
+      // fixed positions once the mask is shifted by 4*(lane/32)
+      const uint32_t mm = tmask >> (4 * (lane >> 5));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (tok >= nvalid) sacc[i] = -__builtin_inff();
-      }
+      for (int i = 0; i < 16; ++i)
+        if (!((mm >> (8 * (i >> 2) + (i & 3))) & 1u)) sacc[i] = -__builtin_inff();
     }
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
@@ -531,13 +538,19 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // latch and force waits on in-flight loads
   const int n_int = (NU + 3) & ~1;
   if (producer) {
+      // unit headers in LDS: (segment << 16 | slot, protected mask, first
+      // protected rank, attended-token mask)
       for (int i = tid; i < nq; i += NPT) {
-        const int u = u0 + i, seg = seg_of(u);
+        const int cu = sel_units ? sel_units[sel_base + u0 + i] : u0 + i;
+        const int seg = cu < np ? 0 : 1, sl = cu < np ? cu : cu - np;
         const uint8_t* hb = seg ? seg1.headers : seg0.headers;
         const int cap = seg ? seg1.slot_cap : seg0.slot_cap;
-        hdr[i] = *reinterpret_cast<const int4*>(hb + ((size_t)b * cap + slot_of(u)) * kHeaderBytes);
+        const int4 h = *reinterpret_cast<const int4*>(hb + ((size_t)b * cap + sl) * kHeaderBytes);
+        uint32_t tm = h.x >= kSlot ? ~0u : (1u << h.x) - 1u;
+        if (sel_mask) tm &= sel_mask[sel_base + cu];
+        hdr[i] = make_int4((seg << 16) | sl, h.y, h.z, (int)tm);
       }
-      if (tid == 0 && has_block) hdr[nq] = make_int4(kSlot, 0, 0, 0);
+      if (tid == 0 && has_block) hdr[nq] = make_int4(0, 0, 0, -1);
     __syncthreads();                         // headers in LDS
     auto hdr_at = [&](int q) { return hdr[min(q, kMaxUnits - 1)]; };
     Pre pre0, pre1;
@@ -653,7 +666,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   half8 pop[2], va[CT][2];
   if (late) {
     // Interval i: softmax and PV of unit i-2, then the scores of unit i-1.
-    int nv = 0;
+    uint32_t nv = ~0u;
     for (int i = 0; i < n_int; ++i) {
       // The late consumers' softmax and PV are the longest path of an
       // interval (their V tiles and MFMAs queue behind the early consumers'
@@ -675,7 +688,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       }
       __builtin_amdgcn_s_setprio(0);
       if (i >= 1 && i - 1 < NU) {
-        nv = hdr[i - 1].x;
+        nv = (uint32_t)hdr[i - 1].w;
         scores(i - 1);
       }
       __syncthreads();
@@ -695,7 +708,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * CT, 0);
       }
       if (i >= 1 && i - 1 < NU) {
-        const int nv = hdr[i - 1].x;
+        const uint32_t nv = (uint32_t)hdr[i - 1].w;
         scores(i - 1);
         softmax(nv, pop);
         zacc(i - 1, pop);
@@ -784,10 +797,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   // both counts read unconditionally, so the two loads overlap
   const int np = a.nslots[0][b], ns_all = a.nslots[1][b];
   const int ns = a.use_suffix ? ns_all : 0;
-  const int U = np + ns + 1;
+  const int r = a.r, kvh = hq / r, hl = hq % r;
+  const int U = (a.sel_count ? a.sel_count[b * a.hkv + kvh] : np + ns) + 1;
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (nsplit <= 1) return;
-  const int r = a.r, kvh = hq / r, hl = hq % r;
   const int tid = threadIdx.x;
   const size_t pstride = (size_t)r * (D + 2) * kSlot;           // one split's partial
   const float* p0 = a.partial + ((((size_t)b * a.hkv + kvh) * a.max_splits) * r + hl) * (size_t)(D + 2) * kSlot;

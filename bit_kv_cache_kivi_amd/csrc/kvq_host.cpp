@@ -96,6 +96,13 @@ void compute_layout(const kvq_config* c, kvq_layout* L) {
                           ? align256(2 * B * kvq::kSlot * H * D * 4) + align256(B * kvq::kSlot * (uint64_t)c->max_q_heads * D * 4)
                           : 0;
   off += L->rotation_bytes;
+  // selection results: contributions per entry, token masks and unit lists
+  // per cached unit, and the list lengths
+  const uint64_t ucap = (uint64_t)c->prefix_slots + (uint64_t)c->suffix_slots;
+  L->sel_contrib_offset = off; off += align256(B * H * ucap * kvq::kSlot * 4);
+  L->sel_mask_offset = off;    off += align256(B * H * ucap * 4);
+  L->sel_units_offset = off;   off += align256(B * H * ucap * 4);
+  L->sel_count_offset = off;   off += align256(B * H * 4);
   L->total_bytes = off;
 }
 
@@ -124,6 +131,10 @@ struct kvq_cache {
   int num_cus = 0;                 // compute units of the device (sizes the attention grid)
   std::vector<CommitTask> tasks;
   kvq::RotParams rot{};            // value rotation (rot.block == 0 until set)
+  // the last selection: valid while no commit has happened since
+  uint64_t commit_gen = 0, sel_gen = 0;
+  bool sel_valid = false;
+  int sel_use_suffix = 0, sel_budget = 0;
 };
 
 namespace {
@@ -404,6 +415,7 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
   }
 
   // ---- host mirror
+  if (reset_segment || !tasks.empty()) ++c->commit_gen;
   for (int b = 0; b < B; ++b) {
     if (reset_segment) { m.ntok[b] = 0; m.nslots[b] = 0; m.nprot[b] = 0; }
     m.ntok[b] += ntok[b];
@@ -413,9 +425,13 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
   return KVQ_OK;
 }
 
-kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
-                          const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
-                          float softmax_scale, void* d_out, int32_t out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                           const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
+                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
@@ -431,17 +447,27 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
     return fail(KVQ_EINVAL, "q, k_blk, v_blk and out must be 16-byte aligned");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
   if (cfg.v_rotation_block != 0 && c->rot.block == 0) return fail(KVQ_EINVAL, "value rotation is not set");
+  if (selected) {
+    if (!c->sel_valid || c->sel_gen != c->commit_gen)
+      return fail(KVQ_EINVAL, "no selection for the cache as it stands (kvq_select after the last commit)");
+    if ((use_suffix ? 1 : 0) != c->sel_use_suffix)
+      return fail(KVQ_EINVAL, "use_suffix %d differs from the selection's", use_suffix);
+  }
 
   const int max_splits = cfg.max_splits ? cfg.max_splits : 32;
   int max_units = 0;
   int64_t total_units = 0;
   kvq::AttnArgs a;
   memset(&a, 0, sizeof(a));
+  // units per sequence: its cached slots (or, with a selection, at most the
+  // budget of them: each selected entry lies in one slot) plus the block
+  std::vector<int> ub(B);
   for (int b = 0; b < B; ++b) {
     const int np = c->seg[0].nslots[b], ns = use_suffix ? c->seg[1].nslots[b] : 0;
     a.nslots[0][b] = (uint16_t)np;
     a.nslots[1][b] = (uint16_t)(use_suffix ? ns : 0);
-    const int U = np + ns + 1;
+    const int U = (selected ? std::min(c->sel_budget, np + ns) : np + ns) + 1;
+    ub[b] = U;
     max_units = std::max(max_units, U);
     total_units += U;
   }
@@ -457,9 +483,7 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
     // the CU count.  Ragged batches need this count per sequence: a length
     // from the total alone leaves a second, mostly idle round.  When even one
     // split per pair exceeds the CUs, split the total evenly instead.
-    std::vector<int> units(B);
-    for (int b = 0; b < B; ++b)
-      units[b] = c->seg[0].nslots[b] + (use_suffix ? c->seg[1].nslots[b] : 0) + 1;
+    const std::vector<int>& units = ub;
     auto groups = [&](int su) {
       int64_t n = 0;
       for (int b = 0; b < B; ++b) n += (units[b] + su - 1) / su;
@@ -503,22 +527,24 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
   a.split_units = split_units;
   a.max_splits = max_splits;
   a.use_suffix = use_suffix ? 1 : 0;
+  if (selected) {
+    a.sel_count = reinterpret_cast<const int32_t*>(c->dbuf + c->lay.sel_count_offset);
+    a.sel_units = reinterpret_cast<const int32_t*>(c->dbuf + c->lay.sel_units_offset);
+    a.sel_mask = reinterpret_cast<const uint32_t*>(c->dbuf + c->lay.sel_mask_offset);
+    a.sel_ucap = cfg.prefix_slots + cfg.suffix_slots;
+  }
   // One-dimensional grid of exactly the workgroups that hold units, when they
   // fit the launch-argument list: with one workgroup per CU, workgroups that
   // exit at once still take dispatch slots, and an uneven spread of the
   // working ones over the XCDs can leave some of them for a second round.
   {
     int64_t n = 0;
-    for (int b = 0; b < B; ++b) {
-      const int U = a.nslots[0][b] + a.nslots[1][b] + 1;
-      n += (int64_t)H * ((U + split_units - 1) / split_units);
-    }
+    for (int b = 0; b < B; ++b) n += (int64_t)H * ((ub[b] + split_units - 1) / split_units);
     a.num_wg = 0;
     if (n <= kvq::kMaxWgTable && grid_splits <= 256 && H <= 256) {
       int i = 0;
       for (int b = 0; b < B; ++b) {
-        const int U = a.nslots[0][b] + a.nslots[1][b] + 1;
-        const int ns = (U + split_units - 1) / split_units;
+        const int ns = (ub[b] + split_units - 1) / split_units;
         for (int h = 0; h < H; ++h)
           for (int sp = 0; sp < ns; ++sp) a.wg[i++] = (uint32_t)sp | ((uint32_t)h << 8) | ((uint32_t)b << 16);
       }
@@ -566,6 +592,113 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
     e = kvq::launch_unrotate(u, D, st);
     if (e != hipSuccess) return fail(KVQ_EHIP, "output rotation launch: %s", hipGetErrorString(e));
   }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                          const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
+                          float softmax_scale, void* d_out, int32_t out_dtype, void* stream) {
+  return block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
+                         softmax_scale, d_out, out_dtype, stream, false);
+}
+
+kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
+                                   int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                                   int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,
+                                   void* stream) {
+  return block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
+                         softmax_scale, d_out, out_dtype, stream, true);
+}
+
+kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                      const void* d_k_blk, int32_t blk_dtype, int32_t block_len, float softmax_scale,
+                      const uint32_t* h_query_mask, int32_t budget, void* stream) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  const kvq_config& cfg = c->cfg;
+  const int B = cfg.batch, H = cfg.num_kv_heads;
+  if (use_suffix && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
+  if (block_len != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "block_len %d (supported: 32)", block_len);
+  if (num_q_heads < H || num_q_heads % H != 0 || num_q_heads > cfg.max_q_heads)
+    return fail(KVQ_EINVAL, "num_q_heads %d must be a multiple of %d and <= %d", num_q_heads, H, cfg.max_q_heads);
+  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (blk_dtype != KVQ_F32 && blk_dtype != KVQ_BF16))
+    return fail(KVQ_EINVAL, "dtype must be KVQ_F32 or KVQ_BF16");
+  if (!d_q || !d_k_blk) return fail(KVQ_EINVAL, "q and k_blk must be non-NULL");
+  if (!aligned16(d_q) || !aligned16(d_k_blk)) return fail(KVQ_EINVAL, "q and k_blk must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
+  if (budget < 0) return fail(KVQ_EINVAL, "budget %d", budget);
+  kvq_status hs = ensure_hip(c);
+  if (hs != KVQ_OK) return hs;
+
+  const int max_splits = cfg.max_splits ? cfg.max_splits : 32;
+  const int ucap = cfg.prefix_slots + cfg.suffix_slots;
+  kvq::SelArgs a;
+  memset(&a, 0, sizeof(a));
+  int max_nc = 0;
+  int64_t total_nc = 0;
+  for (int b = 0; b < B; ++b) {
+    const int np = c->seg[0].nslots[b], ns = use_suffix ? c->seg[1].nslots[b] : 0;
+    a.nslots[0][b] = (uint16_t)np;
+    a.nslots[1][b] = (uint16_t)ns;
+    a.qmask[b] = h_query_mask ? h_query_mask[b] : 0xFFFFFFFFu;
+    max_nc = std::max(max_nc, np + ns);
+    total_nc += np + ns;
+  }
+  // split lengths: about four workgroups per compute unit over all
+  // (sequence, kv head) pairs, at least 4 units, and the stats pass within
+  // the partial capacity of max_splits per pair
+  const int64_t cus = c->num_cus;
+  auto split_len = [&](int64_t total, int maxu) {
+    int su = (int)std::max<int64_t>(4, (total * H + 4 * cus - 1) / (4 * cus));
+    return std::max(su, (maxu + max_splits - 1) / max_splits);
+  };
+  const int su_stats = split_len(total_nc + B, max_nc + 1);
+  const int su_score = split_len(total_nc, max_nc);
+  a.q = d_q;
+  a.k_blk = d_k_blk;
+  a.seg[0] = seg_ptrs(c, 0);
+  a.seg[1] = seg_ptrs(c, 1);
+  a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
+  a.contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_contrib_offset);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.hq = num_q_heads;
+  a.hkv = H;
+  a.r = num_q_heads / H;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.blk_f32 = blk_dtype == KVQ_F32;
+  a.gv_log2 = ilog2(cfg.v_group_channels);
+  a.record_bytes = (uint32_t)c->lay.record_bytes;
+  a.stats_split_units = su_stats;
+  a.max_splits = max_splits;
+  a.use_suffix = use_suffix ? 1 : 0;
+  a.ucap = ucap;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int D = cfg.head_dim;
+  a.split_units = su_stats;
+  hipError_t e = kvq::launch_select(a, 0, (max_nc + 1 + su_stats - 1) / su_stats, B, D, cfg.k_bits, cfg.v_bits, st);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "selection stats launch: %s", hipGetErrorString(e));
+  a.split_units = su_score;
+  e = kvq::launch_select(a, 1, (max_nc + su_score - 1) / su_score, B, D, cfg.k_bits, cfg.v_bits, st);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "selection score launch: %s", hipGetErrorString(e));
+  kvq::TopkArgs t;
+  memset(&t, 0, sizeof(t));
+  t.contrib = a.contrib;
+  t.sel_mask = reinterpret_cast<uint32_t*>(c->dbuf + c->lay.sel_mask_offset);
+  t.sel_units = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_units_offset);
+  t.sel_count = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_count_offset);
+  t.hkv = H;
+  t.ucap = ucap;
+  t.budget = budget;
+  for (int b = 0; b < B; ++b) t.nunits[b] = (uint16_t)(a.nslots[0][b] + a.nslots[1][b]);
+  e = kvq::launch_topk(t, B, st);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "top-k launch: %s", hipGetErrorString(e));
+  c->sel_valid = true;
+  c->sel_gen = c->commit_gen;
+  c->sel_use_suffix = use_suffix ? 1 : 0;
+  c->sel_budget = budget;
   return KVQ_OK;
 }
 

@@ -78,6 +78,12 @@ struct AttnArgs {
   int32_t max_splits;
   int32_t use_suffix;
   int32_t v_centred;    // values in a rotated basis: dequantized around the middle code
+  // selection (all null without one): per (b, kv head) the number of listed
+  // units, the listed cached units, and each cached unit's selected tokens
+  const int32_t* sel_count;
+  const int32_t* sel_units;
+  const uint32_t* sel_mask;
+  int32_t sel_ucap;
   uint16_t nslots[2][KVQ_MAX_BATCH];   // per-sequence slot counts of both segments
   // Workgroup list of a one-dimensional grid: entry i = split | kvh << 8 |
   // b << 16 for workgroup i, only splits that hold units.  num_wg == 0: a
@@ -110,6 +116,40 @@ struct UnrotArgs {
   RotParams rot;
 };
 
+// Mask-query selection: the stats pass (MODE 0) and the score pass (MODE 1)
+// run over the cached units of every (sequence, kv head) in splits of
+// split_units units; MODE 0 also covers the block (the last unit).
+struct SelArgs {
+  const void* q;        // [B, 32, Hq, D]
+  const void* k_blk;    // [B, 32, Hkv, D]
+  SegPtrs seg[2];
+  float* partial;       // per split: [B][Hkv][max_splits][8 heads][2][32] (maximum, sum)
+  float* contrib;       // [B][Hkv][ucap * 32]; -1 for invalid entries
+  float scale_log2;
+  int32_t hq, hkv, r, q_f32, blk_f32, gv_log2;
+  uint32_t record_bytes;
+  int32_t split_units;        // this pass
+  int32_t stats_split_units;  // the stats pass (the score pass merges its partials)
+  int32_t max_splits;
+  int32_t use_suffix;
+  int32_t ucap;               // prefix_slots + suffix_slots
+  uint32_t qmask[KVQ_MAX_BATCH];
+  uint16_t nslots[2][KVQ_MAX_BATCH];
+};
+static_assert(sizeof(SelArgs) <= 4096, "selection launch arguments fit the kernel-argument segment");
+
+// Exact top-k of the contributions per (sequence, kv head), ties to the lower
+// entry; writes per-unit token masks, the list of units with a selected
+// token, and its length.
+struct TopkArgs {
+  const float* contrib;
+  uint32_t* sel_mask;   // [B][Hkv][ucap]
+  int32_t* sel_units;   // [B][Hkv][ucap]
+  int32_t* sel_count;   // [B][Hkv]
+  int32_t hkv, ucap, budget;
+  int32_t nunits[KVQ_MAX_BATCH];    // cached units of each sequence (prefix + suffix if used)
+};
+
 // Record field offsets for (D, kb, vb, G_v): see include/kvq.h.
 __host__ __device__ constexpr uint32_t kc_bytes(int D, int kb) { return kSlot * D * kb / 8; }
 __host__ __device__ constexpr uint32_t vc_bytes(int D, int vb) { return D * vb * 4; }
@@ -125,6 +165,9 @@ hipError_t launch_commit(const CommitArgs& a, int ntasks, int D, int kb, int vb,
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
                             hipStream_t stream);
 hipError_t launch_blk_prep(const BlkPrepArgs& a, int D, hipStream_t stream);
+hipError_t launch_select(const SelArgs& a, int mode, int grid_splits, int B, int D, int kb, int vb,
+                         hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t stream);
 hipError_t launch_unrotate(const UnrotArgs& a, int D, hipStream_t stream);
 
 }  // namespace kvq

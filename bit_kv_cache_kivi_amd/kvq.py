@@ -38,6 +38,8 @@ class KvqLayout(ctypes.Structure):
         ("slot_cap", c_int32 * 2), ("prot_cap", c_int32 * 2),
         ("workspace_offset", c_uint64), ("workspace_bytes", c_uint64),
         ("rotation_offset", c_uint64), ("rotation_bytes", c_uint64),
+        ("sel_contrib_offset", c_uint64), ("sel_mask_offset", c_uint64), ("sel_units_offset", c_uint64),
+        ("sel_count_offset", c_uint64),
     ]
 
 
@@ -62,6 +64,10 @@ def _load():
                                  P(c_int32), P(c_int32), P(c_int32), c_void_p]),
         "kvq_block_attn": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                      c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
+        "kvq_select": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
+                                 c_float, P(ctypes.c_uint32), c_int32, c_void_p]),
+        "kvq_block_attn_selected": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                              c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_segment_info": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_int32)]),
         "kvq_set_split_slots": (c_int32, [c_void_p, c_int32]),
         "kvq_set_v_rotation": (c_int32, [c_void_p, P(c_int32), P(c_float)]),
@@ -199,6 +205,52 @@ class KVCache:
                                  _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
                                  c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
         return out
+
+    def select(self, q, k_blk, budget, use_suffix=False, query_mask=None, softmax_scale=None, stream=None):
+        """Rank the cached entries by the mask queries' contributions and keep
+        the top `budget` per (sequence, kv head).  query_mask: per-sequence
+        32-bit masks of the mask queries (None = all)."""
+        assert q.is_contiguous() and k_blk.is_contiguous()
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
+        qm = None if query_mask is None else (ctypes.c_uint32 * len(query_mask))(*[int(x) & 0xFFFFFFFF for x in query_mask])
+        check(lib.kvq_select(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]), _dtype_code(q),
+                             c_void_p(k_blk.data_ptr()), _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
+                             qm, int(budget), _stream_ptr(stream)))
+
+    def block_attn_selected(self, q, k_blk, v_blk, use_suffix=False, softmax_scale=None, out_dtype=None,
+                            out=None, stream=None):
+        """block_attn over the block and the last selection only."""
+        import torch
+        assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
+        assert k_blk.dtype == v_blk.dtype
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
+        check(lib.kvq_block_attn_selected(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
+                                          _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
+                                          _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
+                                          c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
+        return out
+
+    def selection(self, b, h, nunits):
+        """(contributions fp32 [nunits*32], token masks uint32 [nunits], selected
+        unit list int32) of sequence b, kv head h (views of the buffer)."""
+        import torch
+        L = self.layout
+        H = self.cfg.num_kv_heads
+        ucap = L["slot_cap"][0] + L["slot_cap"][1]
+        pair = b * H + h
+        cb = L["sel_contrib_offset"] + pair * ucap * SLOT * 4
+        contrib = self.buffer[cb:cb + nunits * SLOT * 4].view(torch.float32)
+        mb = L["sel_mask_offset"] + pair * ucap * 4
+        masks = self.buffer[mb:mb + nunits * 4].view(torch.int32)
+        cnt_off = L["sel_count_offset"] + pair * 4
+        n = int(self.buffer[cnt_off:cnt_off + 4].view(torch.int32).item())
+        ub = L["sel_units_offset"] + pair * ucap * 4
+        units = self.buffer[ub:ub + n * 4].view(torch.int32)
+        return contrib, masks, units
 
     def segment_info(self, segment=KVQ_PREFIX):
         B = self.cfg.batch

@@ -158,6 +158,14 @@ typedef struct {
                                                  block K and V in fp32, then the
                                                  rotated output; 0 bytes when
                                                  v_rotation_block == 0            */
+  /* Selection results (kvq_select), ucap = prefix_slots + suffix_slots cached
+   * units per (b, kv head), numbered prefix slots first, then suffix slots:   */
+  uint64_t sel_contrib_offset; /* fp32 [B][Hkv][ucap][32] contribution per entry,
+                                  -1 at slot positions past the valid tokens   */
+  uint64_t sel_mask_offset;    /* uint32 [B][Hkv][ucap] selected tokens per unit */
+  uint64_t sel_units_offset;   /* int32 [B][Hkv][ucap] units with a selected
+                                  token, ascending                             */
+  uint64_t sel_count_offset;   /* int32 [B][Hkv] length of that list          */
 } kvq_layout;
 
 typedef struct kvq_cache kvq_cache;
@@ -208,6 +216,35 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix,
                           const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
                           int32_t block_len, float softmax_scale,
                           void* d_out, int32_t out_dtype, void* stream);
+
+/* Mask-query selection (MaskAhead / Q-MaskAhead abstract: the current block's
+ * mask queries rank the cached KV entries by their estimated contribution to
+ * the attention output; the quantized variant ranks and attends directly from
+ * the low-bit cache).  For every sequence b and kv head h, entry j (a valid
+ * cached token: prefix slots, then suffix slots if use_suffix) gets
+ *     c_j = ||v_j|| * sum over the query heads of h and the mask queries t of
+ *           softmax_t(j),
+ * v_j its dequantized value row and softmax_t the attention distribution of
+ * block query t over all valid cached tokens and the 32 block tokens (scores
+ * q.k * softmax_scale, keys dequantized to fp16).  Mask queries: block tokens
+ * whose bit is set in h_query_mask[b] (host [B]; NULL = all 32).  The
+ * min(budget, valid entries) largest contributions of each (b, h) are
+ * selected, ties to the lower entry (entry number 32 * unit + position).
+ * Arguments as for kvq_block_attn (d_q, d_k_blk; no values are read from the
+ * block); budget >= 0.  Results go to the selection region of the cache buffer
+ * (see kvq_layout) and stay valid until the next commit. */
+kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                      const void* d_k_blk, int32_t blk_dtype, int32_t block_len, float softmax_scale,
+                      const uint32_t* h_query_mask, int32_t budget, void* stream);
+
+/* kvq_block_attn restricted to the last selection: every query token attends
+ * to all 32 block tokens and to the selected cached entries only.  Arguments
+ * as for kvq_block_attn; use_suffix must equal the selection's.  KVQ_EINVAL if
+ * no selection was made since the last commit. */
+kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
+                                   int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                                   int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,
+                                   void* stream);
 
 /* Host mirror of a segment's lengths: any of the [B] arrays may be NULL. */
 kvq_status kvq_segment_info(const kvq_cache* c, int32_t segment,
