@@ -120,6 +120,11 @@ def main():
     ap.add_argument("--layers", type=int, default=28, help="per-layer caches the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--select-budget", type=int, default=0, metavar="K",
+                    help="also time mask-query selection of K entries per (sequence, kv head) and the "
+                         "attention over the selection")
+    ap.add_argument("--select-granularity", type=int, default=1, choices=(1, 32),
+                    help="rank single entries (1) or whole 32-token units (32; the budget then counts units)")
     ap.add_argument("--v-rotation", type=int, default=0, choices=(0, 16, 64),
                     help="store values K-RPBH rotated with this Hadamard block (0: plain values)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -286,6 +291,26 @@ def main():
     commit_ms = timed(do_commit, args.steps, 0)
     commit_bytes = commit_algorithmic(c, [32] * c.B, c.step_protect * c.B, R)
 
+    # (4) optional: selection of the top K entries per (sequence, kv head), then
+    # attention over the selection (the block's mask queries = all 32 tokens)
+    sel = None
+    if args.select_budget:
+        qp, kbp, vbp, op = attn_args
+        use_suf = 1 if c.suffix else 0
+
+        def do_select(i):
+            kvq.check(lib.kvq_select(caches[i % L].handle, use_suf, qp, c.Hq, dtc, kbp, dtc, 32, scale, None,
+                                     args.select_budget, args.select_granularity, sptr))
+
+        def do_attn_sel(i):
+            kvq.check(lib.kvq_block_attn_selected(caches[i % L].handle, use_suf, qp, c.Hq, dtc, kbp, vbp, dtc, 32,
+                                                  scale, op, kvq.KVQ_BF16, sptr))
+        select_ms = timed(do_select, 2 * L, 0)
+        attn_sel_ms = timed(do_attn_sel, args.steps, 0)
+        sel = {"budget": args.select_budget, "granularity": args.select_granularity, "select_ms": select_ms, "attn_selected_ms": attn_sel_ms,
+               "attn_full_ms": attn_ms,
+               "attn_selected_query_tokens_per_s": c.B * 32 / (attn_sel_ms * 1e-3)}
+
     qtok = c.B * 32
     attn_s = attn_ms * 1e-3
     achieved_tflops = a_flops / attn_s / 1e12
@@ -333,6 +358,8 @@ def main():
                                (", with blk_prep_kernel and unrotate_kernel)" if args.v_rotation else ")"),
                      "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS},
     }
+    if sel is not None:
+        res["selection"] = sel
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(c, w, blocks, args.cpu_budget)
     print(json.dumps(res), flush=True)

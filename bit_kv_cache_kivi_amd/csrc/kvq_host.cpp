@@ -100,6 +100,7 @@ void compute_layout(const kvq_config* c, kvq_layout* L) {
   // per cached unit, and the list lengths
   const uint64_t ucap = (uint64_t)c->prefix_slots + (uint64_t)c->suffix_slots;
   L->sel_contrib_offset = off; off += align256(B * H * ucap * kvq::kSlot * 4);
+  L->sel_unit_offset = off;    off += align256(B * H * ucap * 4);
   L->sel_mask_offset = off;    off += align256(B * H * ucap * 4);
   L->sel_units_offset = off;   off += align256(B * H * ucap * 4);
   L->sel_count_offset = off;   off += align256(B * H * 4);
@@ -616,8 +617,9 @@ kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void*
 
 kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                       const void* d_k_blk, int32_t blk_dtype, int32_t block_len, float softmax_scale,
-                      const uint32_t* h_query_mask, int32_t budget, void* stream) {
+                      const uint32_t* h_query_mask, int32_t budget, int32_t granularity, void* stream) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  if (granularity != 1 && granularity != kvq::kSlot) return fail(KVQ_EINVAL, "granularity %d (1 or 32)", granularity);
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
   if (use_suffix && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
@@ -653,16 +655,20 @@ kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t
   const int64_t cus = c->num_cus;
   auto split_len = [&](int64_t total, int maxu) {
     int su = (int)std::max<int64_t>(4, (total * H + 4 * cus - 1) / (4 * cus));
-    return std::max(su, (maxu + max_splits - 1) / max_splits);
+    return std::min(std::max(su, (maxu + max_splits - 1) / max_splits), kvq::kMaxSelSplit);
   };
   const int su_stats = split_len(total_nc + B, max_nc + 1);
   const int su_score = split_len(total_nc, max_nc);
+  if ((int64_t)su_stats * max_splits < max_nc + 1)
+    return fail(KVQ_EUNSUPPORTED, "%d cached units per sequence exceed max_splits %d x %d units", max_nc, max_splits,
+                kvq::kMaxSelSplit);
   a.q = d_q;
   a.k_blk = d_k_blk;
   a.seg[0] = seg_ptrs(c, 0);
   a.seg[1] = seg_ptrs(c, 1);
   a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
   a.contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_contrib_offset);
+  a.unit_contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_unit_offset);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.hq = num_q_heads;
   a.hkv = H;
@@ -686,6 +692,8 @@ kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t
   kvq::TopkArgs t;
   memset(&t, 0, sizeof(t));
   t.contrib = a.contrib;
+  t.unit_contrib = a.unit_contrib;
+  t.granularity = granularity;
   t.sel_mask = reinterpret_cast<uint32_t*>(c->dbuf + c->lay.sel_mask_offset);
   t.sel_units = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_units_offset);
   t.sel_count = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_count_offset);

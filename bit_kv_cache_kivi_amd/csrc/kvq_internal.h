@@ -116,6 +116,8 @@ struct UnrotArgs {
   RotParams rot;
 };
 
+constexpr int kMaxSelSplit = 64;  // units per split of a selection pass
+
 // Mask-query selection: the stats pass (MODE 0) and the score pass (MODE 1)
 // run over the cached units of every (sequence, kv head) in splits of
 // split_units units; MODE 0 also covers the block (the last unit).
@@ -125,6 +127,7 @@ struct SelArgs {
   SegPtrs seg[2];
   float* partial;       // per split: [B][Hkv][max_splits][8 heads][2][32] (maximum, sum)
   float* contrib;       // [B][Hkv][ucap * 32]; -1 for invalid entries
+  float* unit_contrib;  // [B][Hkv][ucap]: sum over each unit's valid entries
   float scale_log2;
   int32_t hq, hkv, r, q_f32, blk_f32, gv_log2;
   uint32_t record_bytes;
@@ -143,6 +146,8 @@ static_assert(sizeof(SelArgs) <= 4096, "selection launch arguments fit the kerne
 // token, and its length.
 struct TopkArgs {
   const float* contrib;
+  const float* unit_contrib;
+  int32_t granularity;  // 1: entries ranked one by one; 32: whole units by their sums
   uint32_t* sel_mask;   // [B][Hkv][ucap]
   int32_t* sel_units;   // [B][Hkv][ucap]
   int32_t* sel_count;   // [B][Hkv]

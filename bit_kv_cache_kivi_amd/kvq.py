@@ -38,7 +38,8 @@ class KvqLayout(ctypes.Structure):
         ("slot_cap", c_int32 * 2), ("prot_cap", c_int32 * 2),
         ("workspace_offset", c_uint64), ("workspace_bytes", c_uint64),
         ("rotation_offset", c_uint64), ("rotation_bytes", c_uint64),
-        ("sel_contrib_offset", c_uint64), ("sel_mask_offset", c_uint64), ("sel_units_offset", c_uint64),
+        ("sel_contrib_offset", c_uint64), ("sel_unit_offset", c_uint64), ("sel_mask_offset", c_uint64),
+        ("sel_units_offset", c_uint64),
         ("sel_count_offset", c_uint64),
     ]
 
@@ -65,7 +66,7 @@ def _load():
         "kvq_block_attn": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                      c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_select": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
-                                 c_float, P(ctypes.c_uint32), c_int32, c_void_p]),
+                                 c_float, P(ctypes.c_uint32), c_int32, c_int32, c_void_p]),
         "kvq_block_attn_selected": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                               c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_segment_info": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_int32)]),
@@ -206,17 +207,19 @@ class KVCache:
                                  c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
         return out
 
-    def select(self, q, k_blk, budget, use_suffix=False, query_mask=None, softmax_scale=None, stream=None):
+    def select(self, q, k_blk, budget, use_suffix=False, query_mask=None, softmax_scale=None, granularity=1,
+               stream=None):
         """Rank the cached entries by the mask queries' contributions and keep
-        the top `budget` per (sequence, kv head).  query_mask: per-sequence
-        32-bit masks of the mask queries (None = all)."""
+        the top `budget` per (sequence, kv head) (granularity 32: the top
+        `budget` 32-token units by summed contributions).  query_mask:
+        per-sequence 32-bit masks of the mask queries (None = all)."""
         assert q.is_contiguous() and k_blk.is_contiguous()
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
         qm = None if query_mask is None else (ctypes.c_uint32 * len(query_mask))(*[int(x) & 0xFFFFFFFF for x in query_mask])
         check(lib.kvq_select(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]), _dtype_code(q),
                              c_void_p(k_blk.data_ptr()), _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
-                             qm, int(budget), _stream_ptr(stream)))
+                             qm, int(budget), int(granularity), _stream_ptr(stream)))
 
     def block_attn_selected(self, q, k_blk, v_blk, use_suffix=False, softmax_scale=None, out_dtype=None,
                             out=None, stream=None):
@@ -236,7 +239,8 @@ class KVCache:
 
     def selection(self, b, h, nunits):
         """(contributions fp32 [nunits*32], token masks uint32 [nunits], selected
-        unit list int32) of sequence b, kv head h (views of the buffer)."""
+        unit list int32, unit sums fp32 [nunits]) of sequence b, kv head h
+        (views of the buffer)."""
         import torch
         L = self.layout
         H = self.cfg.num_kv_heads
@@ -250,7 +254,9 @@ class KVCache:
         n = int(self.buffer[cnt_off:cnt_off + 4].view(torch.int32).item())
         ub = L["sel_units_offset"] + pair * ucap * 4
         units = self.buffer[ub:ub + n * 4].view(torch.int32)
-        return contrib, masks, units
+        sb = L["sel_unit_offset"] + pair * ucap * 4
+        sums = self.buffer[sb:sb + nunits * 4].view(torch.float32)
+        return contrib, masks, units, sums
 
     def segment_info(self, segment=KVQ_PREFIX):
         B = self.cfg.batch

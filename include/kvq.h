@@ -162,6 +162,8 @@ typedef struct {
    * units per (b, kv head), numbered prefix slots first, then suffix slots:   */
   uint64_t sel_contrib_offset; /* fp32 [B][Hkv][ucap][32] contribution per entry,
                                   -1 at slot positions past the valid tokens   */
+  uint64_t sel_unit_offset;    /* fp32 [B][Hkv][ucap] sum of each unit's valid
+                                  entries' contributions                       */
   uint64_t sel_mask_offset;    /* uint32 [B][Hkv][ucap] selected tokens per unit */
   uint64_t sel_units_offset;   /* int32 [B][Hkv][ucap] units with a selected
                                   token, ascending                             */
@@ -230,12 +232,16 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix,
  * whose bit is set in h_query_mask[b] (host [B]; NULL = all 32).  The
  * min(budget, valid entries) largest contributions of each (b, h) are
  * selected, ties to the lower entry (entry number 32 * unit + position).
+ * granularity = 32 ranks whole units (32-token slots) by the sum of their
+ * entries' contributions instead and keeps every valid entry of the
+ * min(budget, units) top units, ties to the lower unit; granularity = 1 is the
+ * per-entry ranking.
  * Arguments as for kvq_block_attn (d_q, d_k_blk; no values are read from the
- * block); budget >= 0.  Results go to the selection region of the cache buffer
+ * block); budget >= 0 (entries, or units with granularity 32).  Results go to the selection region of the cache buffer
  * (see kvq_layout) and stay valid until the next commit. */
 kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                       const void* d_k_blk, int32_t blk_dtype, int32_t block_len, float softmax_scale,
-                      const uint32_t* h_query_mask, int32_t budget, void* stream);
+                      const uint32_t* h_query_mask, int32_t budget, int32_t granularity, void* stream);
 
 /* kvq_block_attn restricted to the last selection: every query token attends
  * to all 32 block tokens and to the selected cached entries only.  Arguments

@@ -25,7 +25,10 @@ Readings where the abstract is silent (each listed in the design notes):
   * the top k = min(budget, number of valid entries) entries are selected,
     ties broken by the lower number;
   * the block always attends to itself; with a selection it attends to the
-    selected cached entries only.
+    selected cached entries only;
+  * a coarser variant ranks whole 32-token slots by the sum of their entries'
+    contributions and keeps every valid entry of the top slots (ties to the
+    lower unit).
 """
 from __future__ import annotations
 
@@ -91,6 +94,19 @@ def select_topk(ids: np.ndarray, contrib: np.ndarray, budget: int) -> np.ndarray
     order = np.lexsort((ids, -np.asarray(contrib, np.float64)))
     k = min(int(budget), len(ids))
     return np.sort(np.asarray(ids)[order[:k]])
+
+
+def select_topk_units(ids: np.ndarray, contrib: np.ndarray, budget: int) -> np.ndarray:
+    """Slot-granular selection: the min(budget, units) units with the largest
+    summed contributions (ties to the lower unit); returns the entry numbers
+    of all their valid tokens, ascending."""
+    ids = np.asarray(ids, np.int64)
+    units = ids // SLOT
+    uniq = np.unique(units)
+    sums = np.array([np.asarray(contrib, np.float64)[units == u].sum() for u in uniq])
+    order = np.lexsort((uniq, -sums))
+    keep = uniq[order[:min(int(budget), len(uniq))]]
+    return np.sort(ids[np.isin(units, keep)])
 
 
 def block_attention_selected(cache, q: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,

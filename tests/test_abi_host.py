@@ -191,17 +191,19 @@ def test_selection_validation(kvq):
     p = ctypes.c_void_p(1 << 33)
     assert kvq.lib.kvq_block_attn_selected(h, 0, p, 4, 1, p, p, 1, 32, 0.125, p, 1, None) == 1
     assert "selection" in kvq.last_error()
-    cases = [(dict(budget=-1), 1), (dict(hq=3), 1), (dict(L=16), 2), (dict(q=None), 1), (dict(suf=1, budget=5), 0)]
+    cases = [(dict(budget=-1), 1), (dict(hq=3), 1), (dict(L=16), 2), (dict(q=None), 1), (dict(gran=16), 1),
+             (dict(suf=1, budget=5), 0)]
     for kw, status in cases:
         a = dict(dict(suf=0, q=p, hq=4, qd=1, kb=p, bd=1, L=32, scale=0.125, budget=8), **kw)
         if status == 0:
             continue     # a well-formed call would launch kernels: covered by the GPU tests
         st = kvq.lib.kvq_select(h, a["suf"], a["q"], a["hq"], a["qd"], a["kb"], a["bd"], a["L"], a["scale"], None,
-                                a["budget"], None)
+                                a["budget"], a.get("gran", 1), None)
         assert st == status, (kw, st, kvq.last_error())
     L = kvq.get_layout(kvq.make_config(2, 2, 64, 4, 4, 64, prefix_slots=3, suffix_slots=1, max_q_heads=4))
     ucap = 4
-    assert L["sel_mask_offset"] - L["sel_contrib_offset"] >= 2 * 2 * ucap * 32 * 4
+    assert L["sel_unit_offset"] - L["sel_contrib_offset"] >= 2 * 2 * ucap * 32 * 4
+    assert L["sel_mask_offset"] - L["sel_unit_offset"] >= 2 * 2 * ucap * 4
     assert L["sel_units_offset"] - L["sel_mask_offset"] >= 2 * 2 * ucap * 4
     assert L["sel_count_offset"] - L["sel_units_offset"] >= 2 * 2 * ucap * 4
     assert L["total_bytes"] - L["sel_count_offset"] >= 2 * 2 * 4

@@ -25,7 +25,7 @@ from gpu_util import announce, attention_error, build_case, dev  # noqa: E402
 SLOT = 32
 
 
-def check_selection(cache, ora, w, budget, use_suffix, qmask):
+def check_selection(cache, ora, w, budget, use_suffix, qmask, granularity=1):
     """Returns {(b, h): selected entry numbers} after checking contributions,
     the GPU top-k and the validity of the selection."""
     c = w.cfg
@@ -36,7 +36,7 @@ def check_selection(cache, ora, w, budget, use_suffix, qmask):
         nu = ora.nslots(0, b) + (ora.nslots(1, b) if use_suffix else 0)
         for h in range(c.Hkv):
             ids, cref = ref[(b, h)]
-            contrib, masks, units = (x.cpu().numpy() for x in cache.selection(b, h, nu))
+            contrib, masks, units, usums = (x.cpu().numpy() for x in cache.selection(b, h, nu))
             # slot positions past the valid tokens carry -1
             valid = np.zeros(nu * SLOT, bool)
             valid[ids] = True
@@ -45,35 +45,52 @@ def check_selection(cache, ora, w, budget, use_suffix, qmask):
             scale = max(cref.max(), 1e-30)
             err = np.abs(got - cref)
             assert np.all(err <= 1e-2 * cref + 1e-4 * scale), (b, h, float((err - 1e-2 * cref).max() / scale))
-            # the GPU's top-k of its own contributions: bit-exact
-            want = select_topk(ids, got, budget)
+            # unit sums against the oracle's sums of its entry contributions
+            uref = np.bincount(ids // SLOT, weights=cref, minlength=nu)
+            assert np.all(np.abs(usums.astype(np.float64) - uref) <= 1e-2 * uref + 1e-4 * uref.max()), (b, h)
             sel = np.flatnonzero(np.unpackbits(masks.view(np.uint8), bitorder="little"))
-            assert np.array_equal(sel, want), (b, h, len(sel), len(want))
             nz = np.flatnonzero(masks != 0)
             assert np.array_equal(units, nz), (b, h)
-            # valid against the oracle: nothing left out is clearly better than what was kept
-            if 0 < len(sel) < len(ids):
-                kept = cref[np.isin(ids, sel)]
-                left = cref[~np.isin(ids, sel)]
-                assert kept.min() >= left.max() - 2e-2 * scale, (b, h, kept.min(), left.max())
+            if granularity == 1:
+                # the GPU's top-k of its own contributions: bit-exact
+                want = select_topk(ids, got, budget)
+                assert np.array_equal(sel, want), (b, h, len(sel), len(want))
+                # valid against the oracle: nothing left out is clearly better than what was kept
+                if 0 < len(sel) < len(ids):
+                    kept = cref[np.isin(ids, sel)]
+                    left = cref[~np.isin(ids, sel)]
+                    assert kept.min() >= left.max() - 2e-2 * scale, (b, h, kept.min(), left.max())
+            else:
+                # top units of the GPU's own unit sums (ties to the lower unit), all their valid entries
+                order = np.lexsort((np.arange(nu), -usums.astype(np.float64)))
+                keep = np.sort(order[:min(budget, nu)])
+                want = np.sort(ids[np.isin(ids // SLOT, keep)])
+                assert np.array_equal(sel, want), (b, h, len(sel), len(want))
+                if 0 < len(keep) < nu:
+                    kept = uref[keep]
+                    left = np.delete(uref, keep)
+                    assert kept.min() >= left.max() - 2e-2 * uref.max(), (b, h)
             selected[(b, h)] = sel
     return selected
 
 
-@pytest.mark.parametrize("name,T,B,budget,use_suffix,qmask", [
-    ("tiny", None, None, 40, False, None),
-    ("dream7b_4bit", 300, 2, 64, False, [0xFFFF0000, 0x0F0F0F0F]),
-    ("dream7b_2bit", 300, 2, 0, False, None),
-    ("dual_long", 400, 2, 150, True, None),
-    ("serve_b32", 384, 6, 10_000, False, None),
+@pytest.mark.parametrize("name,T,B,budget,use_suffix,qmask,gran", [
+    ("tiny", None, None, 40, False, None, 1),
+    ("dream7b_4bit", 300, 2, 64, False, [0xFFFF0000, 0x0F0F0F0F], 1),
+    ("dream7b_2bit", 300, 2, 0, False, None, 1),
+    ("dual_long", 400, 2, 150, True, None, 1),
+    ("serve_b32", 384, 6, 10_000, False, None, 1),
+    ("dream7b_4bit", 300, 2, 3, False, None, 32),
+    ("dual_long", 400, 2, 5, True, [0x0000FFFF, 0xFFFFFFFF], 32),
+    ("tiny", None, None, 100, False, None, 32),
 ])
-def test_select_then_attend(name, T, B, budget, use_suffix, qmask):
-    announce("selection", name, T, B, budget, use_suffix)
+def test_select_then_attend(name, T, B, budget, use_suffix, qmask, gran):
+    announce("selection", name, T, B, budget, use_suffix, gran)
     w, cache, ora = build_case(W.CONFIGS[name], T, B)
     c = w.cfg
     q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
-    cache.select(q, kb, budget, use_suffix=use_suffix, query_mask=qmask)
-    selected = check_selection(cache, ora, w, budget, use_suffix, qmask)
+    cache.select(q, kb, budget, use_suffix=use_suffix, query_mask=qmask, granularity=gran)
+    selected = check_selection(cache, ora, w, budget, use_suffix, qmask, gran)
     ref = block_attention_selected(ora, w.q, w.k_blk, w.v_blk, selected, use_suffix=use_suffix)
     out = cache.block_attn_selected(q, kb, vb, use_suffix=use_suffix, out_dtype=torch.float32)
     e, x = attention_error(out, ref, "f32")

@@ -133,3 +133,19 @@ def test_selected_attention_limits(rot):
                 vbb = O.unrotate(O.rotate_f32(vbb, *c.v_rot), *c.v_rot)
             want = O.attention_rows(q[b, :, hq], kb[b, :, hq // 2], vbb, 1 / 8)
             np.testing.assert_allclose(got[b, :, hq], want, rtol=0, atol=1e-6 if rot else 1e-12)
+
+
+def test_unit_granular_selection_by_hand():
+    """Units ranked by summed contributions; ties to the lower unit; every
+    valid token of a kept unit is kept."""
+    from oracle.selection import select_topk_units
+    ids = np.array([0, 1, 2, 32, 33, 64, 96, 97, 98, 99])
+    cj = np.array([1.0, 1.0, 1.0, 2.0, 1.0, 3.0, 0.5, 0.5, 0.5, 1.5])
+    # unit sums: u0 = 3, u1 = 3, u2 = 3, u3 = 3 -> all tie: lower units first
+    assert select_topk_units(ids, cj, 1).tolist() == [0, 1, 2]
+    assert select_topk_units(ids, cj, 2).tolist() == [0, 1, 2, 32, 33]
+    cj2 = cj.copy()
+    cj2[6] = 5.0                                   # u3 = 7.5 now leads
+    assert select_topk_units(ids, cj2, 1).tolist() == [96, 97, 98, 99]
+    assert select_topk_units(ids, cj2, 0).tolist() == []
+    assert select_topk_units(ids, cj2, 9).tolist() == ids.tolist()
