@@ -331,6 +331,25 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     }
   }
   SegMirror& m = c->seg[segment];
+  // attention-sink protection: a prefix commit that starts a sequence also
+  // protects its first token (merged into the caller's sorted list)
+  std::vector<int32_t> sink_off, sink_idx;
+  if (cfg.protect_sink && segment == KVQ_PREFIX) {
+    bool any = false;
+    for (int b = 0; b < B; ++b) any = any || ((reset_segment || m.ntok[b] == 0) && ntok[b] > 0);
+    if (any) {
+      sink_off.assign(B + 1, 0);
+      for (int b = 0; b < B; ++b) {
+        const int n = h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
+        const int32_t* p = n ? h_prot_idx + h_prot_off[b] : nullptr;
+        if ((reset_segment || m.ntok[b] == 0) && ntok[b] > 0 && (n == 0 || p[0] != 0)) sink_idx.push_back(0);
+        for (int i = 0; i < n; ++i) sink_idx.push_back(p[i]);
+        sink_off[b + 1] = (int32_t)sink_idx.size();
+      }
+      h_prot_off = sink_off.data();
+      h_prot_idx = sink_idx.empty() ? nullptr : sink_idx.data();
+    }
+  }
   const int cap = c->lay.slot_cap[segment], pcap = c->lay.prot_cap[segment];
   for (int b = 0; b < B; ++b) {
     const int base_slots = reset_segment ? 0 : m.nslots[b];

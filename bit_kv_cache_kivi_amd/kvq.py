@@ -25,7 +25,7 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "batch", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group_tokens",
         "v_group_channels", "prefix_slots", "suffix_slots", "prefix_protected",
-        "suffix_protected", "max_q_heads", "max_splits", "v_rotation_block")]
+        "suffix_protected", "max_q_heads", "max_splits", "v_rotation_block", "protect_sink")]
 
 
 class KvqLayout(ctypes.Structure):
@@ -104,10 +104,11 @@ def _int_array(vals):
 
 def make_config(batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128, prefix_slots=1,
                 suffix_slots=0, prefix_protected=0, suffix_protected=0, max_q_heads=None, max_splits=0,
-                v_rotation_block=0):
+                v_rotation_block=0, protect_sink=0):
     return KvqConfig(batch, num_kv_heads, head_dim, k_bits, v_bits, SLOT, v_group, prefix_slots,
                      suffix_slots, prefix_protected, suffix_protected,
-                     max_q_heads if max_q_heads is not None else num_kv_heads, max_splits, v_rotation_block)
+                     max_q_heads if max_q_heads is not None else num_kv_heads, max_splits, v_rotation_block,
+                     int(bool(protect_sink)))
 
 
 def get_layout(cfg: KvqConfig) -> dict:
@@ -140,12 +141,12 @@ class KVCache:
 
     def __init__(self, batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128,
                  prefix_tokens=32, suffix_tokens=0, prefix_protected=0, suffix_protected=0,
-                 max_q_heads=None, max_splits=0, v_rotation_block=0, device="cuda"):
+                 max_q_heads=None, max_splits=0, v_rotation_block=0, protect_sink=False, device="cuda"):
         import torch
         self.cfg = make_config(batch, num_kv_heads, head_dim, k_bits, v_bits, v_group,
                                -(-prefix_tokens // SLOT), -(-suffix_tokens // SLOT),
                                prefix_protected, suffix_protected, max_q_heads, max_splits,
-                               v_rotation_block)
+                               v_rotation_block, protect_sink)
         self.layout = get_layout(self.cfg)
         nbytes = self.layout["total_bytes"]
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)

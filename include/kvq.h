@@ -111,7 +111,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
 #define KVQ_MAX_BATCH 256
 
@@ -141,6 +141,11 @@ typedef struct {
   int32_t max_splits;        /* split-K partial capacity per (b, kv head); 0 = 32   */
   int32_t v_rotation_block;  /* 0 = values stored as they are; 16 or 64 = K-RPBH      */
                              /* rotated values (see kvq_set_v_rotation), D % b == 0 */
+  int32_t protect_sink;      /* != 0: a prefix commit that starts a sequence (segment  */
+                             /* position 0) also protects that first token's key row, */
+                             /* counted against prefix_protected (SoloQ summary page, */
+                             /* paragraph on keeping the attention sink in full       */
+                             /* precision, which matters at 2-bit KV)                 */
 } kvq_config;
 
 typedef struct {

@@ -20,7 +20,11 @@ Readings where the pages are silent (each listed in the design notes):
   * V groups are G_v consecutive channels of one token;
   * a suffix segment is replaced wholesale when it is reset;
   * with a value rotation set (oracle/rotation.py), every committed value row
-    is rotated before it is quantized, and the cache holds rotated values.
+    is rotated before it is quantized, and the cache holds rotated values;
+  * attention-sink protection (SoloQ summary page, paragraph on keeping the
+    attention sink in full precision: barely matters at 4-bit KV, matters at
+    2-bit), when enabled, protects the first token of every sequence's prefix,
+    in addition to the caller's list; the sink is read as that first token.
 """
 from __future__ import annotations
 
@@ -47,8 +51,12 @@ class _SeqSeg:
 class OracleCache:
     """Host model of one layer's cache: B sequences, Hkv kv heads, head dim D."""
 
-    def __init__(self, B: int, Hkv: int, D: int, k_bits: int, v_bits: int, v_group: int, v_rot=None):
-        """v_rot: None, or (perm, mix, block) of the K-RPBH value rotation."""
+    def __init__(self, B: int, Hkv: int, D: int, k_bits: int, v_bits: int, v_group: int, v_rot=None,
+                 protect_sink: bool = False):
+        """v_rot: None, or (perm, mix, block) of the K-RPBH value rotation.
+        protect_sink: a prefix commit that starts a sequence also protects its
+        first token (attention-sink protection)."""
+        self.protect_sink = protect_sink
         assert D % v_group == 0
         self.v_rot = v_rot
         self.B, self.Hkv, self.D = B, Hkv, D
@@ -73,7 +81,10 @@ class OracleCache:
         for b in range(B):
             n = n_max if ntok is None else int(ntok[b])
             p = np.zeros(0, np.int64) if prot is None else np.asarray(prot[b], np.int64)
-            self._commit_seq(self.seg[segment][b], k[b, :n], v[b, :n], p)
+            st = self.seg[segment][b]
+            if self.protect_sink and segment == 0 and st.ntok == 0 and n > 0 and (len(p) == 0 or p[0] != 0):
+                p = np.concatenate([[0], p]).astype(np.int64)
+            self._commit_seq(st, k[b, :n], v[b, :n], p)
 
     def _commit_seq(self, st: _SeqSeg, kb_: np.ndarray, vb_: np.ndarray, prot: np.ndarray):
         n = kb_.shape[0]

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(kvq):
     lib = ctypes.CDLL(SO)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
-    assert kvq.lib.kvq_abi_version() == 2
+    assert kvq.lib.kvq_abi_version() == 3
 
 
 def test_layout_matches_documented_record(kvq):
@@ -207,4 +207,18 @@ def test_selection_validation(kvq):
     assert L["sel_units_offset"] - L["sel_mask_offset"] >= 2 * 2 * ucap * 4
     assert L["sel_count_offset"] - L["sel_units_offset"] >= 2 * 2 * ucap * 4
     assert L["total_bytes"] - L["sel_count_offset"] >= 2 * 2 * 4
+    kvq.lib.kvq_destroy(h)
+
+
+def test_sink_protection_counts_against_capacity(kvq):
+    """With protect_sink, a commit that starts a sequence adds its first token to
+    the protected rows: a list that exactly fills the capacity then overflows."""
+    cfg = kvq.make_config(2, 2, 64, 4, 4, 64, prefix_slots=3, prefix_protected=2, max_q_heads=4, protect_sink=1)
+    n = kvq.lib.kvq_required_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    assert kvq.lib.kvq_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 32), n, ctypes.byref(h)) == 0
+    I = lambda *v: (ctypes.c_int32 * len(v))(*v)   # noqa: E731
+    k = ctypes.c_void_p(1 << 33)
+    # sequence 0 lists 2 positions (not 0): with the sink that is 3 > 2
+    assert kvq.lib.kvq_commit(h, 0, 0, k, k, 1, 40, None, I(0, 2, 3), I(5, 9, 0), None) == 3
     kvq.lib.kvq_destroy(h)

@@ -209,3 +209,33 @@ def test_many_pairs_grid_and_ragged_splits():
             print(f"B={B} split={split}: err={e:.2e}")
             assert x <= 0, (B, split, e)
         cache.close()
+
+
+def test_sink_protection():
+    """protect_sink: the first token of each sequence's prefix is protected in
+    addition to the caller's rows; records bit-exact, attention within the gate."""
+    announce("sink protection")
+    B, H, D = 3, 2, 128
+    g = np.random.default_rng(11)
+    k = g.standard_normal((B, 70, H, D)).astype(np.float32)
+    v = g.standard_normal((B, 70, H, D)).astype(np.float32)
+    cache = kvq.KVCache(B, H, D, 2, 2, 64, prefix_tokens=160, suffix_tokens=32, prefix_protected=8,
+                        suffix_protected=4, max_q_heads=4, protect_sink=True)
+    ora = O.OracleCache(B, H, D, 2, 2, 64, protect_sink=True)
+    prot = [np.array([5, 40]), np.array([0, 3]), np.array([], np.int64)]
+    cache.commit(dev(k, "f32"), dev(v, "f32"), ntok=[70, 33, 0], protected=prot)
+    ora.commit(0, k, v, ntok=[70, 33, 0], prot=prot)
+    cache.commit(dev(k[:, :10], "f32"), dev(v[:, :10], "f32"), ntok=[10, 10, 10])
+    ora.commit(0, k[:, :10], v[:, :10], ntok=[10, 10, 10])
+    cache.commit(dev(k[:, :20], "f32"), dev(v[:, :20], "f32"), segment=kvq.KVQ_SUFFIX)
+    ora.commit(1, k[:, :20], v[:, :20])
+    compare_commit(cache, ora, 0, B)
+    compare_commit(cache, ora, 1, B)
+    assert [cache.protected_rows(0, b)[0].cpu().tolist() for b in range(B)] == [[0, 5, 40], [0, 3], [0]]
+    q = g.standard_normal((B, 32, 4, D)).astype(np.float32)
+    kb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+    vb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+    ref = O.block_attention(ora, q, kb, vb, use_suffix=True)
+    out = cache.block_attn(dev(q, "f32"), dev(kb, "f32"), dev(vb, "f32"), use_suffix=True, out_dtype=torch.float32)
+    e, x = attention_error(out, ref, "f32")
+    assert x <= 0, e
