@@ -45,9 +45,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "9fb781302bfb0a55430cf0b777a4d0449430eb42292ece0e9bb151ebebc8683d",
-        "kib": {"attn_kernel": {"fetch": 33522, "write": 29120},
-                "combine_kernel": {"fetch": 14608, "write": 1792}},
+        "attn_source_sha256": "a1df617ecccb3ea1238467b5ab9361d0caa02896dcb209cea1c1443e25ac3430",
+        "kib": {"attn_kernel": {"fetch": 33527, "write": 29120},
+                "combine_kernel": {"fetch": 14609, "write": 1792}},
     },
 }
 
