@@ -20,6 +20,8 @@ Sources (pages, cited by title and section):
   * MaskAhead / Q-MaskAhead abstract: attention computed directly from low-bit KV.
   * Elastic-Cache abstract, observation (1): masked tokens beyond the active
     window can be cached block-wise (the suffix of the dual cache).
+  * SoloQ abstract and summary page: a hardware-native 4-bit floating-point
+    format with per-block scales (oracle/mxfp4.py, as OCP MX FP4).
   * MaskAhead abstract: mask queries of the current block rank cached entries by
     their estimated contribution to the attention output; the block attends to
     the top-ranked ones (oracle/selection.py).
@@ -35,10 +37,11 @@ from .cache import OracleCache
 from .attention import block_attention, attention_rows
 from .rotation import rotate_f32, unrotate, rotation_matrix, hadamard
 from . import selection
+from . import mxfp4
 
 __all__ = [
     "asym_quantize", "dequantize", "to_bf16_f32", "record_layout", "pack_record",
     "unpack_record", "v_token_position", "HEADER_BYTES", "OracleCache",
     "block_attention", "attention_rows", "rotate_f32", "unrotate", "rotation_matrix", "hadamard",
-    "selection",
+    "selection", "mxfp4",
 ]

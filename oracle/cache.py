@@ -36,6 +36,7 @@ import numpy as np
 from .layout import SLOT, pack_record, pack_header, record_layout
 from .quant import asym_quantize, dequantize, to_bf16_f32
 from .rotation import rotate_f32
+from .mxfp4 import mx_quantize, mx_dequantize, record_layout_mx
 
 
 @dataclasses.dataclass
@@ -52,16 +53,24 @@ class OracleCache:
     """Host model of one layer's cache: B sequences, Hkv kv heads, head dim D."""
 
     def __init__(self, B: int, Hkv: int, D: int, k_bits: int, v_bits: int, v_group: int, v_rot=None,
-                 protect_sink: bool = False):
+                 protect_sink: bool = False, fmt: str = "int"):
         """v_rot: None, or (perm, mix, block) of the K-RPBH value rotation.
         protect_sink: a prefix commit that starts a sequence also protects its
-        first token (attention-sink protection)."""
+        first token (attention-sink protection).
+        fmt: "int" (asymmetric integer codes) or "mxfp4" (oracle/mxfp4.py; 4-bit,
+        value groups of 32 channels)."""
         self.protect_sink = protect_sink
+        self.fmt = fmt
+        assert fmt in ("int", "mxfp4")
+        assert fmt == "int" or (k_bits == 4 and v_bits == 4 and v_group == 32)
         assert D % v_group == 0
         self.v_rot = v_rot
         self.B, self.Hkv, self.D = B, Hkv, D
         self.kb, self.vb, self.gv = k_bits, v_bits, v_group
-        self.layout = record_layout(D, k_bits, v_bits, v_group) if k_bits <= 4 and v_bits <= 4 else None
+        if fmt == "mxfp4":
+            self.layout = record_layout_mx(D)
+        else:
+            self.layout = record_layout(D, k_bits, v_bits, v_group) if k_bits <= 4 and v_bits <= 4 else None
         self.seg = {0: [_SeqSeg() for _ in range(B)], 1: [_SeqSeg() for _ in range(B)]}
 
     # ------------------------------------------------------------------ commit
@@ -104,20 +113,30 @@ class OracleCache:
         # K: per (slot, head, channel), group = the slot's tokens
         k4 = kpad.reshape(ns, SLOT, Hkv, D).transpose(0, 2, 3, 1)          # [ns, Hkv, D, 32]
         kmem = np.broadcast_to((valid & ~isprot)[:, None, None, :], k4.shape)
-        kc, ks, kz = asym_quantize(np.ascontiguousarray(k4), self.kb, kmem)
+        if self.fmt == "mxfp4":
+            kc, ks = mx_quantize(np.ascontiguousarray(k4), kmem)            # ks: scale bytes [ns, Hkv, D]
+            kz = None
+        else:
+            kc, ks, kz = asym_quantize(np.ascontiguousarray(k4), self.kb, kmem)
         kcodes = kc.transpose(0, 1, 3, 2)                                   # [ns, Hkv, 32, D]
         # V: per (slot, head, token, channel group), group = G_v channels
         v5 = vpad.reshape(ns, SLOT, Hkv, G, self.gv).transpose(0, 2, 1, 3, 4)  # [ns, Hkv, 32, G, gv]
         vmem = np.broadcast_to(valid[:, None, :, None, None], v5.shape)
-        vc, vs, vz = asym_quantize(np.ascontiguousarray(v5), self.vb, vmem)
+        if self.fmt == "mxfp4":
+            vc, vs = mx_quantize(np.ascontiguousarray(v5), vmem)            # vs: [ns, Hkv, 32, G]
+            vz = None
+        else:
+            vc, vs, vz = asym_quantize(np.ascontiguousarray(v5), self.vb, vmem)
         vcodes = vc.reshape(ns, Hkv, SLOT, D).transpose(0, 1, 3, 2)          # [ns, Hkv, D, 32]
         vscale = vs.transpose(0, 1, 3, 2)                                    # [ns, Hkv, G, 32]
-        vzero = vz.transpose(0, 1, 3, 2)
+        vzero = None if vz is None else vz.transpose(0, 1, 3, 2)
 
         # the packed record exists for the ABI's bit widths; wider codes (used
         # only to study the high-precision limit) are kept unpacked
         records = None
-        if self.kb in (2, 4) and self.vb in (2, 4):
+        if self.fmt == "mxfp4":
+            records = self._pack_mx(kcodes, vcodes, ks, vscale)
+        elif self.kb in (2, 4) and self.vb in (2, 4):
             records = pack_record(kcodes, vcodes, ks, kz, vscale, vzero, self.kb, self.vb, self.gv)
         headers = []
         base = len(st.prot_pos)
@@ -136,6 +155,23 @@ class OracleCache:
         st.headers.extend(headers)
         st.ntok += n
         st.nslots += ns
+
+    def _pack_mx(self, kcodes, vcodes, kscale, vscale):
+        """MX FP4 records: the 4-bit code layout, then the scale bytes."""
+        from .layout import pack_k_words, pack_v_words
+        lay = self.layout
+        lead = kcodes.shape[:-2]
+        n = int(np.prod(lead, dtype=np.int64))
+        out = np.zeros((n, lay["record_bytes"]), np.uint8)
+
+        def put(off, arr):
+            b = np.ascontiguousarray(arr).reshape(n, -1).view(np.uint8)
+            out[:, off:off + b.shape[1]] = b
+        put(lay["kc_offset"], np.swapaxes(pack_k_words(kcodes, 4), -1, -2).astype("<u4"))
+        put(lay["vc_offset"], np.swapaxes(pack_v_words(vcodes, 4), -1, -2).astype("<u4"))
+        put(lay["kmeta_offset"], np.asarray(kscale, np.uint8))                  # [.., D]
+        put(lay["vmeta_offset"], np.asarray(vscale, np.uint8))                  # [.., G, 32]
+        return out.reshape(lead + (lay["record_bytes"],))
 
     # ------------------------------------------------------------------ views
     def ntok(self, segment: int, b: int) -> int:
@@ -180,12 +216,18 @@ class OracleCache:
         ns = st.nslots
         # K: code * scale_c + zero_c, per channel c of the slot
         kc = c["kcodes"][:, h]                                   # [ns, 32, D]
-        khat = dequantize(kc.transpose(0, 2, 1), c["kscale"][:, h], c["kzero"][:, h]).transpose(0, 2, 1)
+        if self.fmt == "mxfp4":
+            khat = mx_dequantize(kc.transpose(0, 2, 1), c["kscale"][:, h]).transpose(0, 2, 1)
+        else:
+            khat = dequantize(kc.transpose(0, 2, 1), c["kscale"][:, h], c["kzero"][:, h]).transpose(0, 2, 1)
         # V: code * scale_t + zero_t, per token t and channel group
         vc = c["vcodes"][:, h]                                   # [ns, D, 32]
         G = self.D // self.gv
         v5 = vc.reshape(ns, G, self.gv, SLOT).transpose(0, 3, 1, 2)          # [ns, 32, G, gv]
-        vhat = dequantize(v5, c["vscale"][:, h].transpose(0, 2, 1), c["vzero"][:, h].transpose(0, 2, 1))
+        if self.fmt == "mxfp4":
+            vhat = mx_dequantize(v5, c["vscale"][:, h].transpose(0, 2, 1))
+        else:
+            vhat = dequantize(v5, c["vscale"][:, h].transpose(0, 2, 1), c["vzero"][:, h].transpose(0, 2, 1))
         vhat = vhat.reshape(ns, SLOT, self.D)
         rank_rows = st.prot_rows
         for j, (nvalid, mask, base, _) in enumerate(st.headers):
