@@ -125,6 +125,8 @@ def main():
                          "attention over the selection")
     ap.add_argument("--select-granularity", type=int, default=1, choices=(1, 32),
                     help="rank single entries (1) or whole 32-token units (32; the budget then counts units)")
+    ap.add_argument("--kv-format", default="int", choices=("int", "mxfp4"),
+                    help="cache format: asymmetric integer codes, or MX FP4 (4-bit, 32-channel value groups)")
     ap.add_argument("--v-rotation", type=int, default=0, choices=(0, 16, 64),
                     help="store values K-RPBH rotated with this Hadamard block (0: plain values)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -150,6 +152,9 @@ def main():
     from bit_kv_cache_kivi_amd import kvq
 
     cfg = W.CONFIGS[args.config]
+    if args.kv_format == "mxfp4":
+        import dataclasses
+        cfg = dataclasses.replace(cfg, k_bits=4, v_bits=4, v_group=32)
     w = W.make(cfg)
     c = cfg
     L = args.layers
@@ -174,7 +179,8 @@ def main():
                                   prefix_tokens=max_prefix + 32 * (commits_per_layer + 1),
                                   suffix_tokens=c.suffix, prefix_protected=prot_cap,
                                   suffix_protected=sprot_cap if c.suffix else 0, max_q_heads=c.Hq,
-                                  v_rotation_block=args.v_rotation))
+                                  v_rotation_block=args.v_rotation,
+                                  kv_format=kvq.KVQ_FMT_MXFP4 if args.kv_format == "mxfp4" else kvq.KVQ_FMT_INT))
         if args.v_rotation:
             caches[-1].set_v_rotation(*W.krpbh_params(c.D, args.v_rotation))
     torch.cuda.synchronize()
@@ -340,7 +346,7 @@ def main():
         "config": {"workload": c.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D,
                    "prefix_tokens": int(max_prefix), "block": 32, "k_bits": c.k_bits, "v_bits": c.v_bits,
                    "v_group": c.v_group, "protected_frac": c.prot_frac, "layers_rotated": L,
-                   "v_rotation_block": args.v_rotation, "parallelism": "none"},
+                   "v_rotation_block": args.v_rotation, "kv_format": args.kv_format, "parallelism": "none"},
         "attn_ms": attn_ms,
         "commit_ms": commit_ms,
         "attn_query_tokens_per_s": qtok / attn_s,
@@ -353,7 +359,7 @@ def main():
         "prefill_commit_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
         "prefill_commit_hbm_frac": prefill_bytes / (prefill_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
-        "roofline": {**roof, "traffic": None if args.v_rotation else measured_traffic(c.name),
+        "roofline": {**roof, "traffic": None if (args.v_rotation or args.kv_format != "int") else measured_traffic(c.name),
                      "kernel": "attention launch (attn_kernel + combine_kernel" +
                                (", with blk_prep_kernel and unrotate_kernel)" if args.v_rotation else ")"),
                      "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS},

@@ -72,15 +72,20 @@ struct Shape {
 // instead of one shared by every channel with the same code; those shared
 // errors would line up with the constant vector that the transposed
 // Hadamard transform concentrates into one channel per block.
-template <int KB, int VB, int D, int NC, bool CEN>
+// MX (MX FP4 records): codes are E2M1 with one E8M0 scale byte per key
+// channel and per (value group of 32 channels, token); the hardware converts
+// the codes to fp16 exactly and a packed fp16 multiply applies the power-of-two
+// scales, so the keys need no lo part (it is stored as zero).
+template <int KB, int VB, int D, int NC, bool CEN, bool MX>
 __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const AttnArgs a) {
   using S = Shape<D>;
   constexpr int KS = S::KS, CT = S::CT, GPT = S::GPT, VPT = S::VPT, RPT = S::RPT;
   constexpr int NPT = kProducerThreads;
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
-  constexpr uint32_t KM = kmeta_bytes(D);
+  constexpr uint32_t KM = MX ? D : kmeta_bytes(D);
   static_assert(record_bytes(D, KB, VB, 32) <= 48 * D, "record fits a stage");
+  static_assert(!MX || (KB == 4 && VB == 4), "MX FP4 codes are 4-bit");
 
   __shared__ __align__(16) uint8_t rawbuf[2][S::STAGE];      // packed slot records / the block
   __shared__ __align__(16) uint4 prtbuf[2][GPT][NPT];        // a producer thread's protected-row chunks
@@ -293,17 +298,21 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   auto klo_part = [&](int kb, int cg, int t) __attribute__((always_inline)) -> uint2& {
     return reinterpret_cast<uint2*>(&klo[kb][cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1];
   };
-  struct DqIn { uint32_t kw[GPT]; uint4 kp[GPT]; float4 ks[2], kz[2]; uint32_t vw[VPT]; float4 vs[2], vz[2]; };
+  struct DqIn { uint32_t kw[GPT]; uint4 kp[GPT]; float4 ks[2], kz[2]; uint32_t vw[VPT]; float4 vs[2], vz[2]; uint2 kb8, vb8; };
   auto dq_fetch = [&](int q, DqIn& d) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
     // K: tokens kt0 + KTT*gi of channel group kcg; their codes are word kcg
     // (4-bit) or half kcg % 2 of word kcg / 2 (2-bit) of the token's word column.
-    const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC) + 8 * kcg;
-    d.ks[0] = *reinterpret_cast<const float4*>(kmeta);
-    d.ks[1] = *reinterpret_cast<const float4*>(kmeta + 4);
-    d.kz[0] = *reinterpret_cast<const float4*>(kmeta + D);
-    d.kz[1] = *reinterpret_cast<const float4*>(kmeta + D + 4);
+    if constexpr (MX) {
+      d.kb8 = *reinterpret_cast<const uint2*>(rawS + KC + VC + 8 * kcg);     // the 8 channels' scale bytes
+    } else {
+      const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC) + 8 * kcg;
+      d.ks[0] = *reinterpret_cast<const float4*>(kmeta);
+      d.ks[1] = *reinterpret_cast<const float4*>(kmeta + 4);
+      d.kz[0] = *reinterpret_cast<const float4*>(kmeta + D);
+      d.kz[1] = *reinterpret_cast<const float4*>(kmeta + D + 4);
+    }
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
       const int t = kt0 + KTT * gi;
@@ -312,11 +321,17 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     }
     // V: channels vch[vi] of token octet (vmm, vhh); 4-bit: word 2vmm+vhh of
     // the channel; 2-bit: half vmm of word vhh.
-    const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (vch[0] >> gv_log2) * 256);
-    d.vs[0] = *reinterpret_cast<const float4*>(vs + vta);
-    d.vs[1] = *reinterpret_cast<const float4*>(vs + vta + 8);
-    d.vz[0] = *reinterpret_cast<const float4*>(vs + 32 + vta);
-    d.vz[1] = *reinterpret_cast<const float4*>(vs + 32 + vta + 8);
+    if constexpr (MX) {
+      // scale bytes of tokens vta..vta+3 and vta+8..vta+11 of the channels' group
+      const uint8_t* vb = rawS + KC + VC + KM + (vch[0] >> 5) * kSlot;
+      d.vb8 = make_uint2(*reinterpret_cast<const uint32_t*>(vb + vta), *reinterpret_cast<const uint32_t*>(vb + vta + 8));
+    } else {
+      const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (vch[0] >> gv_log2) * 256);
+      d.vs[0] = *reinterpret_cast<const float4*>(vs + vta);
+      d.vs[1] = *reinterpret_cast<const float4*>(vs + vta + 8);
+      d.vz[0] = *reinterpret_cast<const float4*>(vs + 32 + vta);
+      d.vz[1] = *reinterpret_cast<const float4*>(vs + 32 + vta + 8);
+    }
 #pragma unroll
     for (int vi = 0; vi < VPT; ++vi)
       d.vw[vi] = VB == 4 ? words[KC / 4 + (2 * vmm + vhh) * D + vch[vi]] : words[KC / 4 + vhh * D + vch[vi]];
@@ -324,7 +339,52 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   auto dequant = [&](int q, uint32_t mask, const DqIn& d) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const int kb = q & 1, vbuf = q % 3;
-    if (q < nq) {
+    if (MX && q < nq) {
+      // scale pairs 2^(s - 127) as fp16 (exact within the fp16 range; the
+      // scale of an all-zero group, byte 0, reads as 0)
+      auto pairs = [](uint2 b8, half2_t (&sp)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = j < 2 ? b8.x : b8.y;
+          const uint32_t b0 = (w >> (16 * (j & 1))) & 0xFFu, b1 = (w >> (16 * (j & 1) + 8)) & 0xFFu;
+          sp[j] = to_half2(__uint_as_float(b0 << 23), __uint_as_float(b1 << 23));
+        }
+      };
+      auto fp4x8 = [](uint32_t w, const half2_t (&sp)[4]) __attribute__((always_inline)) {
+        half8 h;
+        half2_t p;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sp[0]; h[0] = p.x; h[1] = p.y;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sp[1]; h[2] = p.x; h[3] = p.y;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sp[2]; h[4] = p.x; h[5] = p.y;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sp[3]; h[6] = p.x; h[7] = p.y;
+        return h;
+      };
+      half2_t ksp[4];
+      pairs(d.kb8, ksp);
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi) {
+        const int t = kt0 + KTT * gi;
+        if ((mask >> t) & 1u) {
+          const uint4 w = d.kp[gi];
+          float x[8];
+          x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+          x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+          store_hi_lo8(kop[kb][kks][t + 32 * khh], klo_part(kb, kcg, t), x, neg_one);
+        } else {
+          // key word: channel 8*kcg + c at bits 4c
+          kop[kb][kks][t + 32 * khh] = fp4x8(d.kw[gi], ksp);
+          klo_part(kb, kcg, t) = make_uint2(0u, 0u);
+        }
+      }
+      // value word of channel c: token e (vta + e % 4 + 8 * (e / 4)) at bits 4e
+      half2_t vsp[4];
+      pairs(d.vb8, vsp);
+#pragma unroll
+      for (int vi = 0; vi < VPT; ++vi) {
+        const int c = vch[vi];
+        vop[vbuf][c >> 5][vmm][(c & 31) + 32 * vhh] = fp4x8(d.vw[vi], vsp);
+      }
+    } else if (q < nq) {
       const float ksc[8] = {d.ks[0].x, d.ks[0].y, d.ks[0].z, d.ks[0].w, d.ks[1].x, d.ks[1].y, d.ks[1].z, d.ks[1].w};
       const float kzr[8] = {d.kz[0].x, d.kz[0].y, d.kz[0].z, d.kz[0].w, d.kz[1].x, d.kz[1].y, d.kz[1].z, d.kz[1].w};
 #pragma unroll
@@ -882,12 +942,21 @@ template <int KB, int VB, int D>
 hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
   const dim3 grid = a.num_wg ? dim3(a.num_wg) : dim3(grid_splits, a.hkv, B);
   const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
-  if (a.v_centred) {
-    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, true>), grid, block, 0, s, a);
-    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, true>), grid, block, 0, s, a);
+  bool done = false;
+  if constexpr (KB == 4 && VB == 4) {
+    if (a.mx) {
+      if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, true>), grid, block, 0, s, a);
+      else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, true>), grid, block, 0, s, a);
+      done = true;
+    }
+  }
+  if (done) {
+  } else if (a.v_centred) {
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, true, false>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, true, false>), grid, block, 0, s, a);
   } else {
-    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false>), grid, block, 0, s, a);
-    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false>), grid, block, 0, s, a);
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, false>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, false>), grid, block, 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;

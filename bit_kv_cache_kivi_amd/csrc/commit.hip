@@ -154,7 +154,7 @@ __device__ __forceinline__ float swz_xor(float x) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (M << 10)));
 }
 
-template <int KB, int VB, int D, bool F32IN, bool ROT>
+template <int KB, int VB, int D, bool F32IN, bool ROT, bool MX>
 __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(const CommitArgs a, int ntasks) {
   constexpr int HC = D / 2;              // channels per key wave
   constexpr int NCGK = HC / 8;           // 8-channel groups per key wave
@@ -168,8 +168,9 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
   constexpr int PPR = F32IN ? 2 : 1;     // 16-byte pieces per 8-channel row piece
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
-  constexpr uint32_t KM = kmeta_bytes(D);
-  constexpr uint32_t REC_MAX = record_bytes(D, KB, VB, 32);
+  // MX FP4 records: one scale byte per key channel and per (value group, token)
+  constexpr uint32_t KM = MX ? D : kmeta_bytes(D);
+  constexpr uint32_t REC_MAX = MX ? (KC + VC + 2 * D + 255) / 256 * 256 : record_bytes(D, KB, VB, 32);
   constexpr int TST = 9 * NTQK;          // padded row of the key statistics exchange
   static_assert(NTQK == 8 || NTQK == 16, "key lanes per channel group");
   static_assert(TPLK == 2 || TPLK == 4, "key tokens per lane");
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool keys = wave < 2;
   const uint32_t rbytes = a.record_bytes;
-  const uint32_t raw_end = KC + VC + KM + (uint32_t)(D >> a.gv_log2) * 256u;
+  const uint32_t raw_end = MX ? KC + VC + 2 * D : KC + VC + KM + (uint32_t)(D >> a.gv_log2) * 256u;
   // lane geometry: a key lane holds tokens tq*TPLK + k of channel group cg
   // (the NTQK lanes of a channel group are consecutive); a value lane holds
   // tokens t0 + k of channel group cg (the lanes of a value group are consecutive)
@@ -321,65 +322,102 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
         gmx = vmax3(gmx, m.x, m.y); gmx = vmax3(gmx, m.z, m.w);
       }
     }
-    const GroupParams gp = group_params<KB>(gmn, gmx, true);
-    float* kscale = reinterpret_cast<float*>(rec + KC + VC);
-    if (tq < 8) {
-      kscale[8 * cg + ch] = gp.scale;
-      kscale[D + 8 * cg + ch] = gp.zero;
-      krcp[8 * cg + ch] = gp.rcp;
-    }
-    wave_lds_sync();
-    // scales stay in LDS: only the rare exact path reads them
-    float zero[8], rcp[8];
-    {
-      const float4 z0 = *reinterpret_cast<const float4*>(kscale + D + 8 * cg);
-      const float4 z1 = *reinterpret_cast<const float4*>(kscale + D + 8 * cg + 4);
-      const float4 r0 = *reinterpret_cast<const float4*>(krcp + 8 * cg);
-      const float4 r1 = *reinterpret_cast<const float4*>(krcp + 8 * cg + 4);
-      zero[0] = z0.x; zero[1] = z0.y; zero[2] = z0.z; zero[3] = z0.w;
-      zero[4] = z1.x; zero[5] = z1.y; zero[6] = z1.z; zero[7] = z1.w;
-      rcp[0] = r0.x; rcp[1] = r0.y; rcp[2] = r0.z; rcp[3] = r0.w;
-      rcp[4] = r1.x; rcp[5] = r1.y; rcp[6] = r1.z; rcp[7] = r1.w;
-    }
-    // codes of token k: channel c in bits [KB*c, KB*c + KB) of its word
-    uint32_t word[TPLK];
-#pragma unroll
-    for (int k = 0; k < TPLK; ++k) {
-      uint32_t p[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float d = x[k][c] - zero[c];
-        const float y = d * rcp[c];
-        float r = rintf(y);
-        if (fabsf(y - r) >= kNearHalf) r = exact_code(d, kscale[8 * cg + c], LEV);   // rare: near a boundary
-        if (KB == 4) p[c & 1] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 1, p[c & 1]);
-        else         p[c & 3] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 2, p[c & 3]);
+    if constexpr (MX) {
+      // MX FP4: one E8M0 byte per channel, s = max(E(amax) - 2, 0), codes
+      // E2M1(x * 2^(127 - s)) by the hardware conversion (round to nearest
+      // even, saturating at 6; the power-of-two scaling is exact)
+      const bool any = gmn <= gmx;
+      const float amax = any ? fmaxf(-gmn, gmx) : 0.f;
+      const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
+      const uint32_t sb = eb > 2u ? eb - 2u : 0u;
+      if (tq < 8) {
+        rec[KC + VC + 8 * cg + ch] = (uint8_t)sb;
+        krcp[8 * cg + ch] = amax > 0.f ? __uint_as_float((254u - sb) << 23) : 0.f;
       }
-      const uint32_t w = KB == 4 ? (p[0] | (p[1] << 4)) : (p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6));
-      word[k] = ((member >> k) & 1u) ? w : 0u;
-    }
-    if (__any(gp.bad)) {
+      wave_lds_sync();
+      float mul[8];
+      {
+        const float4 m0 = *reinterpret_cast<const float4*>(krcp + 8 * cg);
+        const float4 m1 = *reinterpret_cast<const float4*>(krcp + 8 * cg + 4);
+        mul[0] = m0.x; mul[1] = m0.y; mul[2] = m0.z; mul[3] = m0.w;
+        mul[4] = m1.x; mul[5] = m1.y; mul[6] = m1.z; mul[7] = m1.w;
+      }
+      uint32_t zm = 0;   // channels of an all-zero group keep code 0 (also for -0 inputs)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) zm |= (mul[c] != 0.f ? 0xFu : 0u) << (4 * c);
+      uint32_t word[TPLK];
 #pragma unroll
       for (int k = 0; k < TPLK; ++k) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float q = exact_code(x[k][c] - zero[c], kscale[8 * cg + c], LEV);
-          w |= (uint32_t)q << (KB * c);
-        }
-        word[k] = ((member >> k) & 1u) ? w : 0u;
+        uint32_t w = 0;   // byte j: channels 2j (low nibble) and 2j + 1
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][0] * mul[0], x[k][1] * mul[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][2] * mul[2], x[k][3] * mul[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][4] * mul[4], x[k][5] * mul[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][6] * mul[6], x[k][7] * mul[7], 1.0f, 3);
+        word[k] = ((member >> k) & 1u) ? (w & zm) : 0u;
       }
-    }
-    // word-major: the word holding channel group cg of token t.  4-bit: the
-    // lane's TPLK tokens are consecutive words, written at once (a wide write
-    // also avoids the bank conflicts of lanes 32 words apart)
-    if (KB == 4) {
       if (TPLK == 4) *reinterpret_cast<uint4*>(rec + (cg * 32 + t0) * 4) = make_uint4(word[0], word[1], word[TPLK - 2], word[TPLK - 1]);
       else           *reinterpret_cast<uint2*>(rec + (cg * 32 + t0) * 4) = make_uint2(word[0], word[TPLK - 1]);
     } else {
-#pragma unroll
-      for (int k = 0; k < TPLK; ++k)
-        *reinterpret_cast<uint16_t*>(rec + ((cg >> 1) * 32 + t0 + k) * 4 + 2 * (cg & 1)) = (uint16_t)word[k];
+      const GroupParams gp = group_params<KB>(gmn, gmx, true);
+      float* kscale = reinterpret_cast<float*>(rec + KC + VC);
+      if (tq < 8) {
+        kscale[8 * cg + ch] = gp.scale;
+        kscale[D + 8 * cg + ch] = gp.zero;
+        krcp[8 * cg + ch] = gp.rcp;
+      }
+      wave_lds_sync();
+      // scales stay in LDS: only the rare exact path reads them
+      float zero[8], rcp[8];
+      {
+        const float4 z0 = *reinterpret_cast<const float4*>(kscale + D + 8 * cg);
+        const float4 z1 = *reinterpret_cast<const float4*>(kscale + D + 8 * cg + 4);
+        const float4 r0 = *reinterpret_cast<const float4*>(krcp + 8 * cg);
+        const float4 r1 = *reinterpret_cast<const float4*>(krcp + 8 * cg + 4);
+        zero[0] = z0.x; zero[1] = z0.y; zero[2] = z0.z; zero[3] = z0.w;
+        zero[4] = z1.x; zero[5] = z1.y; zero[6] = z1.z; zero[7] = z1.w;
+        rcp[0] = r0.x; rcp[1] = r0.y; rcp[2] = r0.z; rcp[3] = r0.w;
+        rcp[4] = r1.x; rcp[5] = r1.y; rcp[6] = r1.z; rcp[7] = r1.w;
+      }
+      // codes of token k: channel c in bits [KB*c, KB*c + KB) of its word
+      uint32_t word[TPLK];
+  #pragma unroll
+      for (int k = 0; k < TPLK; ++k) {
+        uint32_t p[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float d = x[k][c] - zero[c];
+          const float y = d * rcp[c];
+          float r = rintf(y);
+          if (fabsf(y - r) >= kNearHalf) r = exact_code(d, kscale[8 * cg + c], LEV);   // rare: near a boundary
+          if (KB == 4) p[c & 1] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 1, p[c & 1]);
+          else         p[c & 3] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 2, p[c & 3]);
+        }
+        const uint32_t w = KB == 4 ? (p[0] | (p[1] << 4)) : (p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6));
+        word[k] = ((member >> k) & 1u) ? w : 0u;
+      }
+      if (__any(gp.bad)) {
+  #pragma unroll
+        for (int k = 0; k < TPLK; ++k) {
+          uint32_t w = 0;
+  #pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float q = exact_code(x[k][c] - zero[c], kscale[8 * cg + c], LEV);
+            w |= (uint32_t)q << (KB * c);
+          }
+          word[k] = ((member >> k) & 1u) ? w : 0u;
+        }
+      }
+      // word-major: the word holding channel group cg of token t.  4-bit: the
+      // lane's TPLK tokens are consecutive words, written at once (a wide write
+      // also avoids the bank conflicts of lanes 32 words apart)
+      if (KB == 4) {
+        if (TPLK == 4) *reinterpret_cast<uint4*>(rec + (cg * 32 + t0) * 4) = make_uint4(word[0], word[1], word[TPLK - 2], word[TPLK - 1]);
+        else           *reinterpret_cast<uint2*>(rec + (cg * 32 + t0) * 4) = make_uint2(word[0], word[TPLK - 1]);
+      } else {
+  #pragma unroll
+        for (int k = 0; k < TPLK; ++k)
+          *reinterpret_cast<uint16_t*>(rec + ((cg >> 1) * 32 + t0 + k) * 4 + 2 * (cg & 1)) = (uint16_t)word[k];
+      }
     }
   };
 
@@ -514,64 +552,92 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
       smn = pick((kk & 1) != 0, mn[TPLV - 1], mn[0]);
       smx = pick((kk & 1) != 0, mx[TPLV - 1], mx[0]);
     }
-    const GroupParams gp = group_params<VB>(smn, smx, t0 + kk < task.nvalid);
-    float* vs = reinterpret_cast<float*>(rec + KC + VC + KM + g * 256);
-    if (gl < TPLV) {
-      vs[t0 + kk] = gp.scale;
-      vs[32 + t0 + kk] = gp.zero;
-      vrcp[g][t0 + kk] = gp.rcp;
-    }
-    wave_lds_sync();
-    // scales stay in LDS: only the rare exact path reads them
-    float zero[TPLV], rcp[TPLV];
-    if (TPLV == 4) {
-      const float4 z = *reinterpret_cast<const float4*>(vs + 32 + t0);
-      const float4 r = *reinterpret_cast<const float4*>(&vrcp[g][t0]);
-      zero[0] = z.x; zero[1] = z.y; zero[TPLV - 2] = z.z; zero[TPLV - 1] = z.w;
-      rcp[0] = r.x; rcp[1] = r.y; rcp[TPLV - 2] = r.z; rcp[TPLV - 1] = r.w;
+    uint32_t bits[8];
+    if constexpr (MX) {
+      // MX FP4: per (token, 32-channel group) one E8M0 byte, codes as for keys
+      const bool any = t0 + kk < task.nvalid && smn <= smx;
+      const float amax = any ? fmaxf(-smn, smx) : 0.f;
+      const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
+      const uint32_t sb = eb > 2u ? eb - 2u : 0u;
+      if (gl < TPLV) {
+        rec[KC + VC + KM + g * kSlot + t0 + kk] = (uint8_t)sb;
+        vrcp[g][t0 + kk] = amax > 0.f ? __uint_as_float((254u - sb) << 23) : 0.f;
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int c = 0; c < 8; ++c) bits[c] = 0u;
+#pragma unroll
+      for (int k = 0; k < TPLV; ++k) {
+        const float m = vrcp[g][t0 + k];
+        uint32_t w = 0;   // byte j: channels 2j (low nibble) and 2j + 1
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][0] * m, x[k][1] * m, 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][2] * m, x[k][3] * m, 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][4] * m, x[k][5] * m, 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k][6] * m, x[k][7] * m, 1.0f, 3);
+        if (m == 0.f) w = 0u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bits[c] |= ((w >> (4 * c)) & 0xFu) << (4 * k);
+      }
     } else {
-      const float2 z = *reinterpret_cast<const float2*>(vs + 32 + t0);
-      const float2 r = *reinterpret_cast<const float2*>(&vrcp[g][t0]);
-      zero[0] = z.x; zero[TPLV - 1] = z.y;
-      rcp[0] = r.x; rcp[TPLV - 1] = r.y;
-    }
-    // The lane's TPLV consecutive tokens land next to each other in one code
-    // word of each channel: token t goes to
-    //   mm = t / 16, hh = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2)
-    //   4-bit: word 2*mm + hh, bits 4e;  2-bit: word hh, bits 2*(8*mm + e)
-    // bits[c] holds the lane's codes of channel c from bit 0 on.
-    // 4-bit: tokens k = 0, 2 go to bytes 0, 1 of pe and k = 1, 3 to those
-    // of po (v_cvt_pk_u8_f32), so pe | po << 4 has token k at bits 4k
-    uint32_t bits[8], pe[8], po[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) bits[c] = pe[c] = po[c] = 0u;
-#pragma unroll
-    for (int k = 0; k < TPLV; ++k) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float d = x[k][c] - zero[k];
-        const float y = d * rcp[k];
-        float r = rintf(y);
-        if (fabsf(y - r) >= kNearHalf) r = exact_code(d, vs[t0 + k], LEV);   // rare: near a boundary
-        if (VB == 4) {
-          if (k & 1) po[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, po[c]);
-          else       pe[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, pe[c]);
-        } else {
-          bits[c] |= (uint32_t)r << (VB * k);
+      const GroupParams gp = group_params<VB>(smn, smx, t0 + kk < task.nvalid);
+      float* vs = reinterpret_cast<float*>(rec + KC + VC + KM + g * 256);
+      if (gl < TPLV) {
+        vs[t0 + kk] = gp.scale;
+        vs[32 + t0 + kk] = gp.zero;
+        vrcp[g][t0 + kk] = gp.rcp;
+      }
+      wave_lds_sync();
+      // scales stay in LDS: only the rare exact path reads them
+      float zero[TPLV], rcp[TPLV];
+      if (TPLV == 4) {
+        const float4 z = *reinterpret_cast<const float4*>(vs + 32 + t0);
+        const float4 r = *reinterpret_cast<const float4*>(&vrcp[g][t0]);
+        zero[0] = z.x; zero[1] = z.y; zero[TPLV - 2] = z.z; zero[TPLV - 1] = z.w;
+        rcp[0] = r.x; rcp[1] = r.y; rcp[TPLV - 2] = r.z; rcp[TPLV - 1] = r.w;
+      } else {
+        const float2 z = *reinterpret_cast<const float2*>(vs + 32 + t0);
+        const float2 r = *reinterpret_cast<const float2*>(&vrcp[g][t0]);
+        zero[0] = z.x; zero[TPLV - 1] = z.y;
+        rcp[0] = r.x; rcp[TPLV - 1] = r.y;
+      }
+      // The lane's TPLV consecutive tokens land next to each other in one code
+      // word of each channel: token t goes to
+      //   mm = t / 16, hh = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2)
+      //   4-bit: word 2*mm + hh, bits 4e;  2-bit: word hh, bits 2*(8*mm + e)
+      // bits[c] holds the lane's codes of channel c from bit 0 on.
+      // 4-bit: tokens k = 0, 2 go to bytes 0, 1 of pe and k = 1, 3 to those
+      // of po (v_cvt_pk_u8_f32), so pe | po << 4 has token k at bits 4k
+      uint32_t pe[8], po[8];
+  #pragma unroll
+      for (int c = 0; c < 8; ++c) bits[c] = pe[c] = po[c] = 0u;
+  #pragma unroll
+      for (int k = 0; k < TPLV; ++k) {
+  #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float d = x[k][c] - zero[k];
+          const float y = d * rcp[k];
+          float r = rintf(y);
+          if (fabsf(y - r) >= kNearHalf) r = exact_code(d, vs[t0 + k], LEV);   // rare: near a boundary
+          if (VB == 4) {
+            if (k & 1) po[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, po[c]);
+            else       pe[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, pe[c]);
+          } else {
+            bits[c] |= (uint32_t)r << (VB * k);
+          }
         }
       }
-    }
-    if (VB == 4) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) bits[c] = pe[c] | (po[c] << 4);
-    }
-    if (__any(gp.bad)) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint32_t b = 0;
-#pragma unroll
-        for (int k = 0; k < TPLV; ++k) b |= (uint32_t)exact_code(x[k][c] - zero[k], vs[t0 + k], LEV) << (VB * k);
-        bits[c] = b;
+      if (VB == 4) {
+  #pragma unroll
+        for (int c = 0; c < 8; ++c) bits[c] = pe[c] | (po[c] << 4);
+      }
+      if (__any(gp.bad)) {
+  #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          uint32_t b = 0;
+  #pragma unroll
+          for (int k = 0; k < TPLV; ++k) b |= (uint32_t)exact_code(x[k][c] - zero[k], vs[t0 + k], LEV) << (VB * k);
+          bits[c] = b;
+        }
       }
     }
     const int mm = t0 / 16, hh = (t0 / 4) % 2;
@@ -670,26 +736,30 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
 // Persistent grid: as many workgroups as the device holds at once (the
 // kernel's occupancy per CU times the CU count), spread over the kv heads;
 // each workgroup loops over its share of the slots.
-template <int KB, int VB, int D, bool F32IN, bool ROT>
+template <int KB, int VB, int D, bool F32IN, bool ROT, bool MX>
 hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s) {
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN, ROT>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN, ROT, MX>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
     return n;
   }();
   const int per_head = std::max(1, per_cu * a.num_cus / std::max(1, a.hkv));
   dim3 grid(std::min(ntasks, per_head), a.hkv);
-  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT>), grid, dim3(256), 0, s, a, ntasks);
+  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT, MX>), grid, dim3(256), 0, s, a, ntasks);
   return hipGetLastError();
 }
 
 template <int KB, int VB, int D>
 hipError_t launch_d(const CommitArgs& a, int ntasks, bool f32, hipStream_t s) {
+  if constexpr (KB == 4 && VB == 4) {
+    if (a.mx)
+      return f32 ? launch_t<KB, VB, D, true, false, true>(a, ntasks, s) : launch_t<KB, VB, D, false, false, true>(a, ntasks, s);
+  }
   if (a.rot.block != 0)
-    return f32 ? launch_t<KB, VB, D, true, true>(a, ntasks, s) : launch_t<KB, VB, D, false, true>(a, ntasks, s);
-  return f32 ? launch_t<KB, VB, D, true, false>(a, ntasks, s) : launch_t<KB, VB, D, false, false>(a, ntasks, s);
+    return f32 ? launch_t<KB, VB, D, true, true, false>(a, ntasks, s) : launch_t<KB, VB, D, false, true, false>(a, ntasks, s);
+  return f32 ? launch_t<KB, VB, D, true, false, false>(a, ntasks, s) : launch_t<KB, VB, D, false, false, false>(a, ntasks, s);
 }
 
 template <int KB, int VB>

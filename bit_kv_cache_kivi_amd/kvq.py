@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EHIP = range(5)
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_PREFIX, KVQ_SUFFIX = 0, 1
+KVQ_FMT_INT, KVQ_FMT_MXFP4 = 0, 1
 SLOT = 32
 
 
@@ -25,7 +26,7 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "batch", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group_tokens",
         "v_group_channels", "prefix_slots", "suffix_slots", "prefix_protected",
-        "suffix_protected", "max_q_heads", "max_splits", "v_rotation_block", "protect_sink")]
+        "suffix_protected", "max_q_heads", "max_splits", "v_rotation_block", "protect_sink", "kv_format")]
 
 
 class KvqLayout(ctypes.Structure):
@@ -104,11 +105,11 @@ def _int_array(vals):
 
 def make_config(batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128, prefix_slots=1,
                 suffix_slots=0, prefix_protected=0, suffix_protected=0, max_q_heads=None, max_splits=0,
-                v_rotation_block=0, protect_sink=0):
+                v_rotation_block=0, protect_sink=0, kv_format=0):
     return KvqConfig(batch, num_kv_heads, head_dim, k_bits, v_bits, SLOT, v_group, prefix_slots,
                      suffix_slots, prefix_protected, suffix_protected,
                      max_q_heads if max_q_heads is not None else num_kv_heads, max_splits, v_rotation_block,
-                     int(bool(protect_sink)))
+                     int(bool(protect_sink)), int(kv_format))
 
 
 def get_layout(cfg: KvqConfig) -> dict:
@@ -141,12 +142,13 @@ class KVCache:
 
     def __init__(self, batch, num_kv_heads, head_dim, k_bits=4, v_bits=4, v_group=128,
                  prefix_tokens=32, suffix_tokens=0, prefix_protected=0, suffix_protected=0,
-                 max_q_heads=None, max_splits=0, v_rotation_block=0, protect_sink=False, device="cuda"):
+                 max_q_heads=None, max_splits=0, v_rotation_block=0, protect_sink=False, kv_format=0,
+                 device="cuda"):
         import torch
         self.cfg = make_config(batch, num_kv_heads, head_dim, k_bits, v_bits, v_group,
                                -(-prefix_tokens // SLOT), -(-suffix_tokens // SLOT),
                                prefix_protected, suffix_protected, max_q_heads, max_splits,
-                               v_rotation_block, protect_sink)
+                               v_rotation_block, protect_sink, kv_format)
         self.layout = get_layout(self.cfg)
         nbytes = self.layout["total_bytes"]
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -100,6 +100,22 @@
  *   bf16 rows at prot_rows_offset[seg] + ((b * Hkv + h) * prot_cap[seg] + r) * D * 2
  *   int32 position at prot_pos_offset[seg] + (b * prot_cap[seg] + r) * 4
  * A protected token's row in slot s is rank prot_base + popcount(prot_mask & ((1<<t)-1)).
+ *
+ * MX FP4 records (kv_format = KVQ_FMT_MXFP4; k_bits = v_bits = 4, G_v = 32,
+ * no value rotation, no selection).  A hardware-native 4-bit floating-point
+ * format with per-block scales (SoloQ abstract and summary page: NVFP4; here
+ * the OCP microscaling FP4 that gfx950 converts natively):
+ *   codes: E2M1 (sign << 3 | index into {0, .5, 1, 1.5, 2, 3, 4, 6}) at the
+ *          4-bit positions of Kc and Vc above;
+ *   Kmeta at kmeta_offset: one E8M0 byte s per key channel (D bytes);
+ *   Vmeta at vmeta_offset: per 32-channel group g, one byte per token (32 bytes);
+ *   record_bytes = (32*D + 2*D) rounded up to a multiple of 256.
+ * A group (key: one channel over the slot's valid, unprotected tokens; value: 32
+ * channels of a valid token) with largest magnitude amax gets
+ *   s = max(E(amax) - 2, 0), E(amax) the biased exponent field of amax in fp32,
+ *   code = E2M1 round-to-nearest-even (saturating at 6) of x * 2^(127 - s),
+ *   sign from the sign bit of x; a group with amax = 0 (or no member) has s = 0
+ *   and codes 0.  Dequantized value: e2m1(code) * 2^(s - 127).
  */
 #ifndef KVQ_H_
 #define KVQ_H_
@@ -111,7 +127,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 #define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
 #define KVQ_MAX_BATCH 256
 
@@ -146,7 +162,11 @@ typedef struct {
                              /* counted against prefix_protected (SoloQ summary page, */
                              /* paragraph on keeping the attention sink in full       */
                              /* precision, which matters at 2-bit KV)                 */
+  int32_t kv_format;         /* KVQ_FMT_INT (0): the asymmetric integer codes above;   */
+                             /* KVQ_FMT_MXFP4 (1): see "MX FP4 records" below          */
 } kvq_config;
+
+enum { KVQ_FMT_INT = 0, KVQ_FMT_MXFP4 = 1 };
 
 typedef struct {
   uint64_t total_bytes;          /* == kvq_required_bytes                          */

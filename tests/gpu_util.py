@@ -39,6 +39,10 @@ def compare_commit(cache, ora: O.OracleCache, segment: int, B: int):
         got = cache.records(segment, b).cpu().numpy()
         want = ora.records(segment, b)
         assert got.shape == want.shape, (got.shape, want.shape)
+        if not np.array_equal(got, want) and getattr(ora, "fmt", "int") != "int":
+            bad = np.argwhere(got != want)
+            raise AssertionError(f"segment {segment} seq {b}: {len(bad)} record bytes differ, first at "
+                                 f"(slot, head, byte) {tuple(bad[0])}: gpu {got[tuple(bad[0])]} oracle {want[tuple(bad[0])]}")
         if not np.array_equal(got, want):
             gu = O.unpack_record(got, D, kb, vb, gv)
             wu = O.unpack_record(want, D, kb, vb, gv)

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(kvq):
     lib = ctypes.CDLL(SO)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
-    assert kvq.lib.kvq_abi_version() == 3
+    assert kvq.lib.kvq_abi_version() == 4
 
 
 def test_layout_matches_documented_record(kvq):
@@ -71,7 +71,7 @@ def test_layout_matches_documented_record(kvq):
     ("k_group_tokens", 64, 2), ("v_group_channels", 48, 2), ("v_group_channels", 256, 2),
     ("prefix_slots", 0, 1), ("suffix_slots", -1, 1), ("max_q_heads", 3, 1), ("max_q_heads", 36, 2),
     ("max_splits", 1000, 1), ("prefix_protected", -1, 1), ("v_rotation_block", 32, 2),
-    ("v_rotation_block", -16, 2)])
+    ("v_rotation_block", -16, 2), ("kv_format", 2, 2), ("kv_format", 1, 2)])
 def test_bad_configs(kvq, field, value, status):
     cfg = kvq.make_config(2, 4, 128, 4, 4, 64, prefix_slots=8, max_q_heads=8)
     setattr(cfg, field, value)
@@ -222,3 +222,21 @@ def test_sink_protection_counts_against_capacity(kvq):
     # sequence 0 lists 2 positions (not 0): with the sink that is 3 > 2
     assert kvq.lib.kvq_commit(h, 0, 0, k, k, 1, 40, None, I(0, 2, 3), I(5, 9, 0), None) == 3
     kvq.lib.kvq_destroy(h)
+
+
+def test_mxfp4_layout_and_configs(kvq):
+    """MX FP4 records: sizes and offsets as documented (and as the oracle packs
+    them); the format needs 4-bit codes, 32-channel value groups, no rotation."""
+    from oracle.mxfp4 import record_layout_mx
+    for D in (64, 128):
+        cfg = kvq.make_config(2, 2, D, 4, 4, 32, prefix_slots=4, max_q_heads=2, kv_format=1)
+        L = kvq.get_layout(cfg)
+        ref = record_layout_mx(D)
+        for key in ("record_bytes", "kc_offset", "vc_offset", "kmeta_offset", "vmeta_offset"):
+            assert L[key] == ref[key], (D, key)
+    for kw in (dict(k_bits=2), dict(v_bits=2), dict(v_group=64), dict(v_rotation_block=16)):
+        args = dict(k_bits=4, v_bits=4, v_group=32, v_rotation_block=0)
+        args.update(kw)
+        cfg = kvq.make_config(2, 2, 128, args["k_bits"], args["v_bits"], args["v_group"], prefix_slots=4,
+                              max_q_heads=2, v_rotation_block=args["v_rotation_block"], kv_format=1)
+        assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0, kw
