@@ -21,6 +21,9 @@ Readings where the pages are silent (each listed in the design notes):
   * a suffix segment is replaced wholesale when it is reset;
   * with a value rotation set (oracle/rotation.py), every committed value row
     is rotated before it is quantized, and the cache holds rotated values;
+  * fp16 metadata (an engineering variant of the same quantizer): the fp32
+    scale and zero are rounded to fp16 and the codes are taken against the
+    rounded pair (oracle/quant.py, asym_quantize_h16);
   * attention-sink protection (SoloQ summary page, paragraph on keeping the
     attention sink in full precision: barely matters at 4-bit KV, matters at
     2-bit), when enabled, protects the first token of every sequence's prefix,
@@ -33,8 +36,8 @@ from typing import List, Optional
 
 import numpy as np
 
-from .layout import SLOT, pack_record, pack_header, record_layout
-from .quant import asym_quantize, dequantize, to_bf16_f32
+from .layout import SLOT, pack_record, pack_header, record_layout, record_layout_h16
+from .quant import asym_quantize, asym_quantize_h16, dequantize, to_bf16_f32
 from .rotation import rotate_f32
 from .mxfp4 import mx_quantize, mx_dequantize, record_layout_mx
 
@@ -57,18 +60,21 @@ class OracleCache:
         """v_rot: None, or (perm, mix, block) of the K-RPBH value rotation.
         protect_sink: a prefix commit that starts a sequence also protects its
         first token (attention-sink protection).
-        fmt: "int" (asymmetric integer codes) or "mxfp4" (oracle/mxfp4.py; 4-bit,
-        value groups of 32 channels)."""
+        fmt: "int" (asymmetric integer codes), "int_h16" (the same with fp16
+        scales and zeros) or "mxfp4" (oracle/mxfp4.py; 4-bit, value groups of
+        32 channels)."""
         self.protect_sink = protect_sink
         self.fmt = fmt
-        assert fmt in ("int", "mxfp4")
-        assert fmt == "int" or (k_bits == 4 and v_bits == 4 and v_group == 32)
+        assert fmt in ("int", "int_h16", "mxfp4")
+        assert fmt != "mxfp4" or (k_bits == 4 and v_bits == 4 and v_group == 32)
         assert D % v_group == 0
         self.v_rot = v_rot
         self.B, self.Hkv, self.D = B, Hkv, D
         self.kb, self.vb, self.gv = k_bits, v_bits, v_group
         if fmt == "mxfp4":
             self.layout = record_layout_mx(D)
+        elif fmt == "int_h16":
+            self.layout = record_layout_h16(D, k_bits, v_bits, v_group)
         else:
             self.layout = record_layout(D, k_bits, v_bits, v_group) if k_bits <= 4 and v_bits <= 4 else None
         self.seg = {0: [_SeqSeg() for _ in range(B)], 1: [_SeqSeg() for _ in range(B)]}
@@ -116,6 +122,8 @@ class OracleCache:
         if self.fmt == "mxfp4":
             kc, ks = mx_quantize(np.ascontiguousarray(k4), kmem)            # ks: scale bytes [ns, Hkv, D]
             kz = None
+        elif self.fmt == "int_h16":
+            kc, ks, kz = asym_quantize_h16(np.ascontiguousarray(k4), self.kb, kmem)
         else:
             kc, ks, kz = asym_quantize(np.ascontiguousarray(k4), self.kb, kmem)
         kcodes = kc.transpose(0, 1, 3, 2)                                   # [ns, Hkv, 32, D]
@@ -125,6 +133,8 @@ class OracleCache:
         if self.fmt == "mxfp4":
             vc, vs = mx_quantize(np.ascontiguousarray(v5), vmem)            # vs: [ns, Hkv, 32, G]
             vz = None
+        elif self.fmt == "int_h16":
+            vc, vs, vz = asym_quantize_h16(np.ascontiguousarray(v5), self.vb, vmem)
         else:
             vc, vs, vz = asym_quantize(np.ascontiguousarray(v5), self.vb, vmem)
         vcodes = vc.reshape(ns, Hkv, SLOT, D).transpose(0, 1, 3, 2)          # [ns, Hkv, D, 32]
@@ -136,6 +146,8 @@ class OracleCache:
         records = None
         if self.fmt == "mxfp4":
             records = self._pack_mx(kcodes, vcodes, ks, vscale)
+        elif self.fmt == "int_h16":
+            records = self._pack_h16(kcodes, vcodes, ks, kz, vscale, vzero)
         elif self.kb in (2, 4) and self.vb in (2, 4):
             records = pack_record(kcodes, vcodes, ks, kz, vscale, vzero, self.kb, self.vb, self.gv)
         headers = []
@@ -171,6 +183,23 @@ class OracleCache:
         put(lay["vc_offset"], np.swapaxes(pack_v_words(vcodes, 4), -1, -2).astype("<u4"))
         put(lay["kmeta_offset"], np.asarray(kscale, np.uint8))                  # [.., D]
         put(lay["vmeta_offset"], np.asarray(vscale, np.uint8))                  # [.., G, 32]
+        return out.reshape(lead + (lay["record_bytes"],))
+
+    def _pack_h16(self, kcodes, vcodes, kscale, kzero, vscale, vzero):
+        """Integer codes in their usual layout; scales and zeros as fp16."""
+        from .layout import pack_k_words, pack_v_words
+        lay = self.layout
+        lead = kcodes.shape[:-2]
+        n = int(np.prod(lead, dtype=np.int64))
+        out = np.zeros((n, lay["record_bytes"]), np.uint8)
+
+        def put(off, arr):
+            b = np.ascontiguousarray(arr).reshape(n, -1).view(np.uint8)
+            out[:, off:off + b.shape[1]] = b
+        put(lay["kc_offset"], np.swapaxes(pack_k_words(kcodes, self.kb), -1, -2).astype("<u4"))
+        put(lay["vc_offset"], np.swapaxes(pack_v_words(vcodes, self.vb), -1, -2).astype("<u4"))
+        put(lay["kmeta_offset"], np.concatenate([np.asarray(kscale, "<f2"), np.asarray(kzero, "<f2")], axis=-1))
+        put(lay["vmeta_offset"], np.stack([np.asarray(vscale, "<f2"), np.asarray(vzero, "<f2")], axis=-2))
         return out.reshape(lead + (lay["record_bytes"],))
 
     # ------------------------------------------------------------------ views

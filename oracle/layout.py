@@ -44,6 +44,17 @@ def record_layout(D: int, kb: int, vb: int, gv: int) -> dict:
     }
 
 
+def record_layout_h16(D: int, kb: int, vb: int, gv: int) -> dict:
+    """Integer-code records with fp16 metadata: Kmeta = fp16 scale[D], zero[D];
+    Vmeta = per channel group fp16 scale[32 tokens], zero[32 tokens]."""
+    kc = SLOT * D * kb // 8
+    vc = D * vb * 4
+    km = 2 * D * 2
+    vm = (D // gv) * 2 * SLOT * 2
+    return dict(kc_offset=0, vc_offset=kc, kmeta_offset=kc + vc, vmeta_offset=kc + vc + km,
+                record_bytes=(kc + vc + km + vm + 255) // 256 * 256)
+
+
 def v_token_position(t: int, vb: int):
     """(word, first bit) of token t inside a V channel row of vb u32 words."""
     mm = t // 16

@@ -60,6 +60,27 @@ def asym_quantize(x: np.ndarray, bits: int, member: np.ndarray | None = None):
     return code.astype(np.uint16), scale.astype(F32), zero.astype(F32)
 
 
+def asym_quantize_h16(x: np.ndarray, bits: int, member: np.ndarray | None = None):
+    """asym_quantize with fp16 metadata: the fp32 scale and zero above are
+    rounded to fp16 (nearest, ties to even), and the codes are taken against the
+    rounded pair, so that code * scale16 + zero16 is the stored reconstruction:
+        code = scale16 == 0 ? 0 : clamp(rint(fl(fl(x - zero16) / scale16)), 0, 2^b - 1)
+    Returns (codes uint16, scale16, zero16) with the fp16 values as float32."""
+    x = np.asarray(x, F32)
+    if member is None:
+        member = np.ones(x.shape, dtype=bool)
+    member = np.asarray(member, dtype=bool)
+    _, s32, z32 = asym_quantize(x, bits, member)
+    s16 = s32.astype(np.float16).astype(F32) + F32(0)
+    z16 = z32.astype(np.float16).astype(F32) + F32(0)
+    levels = F32(2 ** bits - 1)
+    safe = np.where(s16 == 0, F32(1), s16)[..., None]
+    q = ((x - z16[..., None]).astype(F32) / safe).astype(F32)
+    code = np.clip(np.rint(q), F32(0), levels)
+    code = np.where(member & (s16[..., None] != 0), code, F32(0))
+    return code.astype(np.uint16), s16.astype(F32), z16.astype(F32)
+
+
 def dequantize(code: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
     """x_hat = code * scale + zero, evaluated exactly in fp64.
 
