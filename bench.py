@@ -125,8 +125,9 @@ def main():
                          "attention over the selection")
     ap.add_argument("--select-granularity", type=int, default=1, choices=(1, 32),
                     help="rank single entries (1) or whole 32-token units (32; the budget then counts units)")
-    ap.add_argument("--kv-format", default="int", choices=("int", "mxfp4"),
-                    help="cache format: asymmetric integer codes, or MX FP4 (4-bit, 32-channel value groups)")
+    ap.add_argument("--kv-format", default="int", choices=("int", "int_h16", "mxfp4"),
+                    help="cache format: asymmetric integer codes (fp32 or fp16 scales and zeros), or MX FP4 "
+                         "(4-bit, 32-channel value groups)")
     ap.add_argument("--v-rotation", type=int, default=0, choices=(0, 16, 64),
                     help="store values K-RPBH rotated with this Hadamard block (0: plain values)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -180,7 +181,8 @@ def main():
                                   suffix_tokens=c.suffix, prefix_protected=prot_cap,
                                   suffix_protected=sprot_cap if c.suffix else 0, max_q_heads=c.Hq,
                                   v_rotation_block=args.v_rotation,
-                                  kv_format=kvq.KVQ_FMT_MXFP4 if args.kv_format == "mxfp4" else kvq.KVQ_FMT_INT))
+                                  kv_format={"int": kvq.KVQ_FMT_INT, "int_h16": kvq.KVQ_FMT_INT_H16,
+                                             "mxfp4": kvq.KVQ_FMT_MXFP4}[args.kv_format]))
         if args.v_rotation:
             caches[-1].set_v_rotation(*W.krpbh_params(c.D, args.v_rotation))
     torch.cuda.synchronize()

@@ -76,16 +76,20 @@ struct Shape {
 // channel and per (value group of 32 channels, token); the hardware converts
 // the codes to fp16 exactly and a packed fp16 multiply applies the power-of-two
 // scales, so the keys need no lo part (it is stored as zero).
-template <int KB, int VB, int D, int NC, bool CEN, bool MX>
+// H16 (integer codes with fp16 scales and zeros): the producers read the
+// half-width metadata and widen it to fp32 before the same fused multiply-add.
+template <int KB, int VB, int D, int NC, bool CEN, int FMT>
 __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const AttnArgs a) {
   using S = Shape<D>;
   constexpr int KS = S::KS, CT = S::CT, GPT = S::GPT, VPT = S::VPT, RPT = S::RPT;
   constexpr int NPT = kProducerThreads;
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
-  constexpr uint32_t KM = MX ? D : kmeta_bytes(D);
+  constexpr bool MX = FMT == 1, H16 = FMT == 2;
+  constexpr uint32_t KM = MX ? D : H16 ? kmeta_bytes(D) / 2 : kmeta_bytes(D);
   static_assert(record_bytes(D, KB, VB, 32) <= 48 * D, "record fits a stage");
   static_assert(!MX || (KB == 4 && VB == 4), "MX FP4 codes are 4-bit");
+  static_assert(!(H16 && CEN), "fp16 metadata is not combined with rotated values");
 
   __shared__ __align__(16) uint8_t rawbuf[2][S::STAGE];      // packed slot records / the block
   __shared__ __align__(16) uint4 prtbuf[2][GPT][NPT];        // a producer thread's protected-row chunks
@@ -298,7 +302,10 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   auto klo_part = [&](int kb, int cg, int t) __attribute__((always_inline)) -> uint2& {
     return reinterpret_cast<uint2*>(&klo[kb][cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1];
   };
-  struct DqIn { uint32_t kw[GPT]; uint4 kp[GPT]; float4 ks[2], kz[2]; uint32_t vw[VPT]; float4 vs[2], vz[2]; uint2 kb8, vb8; };
+  struct DqIn {
+    uint32_t kw[GPT]; uint4 kp[GPT]; float4 ks[2], kz[2]; uint32_t vw[VPT]; float4 vs[2], vz[2]; uint2 kb8, vb8;
+    uint4 ksh, kzh; uint2 vsh[2], vzh[2];   // fp16 metadata
+  };
   auto dq_fetch = [&](int q, DqIn& d) __attribute__((always_inline)) {
     const uint8_t* rawS = rawbuf[q & 1];
     const uint32_t* words = reinterpret_cast<const uint32_t*>(rawS);
@@ -306,6 +313,10 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     // (4-bit) or half kcg % 2 of word kcg / 2 (2-bit) of the token's word column.
     if constexpr (MX) {
       d.kb8 = *reinterpret_cast<const uint2*>(rawS + KC + VC + 8 * kcg);     // the 8 channels' scale bytes
+    } else if constexpr (H16) {
+      const uint8_t* kmeta = rawS + KC + VC + 16 * kcg;                      // 8 fp16 scales, then 8 zeros at +2D bytes
+      d.ksh = *reinterpret_cast<const uint4*>(kmeta);
+      d.kzh = *reinterpret_cast<const uint4*>(kmeta + 2 * D);
     } else {
       const float* kmeta = reinterpret_cast<const float*>(rawS + KC + VC) + 8 * kcg;
       d.ks[0] = *reinterpret_cast<const float4*>(kmeta);
@@ -325,6 +336,13 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       // scale bytes of tokens vta..vta+3 and vta+8..vta+11 of the channels' group
       const uint8_t* vb = rawS + KC + VC + KM + (vch[0] >> 5) * kSlot;
       d.vb8 = make_uint2(*reinterpret_cast<const uint32_t*>(vb + vta), *reinterpret_cast<const uint32_t*>(vb + vta + 8));
+    } else if constexpr (H16) {
+      // per token: 32 fp16 scales, then 32 fp16 zeros
+      const _Float16* vs = reinterpret_cast<const _Float16*>(rawS + KC + VC + KM + (vch[0] >> gv_log2) * 128);
+      d.vsh[0] = *reinterpret_cast<const uint2*>(vs + vta);
+      d.vsh[1] = *reinterpret_cast<const uint2*>(vs + vta + 8);
+      d.vzh[0] = *reinterpret_cast<const uint2*>(vs + 32 + vta);
+      d.vzh[1] = *reinterpret_cast<const uint2*>(vs + 32 + vta + 8);
     } else {
       const float* vs = reinterpret_cast<const float*>(rawS + KC + VC + KM + (vch[0] >> gv_log2) * 256);
       d.vs[0] = *reinterpret_cast<const float4*>(vs + vta);
@@ -385,8 +403,20 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         vop[vbuf][c >> 5][vmm][(c & 31) + 32 * vhh] = fp4x8(d.vw[vi], vsp);
       }
     } else if (q < nq) {
-      const float ksc[8] = {d.ks[0].x, d.ks[0].y, d.ks[0].z, d.ks[0].w, d.ks[1].x, d.ks[1].y, d.ks[1].z, d.ks[1].w};
-      const float kzr[8] = {d.kz[0].x, d.kz[0].y, d.kz[0].z, d.kz[0].w, d.kz[1].x, d.kz[1].y, d.kz[1].z, d.kz[1].w};
+      // widen two fp16 values packed in a word
+      auto h2f = [](uint32_t w, float& lo, float& hi) __attribute__((always_inline)) {
+        lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+        hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+      };
+      float ksc[8], kzr[8];
+      if constexpr (H16) {
+        h2f(d.ksh.x, ksc[0], ksc[1]); h2f(d.ksh.y, ksc[2], ksc[3]); h2f(d.ksh.z, ksc[4], ksc[5]); h2f(d.ksh.w, ksc[6], ksc[7]);
+        h2f(d.kzh.x, kzr[0], kzr[1]); h2f(d.kzh.y, kzr[2], kzr[3]); h2f(d.kzh.z, kzr[4], kzr[5]); h2f(d.kzh.w, kzr[6], kzr[7]);
+      } else {
+        const float4 a0 = d.ks[0], a1 = d.ks[1], z0 = d.kz[0], z1 = d.kz[1];
+        ksc[0] = a0.x; ksc[1] = a0.y; ksc[2] = a0.z; ksc[3] = a0.w; ksc[4] = a1.x; ksc[5] = a1.y; ksc[6] = a1.z; ksc[7] = a1.w;
+        kzr[0] = z0.x; kzr[1] = z0.y; kzr[2] = z0.z; kzr[3] = z0.w; kzr[4] = z1.x; kzr[5] = z1.y; kzr[6] = z1.z; kzr[7] = z1.w;
+      }
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
         const int t = kt0 + KTT * gi;
@@ -403,8 +433,15 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
         }
         store_hi_lo8(kop[kb][kks][t + 32 * khh], klo_part(kb, kcg, t), x, neg_one);
       }
-      const float vsc[8] = {d.vs[0].x, d.vs[0].y, d.vs[0].z, d.vs[0].w, d.vs[1].x, d.vs[1].y, d.vs[1].z, d.vs[1].w};
-      float vzr[8] = {d.vz[0].x, d.vz[0].y, d.vz[0].z, d.vz[0].w, d.vz[1].x, d.vz[1].y, d.vz[1].z, d.vz[1].w};
+      float vsc[8], vzr[8];
+      if constexpr (H16) {
+        h2f(d.vsh[0].x, vsc[0], vsc[1]); h2f(d.vsh[0].y, vsc[2], vsc[3]); h2f(d.vsh[1].x, vsc[4], vsc[5]); h2f(d.vsh[1].y, vsc[6], vsc[7]);
+        h2f(d.vzh[0].x, vzr[0], vzr[1]); h2f(d.vzh[0].y, vzr[2], vzr[3]); h2f(d.vzh[1].x, vzr[4], vzr[5]); h2f(d.vzh[1].y, vzr[6], vzr[7]);
+      } else {
+        const float4 a0 = d.vs[0], a1 = d.vs[1], z0 = d.vz[0], z1 = d.vz[1];
+        vsc[0] = a0.x; vsc[1] = a0.y; vsc[2] = a0.z; vsc[3] = a0.w; vsc[4] = a1.x; vsc[5] = a1.y; vsc[6] = a1.z; vsc[7] = a1.w;
+        vzr[0] = z0.x; vzr[1] = z0.y; vzr[2] = z0.z; vzr[3] = z0.w; vzr[4] = z1.x; vzr[5] = z1.y; vzr[6] = z1.z; vzr[7] = z1.w;
+      }
       if constexpr (CEN) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vzr[e] = -kCm * vsc[e];
@@ -944,19 +981,22 @@ hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) 
   const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
   bool done = false;
   if constexpr (KB == 4 && VB == 4) {
-    if (a.mx) {
-      if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, true>), grid, block, 0, s, a);
-      else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, true>), grid, block, 0, s, a);
+    if (a.fmt == 1) {
+      if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, 1>), grid, block, 0, s, a);
+      else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, 1>), grid, block, 0, s, a);
       done = true;
     }
   }
   if (done) {
+  } else if (a.fmt == 2) {
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, 2>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, 2>), grid, block, 0, s, a);
   } else if (a.v_centred) {
-    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, true, false>), grid, block, 0, s, a);
-    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, true, false>), grid, block, 0, s, a);
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, true, 0>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, true, 0>), grid, block, 0, s, a);
   } else {
-    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, false>), grid, block, 0, s, a);
-    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, false>), grid, block, 0, s, a);
+    if (a.r <= 4) hipLaunchKernelGGL((attn_kernel<KB, VB, D, 4, false, 0>), grid, block, 0, s, a);
+    else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, 0>), grid, block, 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;

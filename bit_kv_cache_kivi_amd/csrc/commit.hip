@@ -148,13 +148,25 @@ __device__ __forceinline__ float exact_code(float d, float scale, float lev) {
 
 constexpr float kNearHalf = 0.5f - 0x1p-17f;
 
+// fp16 metadata: scale and zero rounded to fp16 (nearest even), canonical +0,
+// and the reciprocal of the rounded scale
+__device__ __forceinline__ GroupParams to_h16(GroupParams p) {
+  p.scale = (float)(_Float16)p.scale + 0.0f;
+  p.zero = (float)(_Float16)p.zero + 0.0f;
+  p.bad = p.scale != 0.f && !(p.scale >= 0x1p-100f && p.scale <= 0x1p+100f);
+  p.rcp = p.scale == 0.f ? 0.f : __builtin_amdgcn_rcpf(p.scale);
+  return p;
+}
+
 // x of lane (lane ^ M) within each 32-lane half (ds_swizzle, bit-mask mode)
 template <int M>
 __device__ __forceinline__ float swz_xor(float x) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (M << 10)));
 }
 
-template <int KB, int VB, int D, bool F32IN, bool ROT, bool MX>
+// The record format: FMT 0 integer codes with fp32 scale and zero; 1 MX FP4;
+// 2 integer codes with fp16 scale and zero (codes against the rounded pair).
+template <int KB, int VB, int D, bool F32IN, bool ROT, int FMT>
 __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(const CommitArgs a, int ntasks) {
   constexpr int HC = D / 2;              // channels per key wave
   constexpr int NCGK = HC / 8;           // 8-channel groups per key wave
@@ -168,9 +180,12 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
   constexpr int PPR = F32IN ? 2 : 1;     // 16-byte pieces per 8-channel row piece
   constexpr uint32_t KC = kc_bytes(D, KB);
   constexpr uint32_t VC = vc_bytes(D, VB);
-  // MX FP4 records: one scale byte per key channel and per (value group, token)
-  constexpr uint32_t KM = MX ? D : kmeta_bytes(D);
-  constexpr uint32_t REC_MAX = MX ? (KC + VC + 2 * D + 255) / 256 * 256 : record_bytes(D, KB, VB, 32);
+  constexpr bool MX = FMT == 1, H16 = FMT == 2;
+  // MX FP4 records: one scale byte per key channel and per (value group, token);
+  // fp16 metadata: half the bytes of fp32 scales and zeros
+  constexpr uint32_t KM = MX ? D : H16 ? kmeta_bytes(D) / 2 : kmeta_bytes(D);
+  constexpr uint32_t REC_MAX = MX ? (KC + VC + 2 * D + 255) / 256 * 256
+                                  : H16 ? (KC + VC + KM + (D / 32) * 128 + 255) / 256 * 256 : record_bytes(D, KB, VB, 32);
   constexpr int TST = 9 * NTQK;          // padded row of the key statistics exchange
   static_assert(NTQK == 8 || NTQK == 16, "key lanes per channel group");
   static_assert(TPLK == 2 || TPLK == 4, "key tokens per lane");
@@ -180,6 +195,9 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
   __shared__ __align__(16) float kx[2][2][NCGK * TST];      // key partial min/max: [wave][min|max][cgl][channel][tq]
   __shared__ __align__(16) float krcp[D];                   // key reciprocals per channel
   __shared__ __align__(16) float vrcp[D / 32][kSlot];       // value reciprocals per (group, token)
+  // fp16 metadata: the rounded scales and zeros as fp32 for the code step
+  __shared__ __align__(16) float kmf[H16 ? 2 * D : 4];
+  __shared__ __align__(16) float vmf[H16 ? D / 32 : 1][H16 ? 2 * kSlot : 4];
   // rotation only: the value rows of each value wave, the permutation and the mix
   __shared__ __align__(16) float vrow[2][ROT ? kSlot / 2 : 1][ROT ? D : 4];
   __shared__ __align__(16) int32_t rperm[ROT ? D : 4];
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool keys = wave < 2;
   const uint32_t rbytes = a.record_bytes;
-  const uint32_t raw_end = MX ? KC + VC + 2 * D : KC + VC + KM + (uint32_t)(D >> a.gv_log2) * 256u;
+  const uint32_t raw_end = MX ? KC + VC + 2 * D : KC + VC + KM + (uint32_t)(D >> a.gv_log2) * (H16 ? 128u : 256u);
   // lane geometry: a key lane holds tokens tq*TPLK + k of channel group cg
   // (the NTQK lanes of a channel group are consecutive); a value lane holds
   // tokens t0 + k of channel group cg (the lanes of a value group are consecutive)
@@ -358,12 +376,17 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
       if (TPLK == 4) *reinterpret_cast<uint4*>(rec + (cg * 32 + t0) * 4) = make_uint4(word[0], word[1], word[TPLK - 2], word[TPLK - 1]);
       else           *reinterpret_cast<uint2*>(rec + (cg * 32 + t0) * 4) = make_uint2(word[0], word[TPLK - 1]);
     } else {
-      const GroupParams gp = group_params<KB>(gmn, gmx, true);
-      float* kscale = reinterpret_cast<float*>(rec + KC + VC);
+      const GroupParams gp = H16 ? to_h16(group_params<KB>(gmn, gmx, true)) : group_params<KB>(gmn, gmx, true);
+      float* kscale = H16 ? kmf : reinterpret_cast<float*>(rec + KC + VC);
       if (tq < 8) {
         kscale[8 * cg + ch] = gp.scale;
         kscale[D + 8 * cg + ch] = gp.zero;
         krcp[8 * cg + ch] = gp.rcp;
+        if constexpr (H16) {
+          _Float16* k16 = reinterpret_cast<_Float16*>(rec + KC + VC);
+          k16[8 * cg + ch] = (_Float16)gp.scale;
+          k16[D + 8 * cg + ch] = (_Float16)gp.zero;
+        }
       }
       wave_lds_sync();
       // scales stay in LDS: only the rare exact path reads them
@@ -389,6 +412,7 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
           const float y = d * rcp[c];
           float r = rintf(y);
           if (fabsf(y - r) >= kNearHalf) r = exact_code(d, kscale[8 * cg + c], LEV);   // rare: near a boundary
+          if constexpr (H16) r = fminf(fmaxf(r, 0.f), LEV);   // the rounded zero may lie above the minimum
           if (KB == 4) p[c & 1] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 1, p[c & 1]);
           else         p[c & 3] = __builtin_amdgcn_cvt_pk_u8_f32(r, c >> 2, p[c & 3]);
         }
@@ -579,12 +603,18 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
         for (int c = 0; c < 8; ++c) bits[c] |= ((w >> (4 * c)) & 0xFu) << (4 * k);
       }
     } else {
-      const GroupParams gp = group_params<VB>(smn, smx, t0 + kk < task.nvalid);
-      float* vs = reinterpret_cast<float*>(rec + KC + VC + KM + g * 256);
+      const GroupParams gp = H16 ? to_h16(group_params<VB>(smn, smx, t0 + kk < task.nvalid))
+                                 : group_params<VB>(smn, smx, t0 + kk < task.nvalid);
+      float* vs = H16 ? &vmf[g][0] : reinterpret_cast<float*>(rec + KC + VC + KM + g * 256);
       if (gl < TPLV) {
         vs[t0 + kk] = gp.scale;
         vs[32 + t0 + kk] = gp.zero;
         vrcp[g][t0 + kk] = gp.rcp;
+        if constexpr (H16) {
+          _Float16* v16 = reinterpret_cast<_Float16*>(rec + KC + VC + KM + g * 128);
+          v16[t0 + kk] = (_Float16)gp.scale;
+          v16[32 + t0 + kk] = (_Float16)gp.zero;
+        }
       }
       wave_lds_sync();
       // scales stay in LDS: only the rare exact path reads them
@@ -618,6 +648,7 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
           const float y = d * rcp[k];
           float r = rintf(y);
           if (fabsf(y - r) >= kNearHalf) r = exact_code(d, vs[t0 + k], LEV);   // rare: near a boundary
+          if constexpr (H16) r = fminf(fmaxf(r, 0.f), LEV);
           if (VB == 4) {
             if (k & 1) po[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, po[c]);
             else       pe[c] = __builtin_amdgcn_cvt_pk_u8_f32(r, k >> 1, pe[c]);
@@ -736,30 +767,32 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
 // Persistent grid: as many workgroups as the device holds at once (the
 // kernel's occupancy per CU times the CU count), spread over the kv heads;
 // each workgroup loops over its share of the slots.
-template <int KB, int VB, int D, bool F32IN, bool ROT, bool MX>
+template <int KB, int VB, int D, bool F32IN, bool ROT, int FMT>
 hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s) {
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN, ROT, MX>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN, ROT, FMT>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
     return n;
   }();
   const int per_head = std::max(1, per_cu * a.num_cus / std::max(1, a.hkv));
   dim3 grid(std::min(ntasks, per_head), a.hkv);
-  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT, MX>), grid, dim3(256), 0, s, a, ntasks);
+  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT, FMT>), grid, dim3(256), 0, s, a, ntasks);
   return hipGetLastError();
 }
 
 template <int KB, int VB, int D>
 hipError_t launch_d(const CommitArgs& a, int ntasks, bool f32, hipStream_t s) {
   if constexpr (KB == 4 && VB == 4) {
-    if (a.mx)
-      return f32 ? launch_t<KB, VB, D, true, false, true>(a, ntasks, s) : launch_t<KB, VB, D, false, false, true>(a, ntasks, s);
+    if (a.fmt == 1)
+      return f32 ? launch_t<KB, VB, D, true, false, 1>(a, ntasks, s) : launch_t<KB, VB, D, false, false, 1>(a, ntasks, s);
   }
+  if (a.fmt == 2)
+    return f32 ? launch_t<KB, VB, D, true, false, 2>(a, ntasks, s) : launch_t<KB, VB, D, false, false, 2>(a, ntasks, s);
   if (a.rot.block != 0)
-    return f32 ? launch_t<KB, VB, D, true, true, false>(a, ntasks, s) : launch_t<KB, VB, D, false, true, false>(a, ntasks, s);
-  return f32 ? launch_t<KB, VB, D, true, false, false>(a, ntasks, s) : launch_t<KB, VB, D, false, false, false>(a, ntasks, s);
+    return f32 ? launch_t<KB, VB, D, true, true, 0>(a, ntasks, s) : launch_t<KB, VB, D, false, true, 0>(a, ntasks, s);
+  return f32 ? launch_t<KB, VB, D, true, false, 0>(a, ntasks, s) : launch_t<KB, VB, D, false, false, 0>(a, ntasks, s);
 }
 
 template <int KB, int VB>

@@ -63,8 +63,10 @@ kvq_status check_config(const kvq_config* c) {
     return fail(KVQ_EUNSUPPORTED, "v_rotation_block %d (supported: 0, 16, 64)", c->v_rotation_block);
   if (c->v_rotation_block > c->head_dim)
     return fail(KVQ_EUNSUPPORTED, "v_rotation_block %d exceeds head_dim %d", c->v_rotation_block, c->head_dim);
-  if (c->kv_format != KVQ_FMT_INT && c->kv_format != KVQ_FMT_MXFP4)
+  if (c->kv_format != KVQ_FMT_INT && c->kv_format != KVQ_FMT_MXFP4 && c->kv_format != KVQ_FMT_INT_H16)
     return fail(KVQ_EUNSUPPORTED, "kv_format %d", c->kv_format);
+  if (c->kv_format == KVQ_FMT_INT_H16 && c->v_rotation_block != 0)
+    return fail(KVQ_EUNSUPPORTED, "fp16 metadata is not combined with value rotation");
   if (c->kv_format == KVQ_FMT_MXFP4 &&
       (c->k_bits != 4 || c->v_bits != 4 || c->v_group_channels != 32 || c->v_rotation_block != 0))
     return fail(KVQ_EUNSUPPORTED, "MX FP4 needs k_bits = v_bits = 4, v_group_channels = 32 and no value rotation");
@@ -74,13 +76,15 @@ kvq_status check_config(const kvq_config* c) {
 void compute_layout(const kvq_config* c, kvq_layout* L) {
   memset(L, 0, sizeof(*L));
   const uint64_t B = c->batch, H = c->num_kv_heads, D = c->head_dim;
-  const bool mx = c->kv_format == KVQ_FMT_MXFP4;
-  const uint64_t R = mx ? kvq::record_bytes_mx((int)D) : kvq::record_bytes((int)D, c->k_bits, c->v_bits, c->v_group_channels);
+  const bool mx = c->kv_format == KVQ_FMT_MXFP4, h16 = c->kv_format == KVQ_FMT_INT_H16;
+  const uint64_t R = mx ? kvq::record_bytes_mx((int)D)
+                   : h16 ? kvq::record_bytes_h16((int)D, c->k_bits, c->v_bits, c->v_group_channels)
+                         : kvq::record_bytes((int)D, c->k_bits, c->v_bits, c->v_group_channels);
   L->record_bytes = R;
   L->kc_offset = 0;
   L->vc_offset = kvq::kc_bytes((int)D, c->k_bits);
   L->kmeta_offset = L->vc_offset + kvq::vc_bytes((int)D, c->v_bits);
-  L->vmeta_offset = L->kmeta_offset + (mx ? D : kvq::kmeta_bytes((int)D));
+  L->vmeta_offset = L->kmeta_offset + (mx ? D : h16 ? kvq::kmeta_bytes((int)D) / 2 : kvq::kmeta_bytes((int)D));
   uint64_t off = 0;
   for (int s = 0; s < 2; ++s) {
     const uint64_t cap = s == 0 ? c->prefix_slots : c->suffix_slots;
@@ -424,7 +428,7 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     a.v = d_v;
     a.num_cus = c->num_cus;
     a.rot = c->rot;
-    a.mx = cfg.kv_format == KVQ_FMT_MXFP4;
+    a.fmt = cfg.kv_format;
     a.seg = seg_ptrs(c, segment);
     a.n_max = n_max;
     a.hkv = cfg.num_kv_heads;
@@ -554,7 +558,7 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
   a.split_units = split_units;
   a.max_splits = max_splits;
   a.use_suffix = use_suffix ? 1 : 0;
-  a.mx = cfg.kv_format == KVQ_FMT_MXFP4;
+  a.fmt = cfg.kv_format;
   if (selected) {
     a.sel_count = reinterpret_cast<const int32_t*>(c->dbuf + c->lay.sel_count_offset);
     a.sel_units = reinterpret_cast<const int32_t*>(c->dbuf + c->lay.sel_units_offset);

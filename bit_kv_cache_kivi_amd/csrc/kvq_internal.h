@@ -56,7 +56,7 @@ struct CommitArgs {
   int32_t use_inline;
   int32_t num_cus;          // compute units of the device (sizes the persistent grid)
   RotParams rot;            // values are rotated before quantization when rot.block != 0
-  int32_t mx;               // MX FP4 records (4-bit E2M1 codes, E8M0 scale bytes)
+  int32_t fmt;              // record format: 0 integer, 1 MX FP4, 2 integer with fp16 metadata
   CommitTask inline_tasks[kInlineTasks];
 };
 static_assert(sizeof(CommitArgs) <= 4096, "commit launch arguments fit the kernel-argument segment");
@@ -79,7 +79,7 @@ struct AttnArgs {
   int32_t max_splits;
   int32_t use_suffix;
   int32_t v_centred;    // values in a rotated basis: dequantized around the middle code
-  int32_t mx;           // MX FP4 records
+  int32_t fmt;          // record format: 0 integer, 1 MX FP4, 2 integer with fp16 metadata
   // selection (all null without one): per (b, kv head) the number of listed
   // units, the listed cached units, and each cached unit's selected tokens
   const int32_t* sel_count;
@@ -168,6 +168,10 @@ __host__ __device__ constexpr uint32_t record_bytes(int D, int kb, int vb, int g
 // MX FP4 records: 4-bit codes, one scale byte per key channel and per (value group, token)
 __host__ __device__ constexpr uint32_t record_bytes_mx(int D) {
   return (kc_bytes(D, 4) + vc_bytes(D, 4) + 2u * D + 255u) / 256u * 256u;
+}
+// integer codes with fp16 scales and zeros
+__host__ __device__ constexpr uint32_t record_bytes_h16(int D, int kb, int vb, int gv) {
+  return (kc_bytes(D, kb) + vc_bytes(D, vb) + kmeta_bytes(D) / 2 + vmeta_bytes(D, gv) / 2 + 255u) / 256u * 256u;
 }
 
 // Launchers (defined in the .hip files); return the launch status.

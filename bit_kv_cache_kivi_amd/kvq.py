@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EHIP = range(5)
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_PREFIX, KVQ_SUFFIX = 0, 1
-KVQ_FMT_INT, KVQ_FMT_MXFP4 = 0, 1
+KVQ_FMT_INT, KVQ_FMT_MXFP4, KVQ_FMT_INT_H16 = 0, 1, 2
 SLOT = 32
 
 

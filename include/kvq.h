@@ -116,6 +116,21 @@
  *   code = E2M1 round-to-nearest-even (saturating at 6) of x * 2^(127 - s),
  *   sign from the sign bit of x; a group with amax = 0 (or no member) has s = 0
  *   and codes 0.  Dequantized value: e2m1(code) * 2^(s - 127).
+ *
+ * fp16 metadata (kv_format = KVQ_FMT_INT_H16; no value rotation, no selection).
+ * An engineering variant of the same quantizer (the pages fix no width for
+ * the quantization constants): the integer codes above with every scale and
+ * zero stored in fp16, which halves the metadata bytes:
+ *   Kmeta at kmeta_offset: fp16 scale[D], then fp16 zero[D];
+ *   Vmeta at vmeta_offset: per channel group g (D / G_v of them, 128 bytes
+ *          apart): fp16 scale[32 tokens], then fp16 zero[32 tokens];
+ *   record_bytes = (Kc + Vc + 4*D + 128 * D / G_v) rounded up to 256.
+ * scale16 and zero16 are the fp32 scale and zero above rounded to fp16 (nearest,
+ * ties to even; -0 stored as +0), and the codes are taken against that pair:
+ *   code = scale16 == 0 ? 0 : clamp(rint((x - zero16) / scale16), 0, 2^b - 1)
+ * (fp32 subtraction and correctly rounded division), so code * scale16 + zero16
+ * is the stored reconstruction.  Group values must lie within the fp16 range
+ * (|x| <= 65504); a group whose scale or zero overflows fp16 gets unspecified codes.
  */
 #ifndef KVQ_H_
 #define KVQ_H_
@@ -127,7 +142,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 #define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
 #define KVQ_MAX_BATCH 256
 
@@ -163,10 +178,11 @@ typedef struct {
                              /* paragraph on keeping the attention sink in full       */
                              /* precision, which matters at 2-bit KV)                 */
   int32_t kv_format;         /* KVQ_FMT_INT (0): the asymmetric integer codes above;   */
-                             /* KVQ_FMT_MXFP4 (1): see "MX FP4 records" below          */
+                             /* KVQ_FMT_MXFP4 (1): see "MX FP4 records" below;         */
+                             /* KVQ_FMT_INT_H16 (2): see "fp16 metadata" below         */
 } kvq_config;
 
-enum { KVQ_FMT_INT = 0, KVQ_FMT_MXFP4 = 1 };
+enum { KVQ_FMT_INT = 0, KVQ_FMT_MXFP4 = 1, KVQ_FMT_INT_H16 = 2 };
 
 typedef struct {
   uint64_t total_bytes;          /* == kvq_required_bytes                          */

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(kvq):
     lib = ctypes.CDLL(SO)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
-    assert kvq.lib.kvq_abi_version() == 4
+    assert kvq.lib.kvq_abi_version() == 5
 
 
 def test_layout_matches_documented_record(kvq):
@@ -71,7 +71,7 @@ def test_layout_matches_documented_record(kvq):
     ("k_group_tokens", 64, 2), ("v_group_channels", 48, 2), ("v_group_channels", 256, 2),
     ("prefix_slots", 0, 1), ("suffix_slots", -1, 1), ("max_q_heads", 3, 1), ("max_q_heads", 36, 2),
     ("max_splits", 1000, 1), ("prefix_protected", -1, 1), ("v_rotation_block", 32, 2),
-    ("v_rotation_block", -16, 2), ("kv_format", 2, 2), ("kv_format", 1, 2)])
+    ("v_rotation_block", -16, 2), ("kv_format", 3, 2), ("kv_format", -1, 2), ("kv_format", 1, 2)])
 def test_bad_configs(kvq, field, value, status):
     cfg = kvq.make_config(2, 4, 128, 4, 4, 64, prefix_slots=8, max_q_heads=8)
     setattr(cfg, field, value)
@@ -240,3 +240,23 @@ def test_mxfp4_layout_and_configs(kvq):
         cfg = kvq.make_config(2, 2, 128, args["k_bits"], args["v_bits"], args["v_group"], prefix_slots=4,
                               max_q_heads=2, v_rotation_block=args["v_rotation_block"], kv_format=1)
         assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0, kw
+
+
+def test_h16_layout_and_configs(kvq):
+    """fp16-metadata records: sizes and offsets as documented (and as the oracle
+    packs them) for every bit width and value group; rotation is refused."""
+    from oracle.layout import record_layout_h16
+    for D in (64, 128):
+        for kb, vb in ((4, 4), (4, 2), (2, 4), (2, 2)):
+            for gv in (32, 64, 128):
+                if gv > D:
+                    continue
+                cfg = kvq.make_config(2, 2, D, kb, vb, gv, prefix_slots=4, max_q_heads=2, kv_format=2)
+                L = kvq.get_layout(cfg)
+                ref = record_layout_h16(D, kb, vb, gv)
+                for key in ("record_bytes", "kc_offset", "vc_offset", "kmeta_offset", "vmeta_offset"):
+                    assert L[key] == ref[key], (D, kb, vb, gv, key)
+    cfg = kvq.make_config(2, 2, 128, 4, 4, 32, prefix_slots=4, max_q_heads=2, v_rotation_block=16, kv_format=2)
+    assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0
+    cfg = kvq.make_config(2, 2, 128, 4, 4, 32, prefix_slots=4, max_q_heads=2, kv_format=3)
+    assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0
