@@ -45,8 +45,8 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "a1df617ecccb3ea1238467b5ab9361d0caa02896dcb209cea1c1443e25ac3430",
-        "kib": {"attn_kernel": {"fetch": 33527, "write": 29120},
+        "attn_source_sha256": "769bceb69f4dd72284d5741e1ca6fd076ebe4272aac43a5975d64d0755f2924d",
+        "kib": {"attn_kernel": {"fetch": 33525, "write": 29120},
                 "combine_kernel": {"fetch": 14609, "write": 1792}},
     },
 }
