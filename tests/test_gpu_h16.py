@@ -117,3 +117,6 @@ def test_h16_workload_shape():
         e, x = attention_error(out, ref, "f32")
         print(f"dream7b int_h16 split={split}: err={e:.2e}")
         assert x <= 0, e
+    # selection reads integer records with fp32 metadata only: refused before any device work
+    with pytest.raises(Exception):
+        cache.select(dev(w.q, c.dtype), dev(w.k_blk, c.dtype), 64)
