@@ -2,11 +2,14 @@
 
 One step = one denoising step of one layer for a whole batch, as a
 block-diffusion decoder runs it once per block (SoloQ summary page,
-block-diffusion paragraph; Tai et al., abstract):
-    1. kvq_commit   quantize and append the previously finished 32-token block
-                    (3 of its key rows kept in bf16),
-    2. kvq_block_attn  the current 32-token block attends to itself and to the
-                    whole quantized prefix cache.
+block-diffusion paragraph; Tai et al., abstract), made as one
+kvq_attend_commit call:
+    1. the 32-token block attends to itself and to the whole quantized
+       prefix cache,
+    2. the block is quantized and appended to the cache (3 of its key rows
+       kept in bf16); the commit kernel may start in the attention's tail.
+The same work as separate kvq_commit + kvq_block_attn calls is timed too
+(``ms_per_step_separate_calls``).
 Steps rotate over a stack of per-layer caches (28 layers, as in a Dream-7B
 model) so that every call reads its cache from HBM rather than from the
 256 MB Infinity Cache.
@@ -159,7 +162,7 @@ def main():
     w = W.make(cfg)
     c = cfg
     L = args.layers
-    total_steps = 2 * args.steps + args.warmup   # step loop + commit-only loop
+    total_steps = 3 * args.steps + args.warmup   # step loop + separate-calls step loop + commit-only loop
     commits_per_layer = -(-total_steps // L)
     nblk = 4
     blocks = [W.step_block(c, s) for s in range(nblk)]
@@ -272,18 +275,31 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # The step: one kvq_attend_commit call, the attention of a block over the
+    # cache as it is and the commit of that block (32 tokens, step_protect
+    # protected rows per sequence); the commit kernel is launched so that it
+    # may start in the attention kernel's tail.
+    def do_attend_commit(i):
+        qp, _, _, op = attn_args
+        kp_, vp_, off, idx = commit_args[i % nblk]
+        kvq.check(lib.kvq_attend_commit(caches[i % L].handle, 1 if c.suffix else 0, qp, c.Hq, dtc, kp_, vp_, dtc,
+                                        32, scale, op, kvq.KVQ_BF16, None, off, idx, sptr))
+        commits[i % L] += 1
+
     for i in range(args.warmup):
-        do_commit(i)
-        do_attn(i)
+        do_attend_commit(i)
     torch.cuda.synchronize()
 
-    # (1) the step: commit the finished block, then attend
-    def step(i):
+    # (1) the step
+    t0 = time.perf_counter()
+    ms_per_step = timed(do_attend_commit, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+
+    # (1b) the same work as separate calls: commit the finished block, then attend
+    def step_separate(i):
         do_commit(i)
         do_attn(i)
-    t0 = time.perf_counter()
-    ms_per_step = timed(step, args.steps, args.warmup)
-    wall = time.perf_counter() - t0
+    ms_per_step_separate = timed(step_separate, args.steps, 0)
 
     # (2) attention alone (one launch = attention kernel + split combine), same rotation
     a_bytes = a_flops = 0.0
@@ -299,7 +315,8 @@ def main():
     commit_ms = timed(do_commit, args.steps, 0)
     commit_bytes = commit_algorithmic(c, [32] * c.B, c.step_protect * c.B, R)
 
-    # (4) optional: selection of the top K entries per (sequence, kv head), then
+
+    # (5) optional: selection of the top K entries per (sequence, kv head), then
     # attention over the selection (the block's mask queries = all 32 tokens)
     sel = None
     if args.select_budget:
@@ -351,6 +368,7 @@ def main():
                    "v_rotation_block": args.v_rotation, "kv_format": args.kv_format, "parallelism": "none"},
         "attn_ms": attn_ms,
         "commit_ms": commit_ms,
+        "ms_per_step_separate_calls": ms_per_step_separate,
         "attn_query_tokens_per_s": qtok / attn_s,
         "attn_hbm_gbs": achieved_gbs,
         "attn_tflops": achieved_tflops,

@@ -304,9 +304,23 @@ kvq_status kvq_set_split_slots(kvq_cache* c, int32_t slots_per_split) {
   return KVQ_OK;
 }
 
-kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, const void* d_k, const void* d_v,
-                      int32_t in_dtype, int32_t n_max, const int32_t* h_ntok, const int32_t* h_prot_off,
-                      const int32_t* h_prot_idx, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// A validated commit: the task table is in c->tasks; ntok and nprot_add are
+// what the host mirror gains once the commit is launched.
+struct CommitPlan {
+  int segment = 0, reset = 0, in_dtype = 0, n_max = 0;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  std::vector<int32_t> ntok, nprot_add;
+};
+
+// Every check of a commit, and its task table; no device work, no change to the mirror.
+kvq_status commit_plan(kvq_cache* c, int32_t segment, int32_t reset_segment, const void* d_k, const void* d_v,
+                       int32_t in_dtype, int32_t n_max, const int32_t* h_ntok, const int32_t* h_prot_off,
+                       const int32_t* h_prot_idx, CommitPlan& plan) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch;
@@ -400,11 +414,32 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
       tasks.push_back(t);
     }
   }
+  plan.segment = segment;
+  plan.reset = reset_segment;
+  plan.in_dtype = in_dtype;
+  plan.n_max = n_max;
+  plan.k = d_k;
+  plan.v = d_v;
+  plan.ntok = ntok;
+  plan.nprot_add.assign(B, 0);
+  for (int b = 0; b < B; ++b) plan.nprot_add[b] = h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
+  return KVQ_OK;
+}
 
+// Launches a planned commit on st and updates the host mirror.  any_order:
+// the kernel may start before the stream's previous kernel has finished.
+kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st, bool any_order = false) {
+  const kvq_config& cfg = c->cfg;
+  const int B = cfg.batch;
+  const int segment = plan.segment, reset_segment = plan.reset, in_dtype = plan.in_dtype, n_max = plan.n_max;
+  const void* d_k = plan.k;
+  const void* d_v = plan.v;
+  const std::vector<int32_t>& ntok = plan.ntok;
+  SegMirror& m = c->seg[segment];
+  auto& tasks = c->tasks;
   if (!tasks.empty()) {
     kvq_status s = ensure_hip(c);
     if (s != KVQ_OK) return s;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     kvq::CommitArgs a;          // about 2 KB with the inline task table; the launch copies it
     memset(&a, 0, sizeof(a));
     hipError_t e = hipSuccess;
@@ -434,7 +469,8 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     a.hkv = cfg.num_kv_heads;
     a.gv_log2 = ilog2(cfg.v_group_channels);
     a.record_bytes = (uint32_t)c->lay.record_bytes;
-    e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st);
+    e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st,
+                           any_order);
     if (e != hipSuccess) return fail(KVQ_EHIP, "commit launch: %s", hipGetErrorString(e));
     if (!a.use_inline) {
       const int k = c->next_stage;
@@ -451,9 +487,22 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
     if (reset_segment) { m.ntok[b] = 0; m.nslots[b] = 0; m.nprot[b] = 0; }
     m.ntok[b] += ntok[b];
     m.nslots[b] += (ntok[b] + kvq::kSlot - 1) / kvq::kSlot;
-    m.nprot[b] += h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
+    m.nprot[b] += plan.nprot_add[b];
   }
   return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, const void* d_k, const void* d_v,
+                      int32_t in_dtype, int32_t n_max, const int32_t* h_ntok, const int32_t* h_prot_off,
+                      const int32_t* h_prot_idx, void* stream) {
+  CommitPlan plan;
+  kvq_status s = commit_plan(c, segment, reset_segment, d_k, d_v, in_dtype, n_max, h_ntok, h_prot_off, h_prot_idx, plan);
+  if (s != KVQ_OK) return s;
+  return commit_run(c, plan, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -462,7 +511,8 @@ namespace {
 
 kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                            const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
-                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected) {
+                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected,
+                           kvq::LaunchHook between = nullptr, void* ctx = nullptr) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
@@ -611,7 +661,7 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     a.out = rot_o;
     a.out_f32 = 1;
   }
-  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st);
+  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st, between, ctx);
   if (e != hipSuccess) return fail(KVQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   if (rot_o) {
     kvq::UnrotArgs u;
@@ -644,6 +694,41 @@ kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void*
                                    void* stream) {
   return block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
                          softmax_scale, d_out, out_dtype, stream, true);
+}
+
+kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                             const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
+                             float softmax_scale, void* d_out, int32_t out_dtype, const int32_t* h_ntok,
+                             const int32_t* h_prot_off, const int32_t* h_prot_idx, void* stream) {
+  // the commit is checked before anything is launched; the attention checks
+  // its own arguments before its launch, and the commit is launched only
+  // after the attention kernel
+  CommitPlan plan;
+  kvq_status s = commit_plan(c, KVQ_PREFIX, 0, d_k_blk, d_v_blk, blk_dtype, block_len, h_ntok, h_prot_off,
+                             h_prot_idx, plan);
+  if (s != KVQ_OK) return s;
+  if (block_len != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "block_len %d (supported: 32)", block_len);
+  struct Ctx {
+    kvq_cache* c;
+    const CommitPlan* plan;
+    hipStream_t st;
+    bool ran;
+    kvq_status status;
+  } ctx{c, &plan, static_cast<hipStream_t>(stream), false, KVQ_OK};
+  // between the attention kernel and its split combine: the commit kernel,
+  // launched so that it can start in the attention kernel's tail
+  auto hook = [](void* p) -> hipError_t {
+    Ctx* x = static_cast<Ctx*>(p);
+    x->ran = true;
+    x->status = commit_run(x->c, *x->plan, x->st, true);
+    return x->status == KVQ_OK ? hipSuccess : hipErrorLaunchFailure;
+  };
+  s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
+                      softmax_scale, d_out, out_dtype, stream, false, hook, &ctx);
+  if (ctx.ran && ctx.status != KVQ_OK) return ctx.status;
+  if (s != KVQ_OK) return s;
+  if (!ctx.ran) return commit_run(c, plan, static_cast<hipStream_t>(stream));
+  return KVQ_OK;
 }
 
 kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,

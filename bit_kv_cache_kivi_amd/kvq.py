@@ -70,6 +70,9 @@ def _load():
                                  c_float, P(ctypes.c_uint32), c_int32, c_int32, c_void_p]),
         "kvq_block_attn_selected": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                               c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
+        "kvq_attend_commit": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_int32, c_int32, c_float, c_void_p, c_int32, P(c_int32), P(c_int32),
+                                        P(c_int32), c_void_p]),
         "kvq_segment_info": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_int32)]),
         "kvq_set_split_slots": (c_int32, [c_void_p, c_int32]),
         "kvq_set_v_rotation": (c_int32, [c_void_p, P(c_int32), P(c_float)]),
@@ -137,6 +140,18 @@ def _stream_ptr(stream):
     return c_void_p(s.cuda_stream)
 
 
+def _csr(protected):
+    """Per-sequence position lists -> (offsets, indices) C arrays, or (None, None)."""
+    if protected is None:
+        return None, None
+    o = [0]
+    flat = []
+    for p in protected:
+        flat.extend(int(x) for x in p)
+        o.append(len(flat))
+    return _int_array(o), (_int_array(flat) if flat else (c_int32 * 1)(0))
+
+
 class KVCache:
     """One layer's low-bit cache in a torch-owned device buffer."""
 
@@ -177,18 +192,8 @@ class KVCache:
         ntok: per-sequence token counts (default n_max); protected: per-sequence
         sorted positions, relative to this commit, of key rows kept in bf16."""
         assert k.is_contiguous() and v.is_contiguous() and k.dtype == v.dtype and k.shape == v.shape
-        B = self.cfg.batch
         nt = _int_array(ntok)
-        off = idx = None
-        if protected is not None:
-            o = [0]
-            flat = []
-            for p in protected:
-                p = [int(x) for x in p]
-                flat.extend(p)
-                o.append(len(flat))
-            off = _int_array(o)
-            idx = _int_array(flat) if flat else (c_int32 * 1)(0)
+        off, idx = _csr(protected)
         check(lib.kvq_commit(self._h, int(segment), int(bool(reset)), c_void_p(k.data_ptr()),
                              c_void_p(v.data_ptr()), _dtype_code(k), int(k.shape[1]), nt, off, idx,
                              _stream_ptr(stream)))
@@ -208,6 +213,26 @@ class KVCache:
                                  _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
                                  _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
                                  c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
+        return out
+
+    def attend_commit(self, q, k_blk, v_blk, ntok=None, protected=None, use_suffix=False, softmax_scale=None,
+                      out_dtype=None, out=None, stream=None):
+        """block_attn over the cache as it is, then commit k_blk, v_blk to the
+        prefix (ntok, protected as for commit), in one call: the commit kernel
+        may start before the attention kernel has finished."""
+        import torch
+        assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
+        assert k_blk.dtype == v_blk.dtype and k_blk.shape == v_blk.shape
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
+        off, idx = _csr(protected)
+        check(lib.kvq_attend_commit(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
+                                    _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
+                                    _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
+                                    c_void_p(out.data_ptr()), _dtype_code(out), _int_array(ntok), off, idx,
+                                    _stream_ptr(stream)))
         return out
 
     def select(self, q, k_blk, budget, use_suffix=False, query_mask=None, softmax_scale=None, granularity=1,

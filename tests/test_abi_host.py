@@ -260,3 +260,26 @@ def test_h16_layout_and_configs(kvq):
     assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0
     cfg = kvq.make_config(2, 2, 128, 4, 4, 32, prefix_slots=4, max_q_heads=2, kv_format=3)
     assert kvq.lib.kvq_required_bytes(ctypes.byref(cfg)) == 0
+
+
+def test_attend_commit_checks_before_launch(kvq):
+    """kvq_attend_commit checks the commit before anything is launched: a
+    malformed or over-capacity commit fails with the commit's status and the
+    host mirror is unchanged (no device work is needed to get there)."""
+    h = _handle(kvq)
+    I = lambda *v: (ctypes.c_int32 * len(v))(*v)   # noqa: E731
+    p = ctypes.c_void_p(1 << 33)
+    before = [(ctypes.c_int32 * 2)() for _ in range(3)]
+    kvq.lib.kvq_segment_info(h, 0, *before)
+    cases = [(dict(ntok=I(33, 1)), 1),                          # ntok > block length
+             (dict(off=I(0, 1, 1), idx=I(40)), 1),              # protected position outside the block
+             (dict(off=I(0, 5, 5), idx=I(0, 1, 2, 3, 4)), 3),   # protected capacity 4
+             (dict(L=16), 1)]                                   # ntok default 16 is fine, block_len 16 is not
+    for kw, status in cases:
+        st = kvq.lib.kvq_attend_commit(h, 0, p, 4, 1, p, p, 1, kw.get("L", 32), 0.125, p, 1,
+                                       kw.get("ntok"), kw.get("off"), kw.get("idx"), None)
+        assert st in ((status,) if kw.get("L") is None else (1, 2)), (kw, st, kvq.last_error())
+        after = [(ctypes.c_int32 * 2)() for _ in range(3)]
+        kvq.lib.kvq_segment_info(h, 0, *after)
+        assert [list(a) for a in after] == [list(b) for b in before]
+    assert kvq.lib.kvq_destroy(h) == 0

@@ -1,0 +1,75 @@
+"""GPU parity of kvq_attend_commit (attention of a block over the cache as it
+is, then the commit of that block, in one call, the commit kernel launched so
+that it may overlap the attention kernel): over several steps, every output within the attention gate of the
+oracle's attention before the commit, bit-identical to the output of separate
+kvq_block_attn + kvq_commit calls on a twin cache, and records, headers and
+protected rows bit-exact against the oracle afterwards."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from bit_kv_cache_kivi_amd import kvq  # noqa: E402
+from gpu_util import announce, attention_error, build_case, compare_commit, dev  # noqa: E402
+
+
+@pytest.mark.parametrize("name,T,B,nsteps", [
+    ("tiny", None, None, 3), ("dream7b_4bit", 300, 2, 4), ("dual_long", 400, 2, 3), ("serve_b32", 200, 6, 2)])
+def test_attend_commit_steps(name, T, B, nsteps):
+    announce("attend_commit", name, T, B, nsteps)
+    w, cache, ora = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1)
+    _, twin, _ = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1)
+    c = w.cfg
+    use_suffix = bool(c.suffix)
+    g = np.random.default_rng(5)
+    for s in range(nsteps):
+        kb, vb, prot = W.step_block(c, s)
+        q = g.standard_normal(w.q.shape).astype(np.float32)
+        if c.dtype == "bf16":
+            q = torch.from_numpy(q).to(torch.bfloat16).float().numpy()
+        ntok = [32] * c.B if s % 2 == 0 else [32 - (b % 3) * 7 for b in range(c.B)]   # ragged commits too
+        prot_s = [p[p < n] for p, n in zip(prot, ntok)]
+        ref = O.block_attention(ora, q, kb, vb, use_suffix=use_suffix)
+        dq, dk, dv = dev(q, c.dtype), dev(kb, c.dtype), dev(vb, c.dtype)
+        out = cache.attend_commit(dq, dk, dv, ntok=ntok, protected=prot_s, use_suffix=use_suffix,
+                                  out_dtype=torch.float32)
+        out2 = twin.block_attn(dq, dk, dv, use_suffix=use_suffix, out_dtype=torch.float32)
+        twin.commit(dk, dv, ntok=ntok, protected=prot_s)
+        ora.commit(0, kb, vb, ntok=ntok, prot=prot_s)
+        e, x = attention_error(out, ref, "f32")
+        print(f"{name} step {s}: err={e:.2e}")
+        assert x <= 0, (s, e)
+        assert torch.equal(out, out2), f"step {s}: attend_commit output differs from block_attn"
+    torch.cuda.synchronize()
+    compare_commit(cache, ora, 0, c.B)
+    compare_commit(twin, ora, 0, c.B)
+    for b in range(c.B):
+        assert torch.equal(cache.records(0, b), twin.records(0, b))
+
+
+def test_attend_commit_errors_leave_cache_unchanged():
+    """An attention argument error after the commit was checked: nothing runs,
+    the cache is unchanged, and a later good call still works."""
+    announce("attend_commit errors")
+    w, cache, ora = build_case(W.CONFIGS["tiny"], extra_slots=2)
+    c = w.cfg
+    kb, vb, prot = W.step_block(c, 0)
+    before = cache.segment_info(0)
+    q = dev(w.q, c.dtype)
+    bad_q = q[:, :, :c.Hkv + 1].contiguous() if c.Hq > c.Hkv else q[:, :, :1].contiguous()
+    with pytest.raises(Exception):
+        cache.attend_commit(bad_q, dev(kb, c.dtype), dev(vb, c.dtype), protected=prot)
+    assert [list(x) for x in cache.segment_info(0)] == [list(x) for x in before]
+    ref = O.block_attention(ora, w.q, kb, vb)
+    out = cache.attend_commit(q, dev(kb, c.dtype), dev(vb, c.dtype), protected=prot, out_dtype=torch.float32)
+    ora.commit(0, kb, vb, prot=prot)
+    e, x = attention_error(out, ref, "f32")
+    assert x <= 0, e
+    compare_commit(cache, ora, 0, c.B)
