@@ -2,14 +2,13 @@
 
 One step = one denoising step of one layer for a whole batch, as a
 block-diffusion decoder runs it once per block (SoloQ summary page,
-block-diffusion paragraph; Tai et al., abstract), made as one
-kvq_attend_commit call:
-    1. the 32-token block attends to itself and to the whole quantized
-       prefix cache,
-    2. the block is quantized and appended to the cache (3 of its key rows
-       kept in bf16); the commit kernel may start in the attention's tail.
-The same work as separate kvq_commit + kvq_block_attn calls is timed too
-(``ms_per_step_separate_calls``).
+block-diffusion paragraph; Tai et al., abstract):
+    1. kvq_commit   quantize and append the previously finished 32-token block
+                    (3 of its key rows kept in bf16),
+    2. kvq_block_attn  the current 32-token block attends to itself and to the
+                    whole quantized prefix cache.
+The same work as one kvq_attend_commit call per step is timed afterwards
+(``ms_per_step_attend_commit``).
 Steps rotate over a stack of per-layer caches (28 layers, as in a Dream-7B
 model) so that every call reads its cache from HBM rather than from the
 256 MB Infinity Cache.
@@ -162,8 +161,10 @@ def main():
     w = W.make(cfg)
     c = cfg
     L = args.layers
-    total_steps = 3 * args.steps + args.warmup   # step loop + separate-calls step loop + commit-only loop
-    commits_per_layer = -(-total_steps // L)
+    # commits per layer cache: the warm-up loop and three timed loops of
+    # consecutive steps (the step, the separate-calls step, commit alone),
+    # each spread round-robin over the L caches
+    commits_per_layer = -(-args.warmup // L) + 3 * -(-args.steps // L)
     nblk = 4
     blocks = [W.step_block(c, s) for s in range(nblk)]
 
@@ -275,10 +276,8 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    # The step: one kvq_attend_commit call, the attention of a block over the
-    # cache as it is and the commit of that block (32 tokens, step_protect
-    # protected rows per sequence); the commit kernel is launched so that it
-    # may start in the attention kernel's tail.
+    # The same work as one kvq_attend_commit call: the attention of a block over
+    # the cache as it is, then the commit of that block.
     def do_attend_commit(i):
         qp, _, _, op = attn_args
         kp_, vp_, off, idx = commit_args[i % nblk]
@@ -286,20 +285,20 @@ def main():
                                         32, scale, op, kvq.KVQ_BF16, None, off, idx, sptr))
         commits[i % L] += 1
 
-    for i in range(args.warmup):
-        do_attend_commit(i)
-    torch.cuda.synchronize()
-
-    # (1) the step
-    t0 = time.perf_counter()
-    ms_per_step = timed(do_attend_commit, args.steps, args.warmup)
-    wall = time.perf_counter() - t0
-
-    # (1b) the same work as separate calls: commit the finished block, then attend
-    def step_separate(i):
+    def step(i):
         do_commit(i)
         do_attn(i)
-    ms_per_step_separate = timed(step_separate, args.steps, 0)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # (1) the step: commit the finished block, then attend
+    t0 = time.perf_counter()
+    ms_per_step = timed(step, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+
+    # (1b) the same work as one kvq_attend_commit call per step
+    ms_per_step_attend_commit = timed(do_attend_commit, args.steps, 0)
 
     # (2) attention alone (one launch = attention kernel + split combine), same rotation
     a_bytes = a_flops = 0.0
@@ -368,7 +367,7 @@ def main():
                    "v_rotation_block": args.v_rotation, "kv_format": args.kv_format, "parallelism": "none"},
         "attn_ms": attn_ms,
         "commit_ms": commit_ms,
-        "ms_per_step_separate_calls": ms_per_step_separate,
+        "ms_per_step_attend_commit": ms_per_step_attend_commit,
         "attn_query_tokens_per_s": qtok / attn_s,
         "attn_hbm_gbs": achieved_gbs,
         "attn_tflops": achieved_tflops,

@@ -976,7 +976,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
 }
 
 template <int KB, int VB, int D>
-hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s, LaunchHook between, void* ctx) {
+hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
   const dim3 grid = a.num_wg ? dim3(a.num_wg) : dim3(grid_splits, a.hkv, B);
   const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
   bool done = false;
@@ -999,25 +999,24 @@ hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s, 
     else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, 0>), grid, block, 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && between) e = between(ctx);
   if (e != hipSuccess || grid_splits <= 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
-hipError_t launch_kb(const AttnArgs& a, int grid_splits, int B, int D, hipStream_t s, LaunchHook h, void* ctx) {
-  return D == 64 ? launch_kbd<KB, VB, 64>(a, grid_splits, B, s, h, ctx) : launch_kbd<KB, VB, 128>(a, grid_splits, B, s, h, ctx);
+hipError_t launch_kb(const AttnArgs& a, int grid_splits, int B, int D, hipStream_t s) {
+  return D == 64 ? launch_kbd<KB, VB, 64>(a, grid_splits, B, s) : launch_kbd<KB, VB, 128>(a, grid_splits, B, s);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
-                            hipStream_t stream, LaunchHook between, void* ctx) {
-  if (kb == 4 && vb == 4) return launch_kb<4, 4>(a, grid_splits, B, D, stream, between, ctx);
-  if (kb == 4 && vb == 2) return launch_kb<4, 2>(a, grid_splits, B, D, stream, between, ctx);
-  if (kb == 2 && vb == 4) return launch_kb<2, 4>(a, grid_splits, B, D, stream, between, ctx);
-  return launch_kb<2, 2>(a, grid_splits, B, D, stream, between, ctx);
+                            hipStream_t stream) {
+  if (kb == 4 && vb == 4) return launch_kb<4, 4>(a, grid_splits, B, D, stream);
+  if (kb == 4 && vb == 2) return launch_kb<4, 2>(a, grid_splits, B, D, stream);
+  if (kb == 2 && vb == 4) return launch_kb<2, 4>(a, grid_splits, B, D, stream);
+  return launch_kb<2, 2>(a, grid_splits, B, D, stream);
 }
 
 }  // namespace kvq

@@ -44,8 +44,6 @@
 #include <algorithm>
 #include <type_traits>
 
-#include <hip/hip_ext.h>
-
 #include "device_common.h"
 #include "kvq_internal.h"
 
@@ -770,7 +768,7 @@ __global__ __launch_bounds__(256, (F32IN || ROT) ? 3 : 4) void commit_kernel(con
 // kernel's occupancy per CU times the CU count), spread over the kv heads;
 // each workgroup loops over its share of the slots.
 template <int KB, int VB, int D, bool F32IN, bool ROT, int FMT>
-hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s, bool any_order) {
+hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s) {
   static const int per_cu = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, commit_kernel<KB, VB, D, F32IN, ROT, FMT>, 256, 0) != hipSuccess ||
@@ -780,41 +778,37 @@ hipError_t launch_t(const CommitArgs& a, int ntasks, hipStream_t s, bool any_ord
   }();
   const int per_head = std::max(1, per_cu * a.num_cus / std::max(1, a.hkv));
   dim3 grid(std::min(ntasks, per_head), a.hkv);
-  if (any_order)
-    hipExtLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT, FMT>), grid, dim3(256), 0, s, nullptr, nullptr,
-                          hipExtAnyOrderLaunch, a, ntasks);
-  else
-    hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT, FMT>), grid, dim3(256), 0, s, a, ntasks);
+  hipLaunchKernelGGL((commit_kernel<KB, VB, D, F32IN, ROT, FMT>), grid, dim3(256), 0, s, a, ntasks);
   return hipGetLastError();
 }
 
 template <int KB, int VB, int D>
-hipError_t launch_d(const CommitArgs& a, int ntasks, bool f32, hipStream_t s, bool ao) {
+hipError_t launch_d(const CommitArgs& a, int ntasks, bool f32, hipStream_t s) {
   if constexpr (KB == 4 && VB == 4) {
     if (a.fmt == 1)
-      return f32 ? launch_t<KB, VB, D, true, false, 1>(a, ntasks, s, ao) : launch_t<KB, VB, D, false, false, 1>(a, ntasks, s, ao);
+      return f32 ? launch_t<KB, VB, D, true, false, 1>(a, ntasks, s) : launch_t<KB, VB, D, false, false, 1>(a, ntasks, s);
   }
   if (a.fmt == 2)
-    return f32 ? launch_t<KB, VB, D, true, false, 2>(a, ntasks, s, ao) : launch_t<KB, VB, D, false, false, 2>(a, ntasks, s, ao);
+    return f32 ? launch_t<KB, VB, D, true, false, 2>(a, ntasks, s) : launch_t<KB, VB, D, false, false, 2>(a, ntasks, s);
   if (a.rot.block != 0)
-    return f32 ? launch_t<KB, VB, D, true, true, 0>(a, ntasks, s, ao) : launch_t<KB, VB, D, false, true, 0>(a, ntasks, s, ao);
-  return f32 ? launch_t<KB, VB, D, true, false, 0>(a, ntasks, s, ao) : launch_t<KB, VB, D, false, false, 0>(a, ntasks, s, ao);
+    return f32 ? launch_t<KB, VB, D, true, true, 0>(a, ntasks, s) : launch_t<KB, VB, D, false, true, 0>(a, ntasks, s);
+  return f32 ? launch_t<KB, VB, D, true, false, 0>(a, ntasks, s) : launch_t<KB, VB, D, false, false, 0>(a, ntasks, s);
 }
 
 template <int KB, int VB>
-hipError_t launch_b(const CommitArgs& a, int ntasks, int D, bool f32, hipStream_t s, bool ao) {
-  return D == 64 ? launch_d<KB, VB, 64>(a, ntasks, f32, s, ao) : launch_d<KB, VB, 128>(a, ntasks, f32, s, ao);
+hipError_t launch_b(const CommitArgs& a, int ntasks, int D, bool f32, hipStream_t s) {
+  return D == 64 ? launch_d<KB, VB, 64>(a, ntasks, f32, s) : launch_d<KB, VB, 128>(a, ntasks, f32, s);
 }
 
 }  // namespace
 
 hipError_t launch_commit(const CommitArgs& a, int ntasks, int D, int kb, int vb, bool f32_in,
-                         hipStream_t stream, bool any_order) {
+                         hipStream_t stream) {
   if (ntasks == 0) return hipSuccess;
-  if (kb == 4 && vb == 4) return launch_b<4, 4>(a, ntasks, D, f32_in, stream, any_order);
-  if (kb == 4 && vb == 2) return launch_b<4, 2>(a, ntasks, D, f32_in, stream, any_order);
-  if (kb == 2 && vb == 4) return launch_b<2, 4>(a, ntasks, D, f32_in, stream, any_order);
-  return launch_b<2, 2>(a, ntasks, D, f32_in, stream, any_order);
+  if (kb == 4 && vb == 4) return launch_b<4, 4>(a, ntasks, D, f32_in, stream);
+  if (kb == 4 && vb == 2) return launch_b<4, 2>(a, ntasks, D, f32_in, stream);
+  if (kb == 2 && vb == 4) return launch_b<2, 4>(a, ntasks, D, f32_in, stream);
+  return launch_b<2, 2>(a, ntasks, D, f32_in, stream);
 }
 
 }  // namespace kvq

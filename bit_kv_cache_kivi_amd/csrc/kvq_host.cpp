@@ -426,9 +426,8 @@ kvq_status commit_plan(kvq_cache* c, int32_t segment, int32_t reset_segment, con
   return KVQ_OK;
 }
 
-// Launches a planned commit on st and updates the host mirror.  any_order:
-// the kernel may start before the stream's previous kernel has finished.
-kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st, bool any_order = false) {
+// Launches a planned commit on st and updates the host mirror.
+kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch;
   const int segment = plan.segment, reset_segment = plan.reset, in_dtype = plan.in_dtype, n_max = plan.n_max;
@@ -469,8 +468,7 @@ kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st, bool
     a.hkv = cfg.num_kv_heads;
     a.gv_log2 = ilog2(cfg.v_group_channels);
     a.record_bytes = (uint32_t)c->lay.record_bytes;
-    e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st,
-                           any_order);
+    e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st);
     if (e != hipSuccess) return fail(KVQ_EHIP, "commit launch: %s", hipGetErrorString(e));
     if (!a.use_inline) {
       const int k = c->next_stage;
@@ -511,8 +509,7 @@ namespace {
 
 kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                            const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
-                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected,
-                           kvq::LaunchHook between = nullptr, void* ctx = nullptr) {
+                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
@@ -661,7 +658,7 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     a.out = rot_o;
     a.out_f32 = 1;
   }
-  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st, between, ctx);
+  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st);
   if (e != hipSuccess) return fail(KVQ_EHIP, "attention launch: %s", hipGetErrorString(e));
   if (rot_o) {
     kvq::UnrotArgs u;
@@ -701,34 +698,15 @@ kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, 
                              float softmax_scale, void* d_out, int32_t out_dtype, const int32_t* h_ntok,
                              const int32_t* h_prot_off, const int32_t* h_prot_idx, void* stream) {
   // the commit is checked before anything is launched; the attention checks
-  // its own arguments before its launch, and the commit is launched only
-  // after the attention kernel
+  // its own arguments before its launches, and reads the cache as it was
   CommitPlan plan;
   kvq_status s = commit_plan(c, KVQ_PREFIX, 0, d_k_blk, d_v_blk, blk_dtype, block_len, h_ntok, h_prot_off,
                              h_prot_idx, plan);
   if (s != KVQ_OK) return s;
-  if (block_len != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "block_len %d (supported: 32)", block_len);
-  struct Ctx {
-    kvq_cache* c;
-    const CommitPlan* plan;
-    hipStream_t st;
-    bool ran;
-    kvq_status status;
-  } ctx{c, &plan, static_cast<hipStream_t>(stream), false, KVQ_OK};
-  // between the attention kernel and its split combine: the commit kernel,
-  // launched so that it can start in the attention kernel's tail
-  auto hook = [](void* p) -> hipError_t {
-    Ctx* x = static_cast<Ctx*>(p);
-    x->ran = true;
-    x->status = commit_run(x->c, *x->plan, x->st, true);
-    return x->status == KVQ_OK ? hipSuccess : hipErrorLaunchFailure;
-  };
   s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
-                      softmax_scale, d_out, out_dtype, stream, false, hook, &ctx);
-  if (ctx.ran && ctx.status != KVQ_OK) return ctx.status;
+                      softmax_scale, d_out, out_dtype, stream, false);
   if (s != KVQ_OK) return s;
-  if (!ctx.ran) return commit_run(c, plan, static_cast<hipStream_t>(stream));
-  return KVQ_OK;
+  return commit_run(c, plan, static_cast<hipStream_t>(stream));
 }
 
 kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,

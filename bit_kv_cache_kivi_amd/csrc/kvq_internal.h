@@ -175,15 +175,10 @@ __host__ __device__ constexpr uint32_t record_bytes_h16(int D, int kb, int vb, i
 }
 
 // Launchers (defined in the .hip files); return the launch status.
-// any_order: the commit kernel is launched without waiting for the stream's
-// previous kernel to finish (work enqueued later still waits for it).
 hipError_t launch_commit(const CommitArgs& a, int ntasks, int D, int kb, int vb, bool f32_in,
-                         hipStream_t stream, bool any_order = false);
-// between (if set) is called once the attention kernel is launched and before
-// the split combine, so the caller can enqueue work that may overlap it.
-using LaunchHook = hipError_t (*)(void* ctx);
+                         hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
-                            hipStream_t stream, LaunchHook between = nullptr, void* ctx = nullptr);
+                            hipStream_t stream);
 hipError_t launch_blk_prep(const BlkPrepArgs& a, int D, hipStream_t stream);
 hipError_t launch_select(const SelArgs& a, int mode, int grid_splits, int B, int D, int kb, int vb,
                          hipStream_t stream);

@@ -218,8 +218,7 @@ class KVCache:
     def attend_commit(self, q, k_blk, v_blk, ntok=None, protected=None, use_suffix=False, softmax_scale=None,
                       out_dtype=None, out=None, stream=None):
         """block_attn over the cache as it is, then commit k_blk, v_blk to the
-        prefix (ntok, protected as for commit), in one call: the commit kernel
-        may start before the attention kernel has finished."""
+        prefix (ntok, protected as for commit), in one call."""
         import torch
         assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
         assert k_blk.dtype == v_blk.dtype and k_blk.shape == v_blk.shape

@@ -301,13 +301,9 @@ kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void*
  * kvq_commit(c, KVQ_PREFIX, 0, d_k_blk, d_v_blk, blk_dtype, block_len, h_ntok,
  * h_prot_off, h_prot_idx, stream), with the same arguments and results: the
  * output is that of the attention over the cache as it was before the call.
- * The attention never reads the slots and protected rows the commit writes, so
- * the commit kernel is launched on `stream` right after the attention kernel
- * without waiting for it to finish (HIP's any-order launch); its workgroups can
- * take compute units freed in the attention's tail.  Work enqueued on `stream`
- * later waits for both.  The commit is checked before anything is launched
- * and is launched only after the attention kernel: on an error the cache is
- * unchanged.  Calls on one handle must not overlap. */
+ * The kernels are launched back to back on `stream`.  The commit is checked
+ * before anything is launched: on an error the cache is unchanged.  Calls on
+ * one handle must not overlap. */
 kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
                              int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
                              int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,

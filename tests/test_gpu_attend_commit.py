@@ -1,6 +1,5 @@
 """GPU parity of kvq_attend_commit (attention of a block over the cache as it
-is, then the commit of that block, in one call, the commit kernel launched so
-that it may overlap the attention kernel): over several steps, every output within the attention gate of the
+is, then the commit of that block, in one call): over several steps, every output within the attention gate of the
 oracle's attention before the commit, bit-identical to the output of separate
 kvq_block_attn + kvq_commit calls on a twin cache, and records, headers and
 protected rows bit-exact against the oracle afterwards."""
