@@ -19,12 +19,13 @@ from bit_kv_cache_kivi_amd import kvq  # noqa: E402
 from gpu_util import announce, attention_error, build_case, compare_commit, dev  # noqa: E402
 
 
-@pytest.mark.parametrize("name,T,B,nsteps", [
-    ("tiny", None, None, 3), ("dream7b_4bit", 300, 2, 4), ("dual_long", 400, 2, 3), ("serve_b32", 200, 6, 2)])
-def test_attend_commit_steps(name, T, B, nsteps):
-    announce("attend_commit", name, T, B, nsteps)
-    w, cache, ora = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1)
-    _, twin, _ = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1)
+@pytest.mark.parametrize("name,T,B,nsteps,v_rot", [
+    ("tiny", None, None, 3, 0), ("dream7b_4bit", 300, 2, 4, 0), ("dual_long", 400, 2, 3, 0),
+    ("serve_b32", 200, 6, 2, 0), ("dream7b_4bit", 300, 2, 2, 64)])
+def test_attend_commit_steps(name, T, B, nsteps, v_rot):
+    announce("attend_commit", name, T, B, nsteps, v_rot)
+    w, cache, ora = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1, v_rot_block=v_rot)
+    _, twin, _ = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1, v_rot_block=v_rot)
     c = w.cfg
     use_suffix = bool(c.suffix)
     g = np.random.default_rng(5)
