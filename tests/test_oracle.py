@@ -56,12 +56,18 @@ def test_round_half_to_even():
 
 
 def test_division_not_reciprocal():
-    # (x - mn) / scale with an exactly rounded fp32 division: for scale = 1/3
-    # rounded, q = fl(x / fl(1/3)) must equal numpy's fp32 division, and the
-    # code follows rint of that quotient.
-    c, s, z = q1([0.0, 1.0], 2)
-    assert s == F32(1.0) / F32(3.0)
-    assert c[1] == 3
+    # The code takes an IEEE fp32 division (x - mn) / scale.  Hand values, all
+    # exact in bf16: {-2.109375, 0.7265625, 3.5625} at 2 bits has range
+    # 5.671875 and scale 5.671875 / 3 = 1.890625 exactly; the middle element
+    # sits at 2.8359375 / 1.890625 = 1.5 exactly, a tie that rounds to even (2).
+    # Multiplying by the rounded reciprocal 1/1.890625 instead gives
+    # 1.4999999 and code 1, so a reciprocal-multiply quantizer fails here.
+    c, s, z = q1([-2.109375, 0.7265625, 3.5625], 2)
+    assert s == F32(1.890625) and z == F32(-2.109375)
+    assert list(c) == [0, 2, 3]
+    # the same group one octave up: scale 3.78125, the same tie
+    c, s, z = q1([-4.21875, 1.453125, 7.125], 2)
+    assert s == F32(3.78125) and list(c) == [0, 2, 3]
 
 
 def test_subnormal_group():

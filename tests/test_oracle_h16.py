@@ -58,3 +58,19 @@ def test_record_bytes_h16():
         off = L["vmeta_offset"] + grp * 128
         assert np.float32(rec[off + 2 * t:off + 2 * t + 2].view("<f2")[0]) == s16[0]
         assert np.float32(rec[off + 64 + 2 * t:off + 64 + 2 * t + 2].view("<f2")[0]) == z16[0]
+
+
+def test_codes_against_the_rounded_pair():
+    # Group {0, 0.5 - 2^-13, 1} at 2 bits: the fp32 scale is fl(1/3) =
+    # 0.3333333432..., which rounds to the fp16 scale 1365/4096 = 0.333251953125,
+    # and the zero 0 is exact in both.  Against the rounded pair the middle
+    # element is (0.5 - 2^-13) / (1365/4096) = 1.5 exactly (1.5 * 1365/4096 =
+    # 0.4998779296875), a tie that rounds to even: code 2.  Against the fp32
+    # pair it is 1.49963 and would give code 1.
+    x = np.array([[0.0, 0.5 - 2.0 ** -13, 1.0]], np.float32)
+    code, s16, z16 = asym_quantize_h16(x, 2)
+    assert s16[0] == np.float32(1365 / 4096) and z16[0] == 0.0
+    assert list(code[0]) == [0, 2, 3]
+    # the fp32 quantizer on the same group gives the other code for the middle
+    c32, s32, _ = asym_quantize(x, 2)
+    assert s32[0] == np.float32(1.0) / np.float32(3.0) and list(c32[0]) == [0, 1, 3]

@@ -102,3 +102,57 @@ def test_rotated_cache_high_precision_limit():
             vals = np.concatenate([v[bb, :, h], vb[bb, :, h]])
             exact = O.attention_rows(q[bb, :, hq], keys, vals, 1 / np.sqrt(D))
             assert np.abs(out[bb, :, hq] - exact).max() < 2e-4
+
+
+# ---- the fp32 operation order of the forward rotation decides value codes;
+# these hand-computed rows fail for any other order, for a fused multiply-add
+# in the mix, and for a rotation computed in higher precision and rounded once.
+
+def test_hadamard_stage_order_by_hand():
+    # One block of 16, identity permutation, mix [[1]].  x = (1, 2^-24, 2^-24, 0, ...).
+    # Stage h=1: (1 + 2^-24 -> 1 (tie to even), 1 - 2^-24, 2^-24, 2^-24).
+    # Stage h=2: y0 = 1 + 2^-24 -> 1, y2 = 1 - 2^-24, y1 = (1 - 2^-24) + 2^-24 = 1,
+    #            y3 = (1 - 2^-24) - 2^-24 = 1 - 2^-23.
+    # Stages h=4, 8 pair these with zeros, so they are copied.  Then /4.
+    # Stages in the reverse order would give y1 = 1 - 2^-24, and the exact
+    # transform gives y0 = 1 + 2^-23.
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0], x[0, 1], x[0, 2] = 1.0, 2.0 ** -24, 2.0 ** -24
+    y = O.rotate_f32(x, np.arange(16), np.ones((1, 1), np.float32), 16)[0]
+    quad = np.array([1.0, 1.0, 1.0 - 2.0 ** -24, 1.0 - 2.0 ** -23], np.float64) / 4
+    assert np.array_equal(y.astype(np.float64), np.tile(quad, 4))
+
+
+def test_mix_products_rounded_before_the_sum():
+    # D = 128, b = 64 (k = 2).  x = 8 (1 + 2^-23) at the first coordinate of each
+    # block, so every Hadamard output is 1 + 2^-23 (exact).  Mix row 0 =
+    # (1 + 2^-23, -(1 + 2^-22)):
+    #   p0 = (1 + 2^-23)^2 = 1 + 2^-22 + 2^-46 -> 1 + 2^-22
+    #   p1 = -(1 + 2^-23)(1 + 2^-22) = -(1 + 3*2^-23 + 2^-45) -> -(1 + 3*2^-23)
+    #   p0 + p1 = -2^-23 exactly.
+    # A fused multiply-add gives -(2^-23 + 2^-45); exact products summed and
+    # rounded once give -(2^-23 + 2^-46).  Mix row 1 = (1, 0): 1 + 2^-23.
+    D, b = 128, 64
+    x = np.zeros((1, D), np.float32)
+    x[0, 0] = x[0, 64] = np.float32(8 * (1 + 2.0 ** -23))
+    mix = np.array([[1 + 2.0 ** -23, -(1 + 2.0 ** -22)], [1.0, 0.0]], np.float32)
+    z = O.rotate_f32(x, np.arange(D), mix, b)[0]
+    assert np.all(z[:64] == np.float32(-(2.0 ** -23)))
+    assert np.all(z[64:] == np.float32(1 + 2.0 ** -23))
+
+
+def test_mix_summed_in_block_order():
+    # D = 64, b = 16 (k = 4).  x = 4 at the first coordinate of each block, so
+    # every Hadamard output is 1.  Mix row 0 = (2^-24, 1, 2^-24, 2^-24):
+    # in block order ((2^-24 + 1) + 2^-24) + 2^-24 rounds to 1 at every step
+    # (each a tie to even).  The reverse order gives 1 + 2^-22, pairs summed
+    # first give 1 + 2^-23, and one rounding of the exact sum 1 + 3*2^-24
+    # gives 1 + 2^-22.
+    D, b = 64, 16
+    x = np.zeros((1, D), np.float32)
+    x[0, [0, 16, 32, 48]] = 4.0
+    mix = np.eye(4, dtype=np.float32)
+    mix[0] = [2.0 ** -24, 1.0, 2.0 ** -24, 2.0 ** -24]
+    z = O.rotate_f32(x, np.arange(D), mix, b)[0].reshape(4, 16)
+    assert np.all(z[0] == 1.0)
+    assert np.all(z[1:] == 1.0)
