@@ -152,6 +152,36 @@ def _csr(protected):
     return _int_array(o), (_int_array(flat) if flat else (c_int32 * 1)(0))
 
 
+def _expect(name, t, shape, dtypes=None):
+    """Checks one tensor argument before any library call: exact shape,
+    contiguity and dtype.  The C ABI receives raw pointers only, so a tensor
+    of the wrong shape would be read or written out of bounds by the kernels."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(buffer, **tensors):
+    """Every tensor argument must live on the cache buffer's GPU (a host
+    pointer handed to a kernel faults the device)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != buffer.device:
+            raise ValueError(f"{name} is on {t.device}; the cache lives on {buffer.device}")
+
+
+def _per_sequence(name, vals, B):
+    if vals is not None and len(vals) != B:
+        raise ValueError(f"{name} has {len(vals)} entries, expected one per sequence ({B})")
+
+
 class KVCache:
     """One layer's low-bit cache in a torch-owned device buffer."""
 
@@ -186,12 +216,50 @@ class KVCache:
         except Exception:
             pass
 
+    def _q_heads(self, q):
+        hq = int(q.shape[2])
+        H = self.cfg.num_kv_heads
+        if hq < H or hq % H != 0 or hq > self.cfg.max_q_heads:
+            raise ValueError(f"q has {hq} heads: a multiple of num_kv_heads {H} up to max_q_heads "
+                             f"{self.cfg.max_q_heads} is needed")
+        return hq
+
+    def _check_attn(self, q, k_blk, v_blk, out, out_dtype):
+        """Shapes [B, 32, Hq, D] (q, out) and [B, 32, Hkv, D] (k_blk, v_blk),
+        dtypes, contiguity and device, before any library call; returns out
+        (allocated when None)."""
+        import torch
+        B, H, D = self.cfg.batch, self.cfg.num_kv_heads, self.cfg.head_dim
+        fp = (torch.float32, torch.bfloat16)
+        if not hasattr(q, "shape") or q.dim() != 4:
+            raise ValueError("q must be a [B, 32, Hq, D] tensor")
+        hq = self._q_heads(q)
+        _expect("q", q, (B, SLOT, hq, D), fp)
+        _expect("k_blk", k_blk, (B, SLOT, H, D), fp)
+        _expect("v_blk", v_blk, (B, SLOT, H, D), (k_blk.dtype,))
+        if out is None:
+            _on_device(self.buffer, q=q, k_blk=k_blk, v_blk=v_blk)
+            return torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
+        _expect("out", out, (B, SLOT, hq, D), fp)
+        _on_device(self.buffer, q=q, k_blk=k_blk, v_blk=v_blk, out=out)
+        return out
+
     def commit(self, k, v, ntok=None, protected=None, segment=KVQ_PREFIX, reset=False, stream=None):
         """k, v: [B, n_max, Hkv, D] (fp32 or bf16, contiguous, on the device).
 
         ntok: per-sequence token counts (default n_max); protected: per-sequence
         sorted positions, relative to this commit, of key rows kept in bf16."""
-        assert k.is_contiguous() and v.is_contiguous() and k.dtype == v.dtype and k.shape == v.shape
+        import torch
+        B, H, D = self.cfg.batch, self.cfg.num_kv_heads, self.cfg.head_dim
+        if not hasattr(k, "shape") or k.dim() != 4:
+            raise ValueError("k must be a [B, n_max, Hkv, D] tensor")
+        n_max = int(k.shape[1])
+        fp = (torch.float32, torch.bfloat16)
+        _expect("k", k, (B, n_max, H, D), fp)
+        _expect("v", v, (B, n_max, H, D), (k.dtype,))
+        _per_sequence("ntok", ntok, B)
+        _per_sequence("protected", protected, B)
+        _on_device(self.buffer, k=k, v=v)
         nt = _int_array(ntok)
         off, idx = _csr(protected)
         check(lib.kvq_commit(self._h, int(segment), int(bool(reset)), c_void_p(k.data_ptr()),
@@ -202,13 +270,10 @@ class KVCache:
                    out=None, stream=None):
         """q [B, 32, Hq, D]; k_blk, v_blk [B, 32, Hkv, D].  Returns out [B, 32, Hq, D]."""
         import torch
-        assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
-        assert k_blk.dtype == v_blk.dtype
+        out = self._check_attn(q, k_blk, v_blk, out, out_dtype)
         D = self.cfg.head_dim
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(D)
-        if out is None:
-            out = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
         check(lib.kvq_block_attn(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
                                  _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
                                  _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
@@ -219,13 +284,11 @@ class KVCache:
                       out_dtype=None, out=None, stream=None):
         """block_attn over the cache as it is, then commit k_blk, v_blk to the
         prefix (ntok, protected as for commit), in one call."""
-        import torch
-        assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
-        assert k_blk.dtype == v_blk.dtype and k_blk.shape == v_blk.shape
+        out = self._check_attn(q, k_blk, v_blk, out, out_dtype)
+        _per_sequence("ntok", ntok, self.cfg.batch)
+        _per_sequence("protected", protected, self.cfg.batch)
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
-        if out is None:
-            out = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
         off, idx = _csr(protected)
         check(lib.kvq_attend_commit(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
                                     _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
@@ -240,7 +303,15 @@ class KVCache:
         the top `budget` per (sequence, kv head) (granularity 32: the top
         `budget` 32-token units by summed contributions).  query_mask:
         per-sequence 32-bit masks of the mask queries (None = all)."""
-        assert q.is_contiguous() and k_blk.is_contiguous()
+        import torch
+        B, H, D = self.cfg.batch, self.cfg.num_kv_heads, self.cfg.head_dim
+        fp = (torch.float32, torch.bfloat16)
+        if not hasattr(q, "shape") or q.dim() != 4:
+            raise ValueError("q must be a [B, 32, Hq, D] tensor")
+        _expect("q", q, (B, SLOT, self._q_heads(q), D), fp)
+        _expect("k_blk", k_blk, (B, SLOT, H, D), fp)
+        _per_sequence("query_mask", query_mask, B)
+        _on_device(self.buffer, q=q, k_blk=k_blk)
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
         qm = None if query_mask is None else (ctypes.c_uint32 * len(query_mask))(*[int(x) & 0xFFFFFFFF for x in query_mask])
@@ -251,13 +322,9 @@ class KVCache:
     def block_attn_selected(self, q, k_blk, v_blk, use_suffix=False, softmax_scale=None, out_dtype=None,
                             out=None, stream=None):
         """block_attn over the block and the last selection only."""
-        import torch
-        assert q.is_contiguous() and k_blk.is_contiguous() and v_blk.is_contiguous()
-        assert k_blk.dtype == v_blk.dtype
+        out = self._check_attn(q, k_blk, v_blk, out, out_dtype)
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
-        if out is None:
-            out = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16, device=q.device)
         check(lib.kvq_block_attn_selected(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
                                           _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
                                           _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),

@@ -283,3 +283,80 @@ def test_attend_commit_checks_before_launch(kvq):
         kvq.lib.kvq_segment_info(h, 0, *after)
         assert [list(a) for a in after] == [list(b) for b in before]
     assert kvq.lib.kvq_destroy(h) == 0
+
+
+# ---- the Python binding checks every tensor argument before a library call
+def test_binding_rejects_bad_inputs_before_any_call(kvq):
+    """Wrong shapes, dtypes, per-sequence list lengths and host tensors raise
+    in the binding; nothing reaches the C ABI (a kernel would read or write out
+    of bounds).  The cache buffer here is host memory that no call touches:
+    every case below must raise before the library is called."""
+    import torch
+    B, H, D, hq = 2, 2, 64, 4
+    # a handle-less cache object over a host buffer (no library handle is needed:
+    # no case may get that far)
+    c = object.__new__(kvq.KVCache)
+    c.cfg = kvq.make_config(B, H, D, 4, 4, 64, prefix_slots=2, prefix_protected=4, max_q_heads=hq)
+    c.layout = kvq.get_layout(c.cfg)
+    c.buffer = torch.empty(16, dtype=torch.uint8)
+    c._h = ctypes.c_void_p()
+    calls = []
+    real = kvq.lib
+    class Spy:
+        def __getattr__(self, name):
+            fn = getattr(real, name)
+            if name in ("kvq_commit", "kvq_block_attn", "kvq_attend_commit", "kvq_select",
+                        "kvq_block_attn_selected"):
+                def rec(*a):
+                    calls.append(name)
+                    raise AssertionError(f"{name} reached")
+                return rec
+            return fn
+    kvq.lib = Spy()
+    try:
+        f32, bf = torch.float32, torch.bfloat16
+        z = lambda *s, dt=bf: torch.zeros(*s, dtype=dt)   # noqa: E731
+        kv = z(B, 32, H, D)
+        bad_commit = [
+            dict(k=z(B + 1, 32, H, D), v=z(B + 1, 32, H, D)),            # batch
+            dict(k=z(B, 32, H + 1, D), v=z(B, 32, H + 1, D)),            # kv heads
+            dict(k=z(B, 32, H, 2 * D), v=z(B, 32, H, 2 * D)),            # head dim
+            dict(k=kv, v=z(B, 16, H, D)),                                # v shape differs
+            dict(k=kv, v=z(B, 32, H, D, dt=f32)),                        # v dtype differs
+            dict(k=z(B, 32, H, D, dt=torch.float16), v=z(B, 32, H, D, dt=torch.float16)),
+            dict(k=z(B, H, 32, D).transpose(1, 2), v=kv),                # not contiguous
+            dict(k=kv, v=kv, ntok=[32]),                                 # one count per sequence
+            dict(k=kv, v=kv, protected=[[0]]),                           # one list per sequence
+            dict(k=kv, v=kv),                                            # host tensors
+            dict(k=z(B, 32, H * D), v=z(B, 32, H * D)),                  # rank
+        ]
+        for kw in bad_commit:
+            with pytest.raises((ValueError, TypeError)):
+                c.commit(**kw)
+        q = z(B, 32, hq, D)
+        bad_attn = [
+            dict(q=z(B, 32, hq, D + 64), k_blk=kv, v_blk=kv),
+            dict(q=z(B + 1, 32, hq, D), k_blk=kv, v_blk=kv),
+            dict(q=z(B, 16, hq, D), k_blk=kv, v_blk=kv),                 # block length
+            dict(q=z(B, 32, 3, D), k_blk=kv, v_blk=kv),                  # heads not a multiple of H
+            dict(q=z(B, 32, 2 * hq, D), k_blk=kv, v_blk=kv),             # above max_q_heads
+            dict(q=q, k_blk=z(B, 32, hq, D), v_blk=z(B, 32, hq, D)),     # [B, n, Hq, D] keys
+            dict(q=q, k_blk=kv, v_blk=z(B, 32, H, D, dt=f32)),
+            dict(q=q, k_blk=kv, v_blk=kv, out=z(B, 32, H, D)),           # out shape
+            dict(q=q, k_blk=kv, v_blk=kv, out=z(B, 32, hq, D, dt=torch.float16)),
+            dict(q=q, k_blk=kv, v_blk=kv),                               # host tensors
+            dict(q=q, k_blk=kv, v_blk=kv, out=z(B, 32, hq, D)),          # host output
+        ]
+        for kw in bad_attn:
+            for fn in (c.block_attn, c.block_attn_selected, c.attend_commit):
+                with pytest.raises((ValueError, TypeError)):
+                    fn(**kw)
+        with pytest.raises(ValueError):
+            c.attend_commit(q, kv, kv, ntok=[32, 32, 32])
+        for kw in (dict(q=z(B, 32, hq, D + 64), k_blk=kv), dict(q=q, k_blk=z(B, 32, hq, D)),
+                   dict(q=q, k_blk=kv, query_mask=[1]), dict(q=q, k_blk=kv)):
+            with pytest.raises((ValueError, TypeError)):
+                c.select(budget=4, **kw)
+    finally:
+        kvq.lib = real
+    assert calls == []
