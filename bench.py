@@ -215,8 +215,10 @@ def main():
     torch.cuda.synchronize()
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record(stream0)
+    th0 = time.perf_counter()
     for cache in caches:
         prefill(cache, 1)
+    prefill_host_ms = (time.perf_counter() - th0) * 1e3 / L    # host time to issue one call
     p1.record(stream0)
     torch.cuda.synchronize()
     prefill_ms = p0.elapsed_time(p1) / L
@@ -377,6 +379,7 @@ def main():
         "prefill_commit_tokens_per_s": float(np.sum(w.lengths)) / (prefill_ms * 1e-3),
         "prefill_commit_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
         "prefill_commit_hbm_frac": prefill_bytes / (prefill_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "prefill_commit_host_issue_ms": prefill_host_ms,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
         "roofline": {**roof, "traffic": None if (args.v_rotation or args.kv_format != "int") else measured_traffic(c.name),
                      "kernel": "attention launch (attn_kernel + combine_kernel" +

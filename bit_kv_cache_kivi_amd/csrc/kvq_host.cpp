@@ -129,17 +129,22 @@ struct kvq_cache {
   uint8_t* dbuf;
   SegMirror seg[2];
   int32_t split_slots = 0;
-  // Ring of two task tables in pinned host memory (created on first device
-  // use): a large commit's kernel reads its table straight from host memory,
-  // so no copy operation sits on the stream ahead of the kernel.  ev[k] marks
-  // the end of the last kernel that read table k.
-  bool hip_ready = false;
+  // Ring of kStageRing task tables in pinned host memory (created by the first
+  // commit of more than kInlineTasks slots): such a commit's kernel reads its
+  // table straight from host memory (each workgroup's first tasks in one
+  // parallel read), so no copy operation sits on the stream ahead of the
+  // kernel.  ev[k] marks the end of the last kernel that read table k; a
+  // commit blocks the calling thread only when it needs a table whose kernel
+  // has not finished, i.e. when kStageRing large commits are still in flight.
+  static constexpr int kStageRing = 4;
+  bool dev_ready = false;
+  bool stage_ready = false;
   uint8_t* h_stage = nullptr;
   size_t task_bytes = 0;           // one table: B * max(slot capacity) tasks
-  hipEvent_t ev[2] = {nullptr, nullptr};
-  bool ev_used[2] = {false, false};
+  hipEvent_t ev[kStageRing] = {};
+  bool ev_used[kStageRing] = {};
   int next_stage = 0;
-  int num_cus = 0;                 // compute units of the device (sizes the attention grid)
+  int num_cus = 0;                 // compute units of the device (sizes the grids)
   std::vector<CommitTask> tasks;
   kvq::RotParams rot{};            // value rotation (rot.block == 0 until set)
   // the last selection: valid while no commit has happened since
@@ -150,21 +155,53 @@ struct kvq_cache {
 
 namespace {
 
-kvq_status ensure_hip(kvq_cache* c) {
-  if (c->hip_ready) return KVQ_OK;
-  const size_t maxcap = std::max(c->cfg.prefix_slots, c->cfg.suffix_slots);
-  c->task_bytes = ((size_t)c->cfg.batch * maxcap * sizeof(CommitTask) + 255) & ~(size_t)255;
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), 2 * c->task_bytes, hipHostMallocDefault);
-  if (e != hipSuccess) { c->h_stage = nullptr; return fail(KVQ_EHIP, "hipHostMalloc: %s", hipGetErrorString(e)); }
-  for (int i = 0; i < 2; ++i) {
-    e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
-    if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
-  }
+// Device properties the launches need; allocates nothing.
+kvq_status ensure_device(kvq_cache* c) {
+  if (c->dev_ready) return KVQ_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c->num_cus <= 0)
     c->num_cus = 256;
-  c->hip_ready = true;
+  c->dev_ready = true;
+  return KVQ_OK;
+}
+
+void release_stage(kvq_cache* c) {
+  for (int i = 0; i < kvq_cache::kStageRing; ++i) {
+    if (c->ev[i]) {
+      if (c->ev_used[i]) hipEventSynchronize(c->ev[i]);
+      hipEventDestroy(c->ev[i]);
+      c->ev[i] = nullptr;
+    }
+    c->ev_used[i] = false;
+  }
+  if (c->h_stage) hipHostFree(c->h_stage);
+  c->h_stage = nullptr;
+  c->stage_ready = false;
+}
+
+// The pinned task-table ring of large commits (allocated once per handle;
+// on failure nothing stays allocated).
+kvq_status ensure_stage(kvq_cache* c) {
+  if (c->stage_ready) return KVQ_OK;
+  const size_t maxcap = std::max(c->cfg.prefix_slots, c->cfg.suffix_slots);
+  c->task_bytes = ((size_t)c->cfg.batch * maxcap * sizeof(CommitTask) + 255) & ~(size_t)255;
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), kvq_cache::kStageRing * c->task_bytes,
+                               hipHostMallocDefault);
+  if (e != hipSuccess) {
+    c->h_stage = nullptr;
+    return fail(KVQ_EHIP, "hipHostMalloc: %s", hipGetErrorString(e));
+  }
+  for (int i = 0; i < kvq_cache::kStageRing; ++i) {
+    e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      c->ev[i] = nullptr;
+      release_stage(c);
+      return fail(KVQ_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  c->next_stage = 0;
+  c->stage_ready = true;
   return KVQ_OK;
 }
 
@@ -241,15 +278,7 @@ kvq_status kvq_create(const kvq_config* cfg, void* d_buf, size_t buf_bytes, kvq_
 
 kvq_status kvq_destroy(kvq_cache* c) {
   if (!c) return KVQ_OK;
-  if (c->hip_ready) {
-    for (int i = 0; i < 2; ++i) {
-      if (c->ev[i]) {
-        if (c->ev_used[i]) hipEventSynchronize(c->ev[i]);
-        hipEventDestroy(c->ev[i]);
-      }
-    }
-    if (c->h_stage) hipHostFree(c->h_stage);
-  }
+  release_stage(c);
   delete c;
   return KVQ_OK;
 }
@@ -437,8 +466,12 @@ kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
   SegMirror& m = c->seg[segment];
   auto& tasks = c->tasks;
   if (!tasks.empty()) {
-    kvq_status s = ensure_hip(c);
+    kvq_status s = ensure_device(c);
     if (s != KVQ_OK) return s;
+    if ((int)tasks.size() > kvq::kInlineTasks) {
+      s = ensure_stage(c);
+      if (s != KVQ_OK) return s;
+    }
     kvq::CommitArgs a;          // about 2 KB with the inline task table; the launch copies it
     memset(&a, 0, sizeof(a));
     hipError_t e = hipSuccess;
@@ -475,7 +508,7 @@ kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
       e = hipEventRecord(c->ev[k], st);
       if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
       c->ev_used[k] = true;
-      c->next_stage = k ^ 1;
+      c->next_stage = (k + 1) % kvq_cache::kStageRing;
     }
   }
 
@@ -549,7 +582,7 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     max_units = std::max(max_units, U);
     total_units += U;
   }
-  kvq_status hs = ensure_hip(c);
+  kvq_status hs = ensure_device(c);
   if (hs != KVQ_OK) return hs;
   int split_units;
   if (c->split_slots > 0) {
@@ -727,7 +760,7 @@ kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
   if (budget < 0) return fail(KVQ_EINVAL, "budget %d", budget);
   if (cfg.kv_format != KVQ_FMT_INT) return fail(KVQ_EUNSUPPORTED, "selection reads integer-format records only");
-  kvq_status hs = ensure_hip(c);
+  kvq_status hs = ensure_device(c);
   if (hs != KVQ_OK) return hs;
 
   const int max_splits = cfg.max_splits ? cfg.max_splits : 32;

@@ -45,12 +45,17 @@
  * ------------------------------------------------------------------------
  *  - The caller owns all device memory: the cache buffer handed to kvq_create
  *    (kvq_required_bytes bytes, 256-byte aligned), inputs and outputs.  The
- *    library never allocates device memory.  It allocates a small pinned host
- *    ring of two commit task tables (read by the commit kernel directly from
- *    host memory) and two events on first device use; kvq_destroy frees them.
+ *    library never allocates device memory.  The first commit of more than 64
+ *    slots on a handle allocates a small pinned host ring of four commit task
+ *    tables (read by the commit kernel directly from host memory) and four
+ *    events; kvq_destroy frees them.  No other call allocates anything.
  *  - Pointers named d_* are device pointers; h_* are host pointers read only
  *    during the call.  `stream` is a hipStream_t (NULL = default stream).
- *  - Calls are asynchronous and stream-ordered.  All calls on one handle must be
+ *  - Calls are asynchronous and stream-ordered, with one exception: a commit of
+ *    more than 64 slots (a prefill) reuses one of the four pinned task tables
+ *    and blocks the calling thread until the kernel that last read that table
+ *    has finished, i.e. only while four such commits on the handle are still
+ *    in flight on the device.  All calls on one handle must be
  *    issued on one stream or be ordered by the caller.  A handle is not
  *    thread-safe.
  *  - Every call returns a kvq_status.  All argument checks run on the host
