@@ -33,6 +33,7 @@
 // A split's partial (reference maximum, sum, unnormalised O) goes to the
 // workspace and the combine kernel merges splits with log-sum-exp weights; a
 // single split writes the normalised output itself.
+#include "commit_slot.h"
 #include "device_common.h"
 #include "kvq_internal.h"
 
@@ -63,6 +64,56 @@ struct Shape {
   static_assert(NKG % kProducerThreads == 0 && NVC % kProducerThreads == 0, "thread mapping");
   static_assert(RPT >= GPT, "the block's K rows use the record prefetch slots");
 };
+
+// Fused commit of the block (SoloQ summary page, block-diffusion paragraph:
+// the block's keys and values are quantized once, when it is committed): the
+// four producer waves of the workgroup that attended with the block quantize
+// its first cvalid[b] tokens for kv head kvh into prefix slot nslots[0][b]
+// once their pipeline is done, with the same per-slot quantizer as the commit
+// kernel, in LDS the pipeline no longer reads.  The slot's protected rank and
+// token bases continue those of the previous slot's header (0 for the first
+// slot).  Ends with one workgroup barrier before the record leaves; the
+// consumer waves match it.
+template <int KB, int VB, int D, bool F32IN, int FMT>
+__device__ __forceinline__ void commit_block(uint8_t* lds_base, size_t lds_bytes, const AttnArgs& a, int b, int kvh,
+                                             int tid) {
+  using Q = SlotQuant<KB, VB, D, F32IN, false, FMT>;
+  constexpr size_t kLds = (sizeof(typename Q::Lds) + 15) / 16 * 16;
+  (void)lds_bytes;
+  auto& lds = *reinterpret_cast<typename Q::Lds*>(lds_base);
+  uint8_t* rec = lds_base + kLds;
+  const SlotIO io{a.k_blk, a.v_blk, a.seg[0], kSlot, a.hkv, a.gv_log2, a.record_bytes};
+  Q q(lds, io, kvh, tid);
+  CommitTask task;
+  task.b = b;
+  task.dst_slot = a.nslots[0][b];
+  task.src_tok = 0;
+  task.nvalid = a.cvalid[b];
+  task.mask = a.cmask[b];
+  task.rank_base = 0;
+  task.token_base = 0;
+  task.pad = 0;
+  if (task.dst_slot > 0) {
+    const int4 ph = *reinterpret_cast<const int4*>(a.seg[0].headers +
+                                                   ((size_t)b * a.seg[0].slot_cap + task.dst_slot - 1) * kHeaderBytes);
+    task.rank_base = __builtin_amdgcn_readfirstlane(ph.z + __popc((uint32_t)ph.y));
+    task.token_base = __builtin_amdgcn_readfirstlane(ph.w + ph.x);
+  }
+  q.clear_tail(rec);
+  typename Q::Raw raw;
+  q.fetch(true, task, raw);
+  float x[Q::TPL][8];
+#pragma unroll
+  for (int k = 0; k < Q::TPL; ++k) Q::unpack_row(raw, k, x[k]);
+  if (q.keys) {
+    if (task.mask != 0u) q.store_protected(task, x);
+    q.process_keys(task, x, rec);
+  } else {
+    q.process_values(task, x, rec, 0);
+  }
+  __syncthreads();
+  q.copy_out(task, rec);
+}
 
 // CEN (values stored in a rotated basis): a value is dequantized as
 // (code - cm) * scale with cm the middle code, (2^vb - 1) / 2, and the offset
@@ -136,6 +187,8 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   const int nq = min(u1, U - 1) - u0;        // slot units of this split
   const bool has_block = u1 == U;
   const int NU = nq + (has_block ? 1 : 0);   // units; the block, if here, is unit nq
+  // this workgroup also commits the block (uniform)
+  const bool fuse = a.commit_blk && has_block && a.cvalid[b] > 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -683,6 +736,17 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       load_unit(i + 4, pre0, h4);
       __syncthreads();
     }
+    if constexpr (!CEN) {
+      if (fuse) {
+        // the pipeline's last barrier has passed: the producers own rawbuf
+        static_assert(sizeof(typename SlotQuant<KB, VB, D, true, false, FMT>::Lds) + 16 +
+                          SlotQuant<KB, VB, D, true, false, FMT>::REC_MAX <= sizeof(rawbuf),
+                      "the fused commit fits the staging buffers");
+        uint8_t* base = &rawbuf[0][0];
+        if (blk_f32) commit_block<KB, VB, D, true, FMT>(base, sizeof(rawbuf), a, b, kvh, tid);
+        else         commit_block<KB, VB, D, false, FMT>(base, sizeof(rawbuf), a, b, kvh, tid);
+      }
+    }
     return;
   }
   {
@@ -758,6 +822,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   __syncthreads();
   if (ci >= r) {
     for (int i = 0; i < n_int; ++i) __syncthreads();
+    if (!CEN && fuse) __syncthreads();   // the fused commit's barrier
     return;
   }
   half8 pop[2], va[CT][2];
@@ -876,6 +941,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       base[(D + 1) * kSlot + j] = l_tot;
     }
   }
+  if (!CEN && fuse) __syncthreads();   // the fused commit's barrier
 }
 
 // One workgroup per (query head, sequence, 32-channel chunk): merges the

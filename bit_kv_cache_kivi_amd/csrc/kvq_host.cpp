@@ -455,6 +455,8 @@ kvq_status commit_plan(kvq_cache* c, int32_t segment, int32_t reset_segment, con
   return KVQ_OK;
 }
 
+void commit_mirror(kvq_cache* c, const CommitPlan& plan);
+
 // Launches a planned commit on st and updates the host mirror.
 kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
   const kvq_config& cfg = c->cfg;
@@ -512,15 +514,23 @@ kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
     }
   }
 
-  // ---- host mirror
-  if (reset_segment || !tasks.empty()) ++c->commit_gen;
+  commit_mirror(c, plan);
+  return KVQ_OK;
+}
+
+// Updates the host mirror for a planned commit that has been launched.
+void commit_mirror(kvq_cache* c, const CommitPlan& plan) {
+  const int B = c->cfg.batch;
+  const int segment = plan.segment, reset_segment = plan.reset;
+  const std::vector<int32_t>& ntok = plan.ntok;
+  SegMirror& m = c->seg[segment];
+  if (reset_segment || !c->tasks.empty()) ++c->commit_gen;
   for (int b = 0; b < B; ++b) {
     if (reset_segment) { m.ntok[b] = 0; m.nslots[b] = 0; m.nprot[b] = 0; }
     m.ntok[b] += ntok[b];
     m.nslots[b] += (ntok[b] + kvq::kSlot - 1) / kvq::kSlot;
     m.nprot[b] += plan.nprot_add[b];
   }
-  return KVQ_OK;
 }
 
 }  // namespace
@@ -540,9 +550,12 @@ kvq_status kvq_commit(kvq_cache* c, int32_t segment, int32_t reset_segment, cons
 
 namespace {
 
+// fused: a planned commit of this same block into the prefix (one slot per
+// sequence), carried out by the attention launch itself.
 kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                            const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
-                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected) {
+                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected,
+                           const CommitPlan* fused = nullptr) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
@@ -639,6 +652,17 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
   a.max_splits = max_splits;
   a.use_suffix = use_suffix ? 1 : 0;
   a.fmt = cfg.kv_format;
+  if (fused) {
+    // one task per committing sequence: slot nslots[0][b], first token 0
+    a.commit_blk = 1;
+    for (const CommitTask& t : c->tasks) {
+      if (t.dst_slot != c->seg[0].nslots[t.b] || t.src_tok != 0 || t.nvalid < 1 || t.nvalid > kvq::kSlot ||
+          t.rank_base != c->seg[0].nprot[t.b] || t.token_base != c->seg[0].ntok[t.b])
+        return fail(KVQ_EINVAL, "internal: the block commit of sequence %d is not one slot after the cache", t.b);
+      a.cmask[t.b] = t.mask;
+      a.cvalid[t.b] = (uint8_t)t.nvalid;
+    }
+  }
   if (selected) {
     a.sel_count = reinterpret_cast<const int32_t*>(c->dbuf + c->lay.sel_count_offset);
     a.sel_units = reinterpret_cast<const int32_t*>(c->dbuf + c->lay.sel_units_offset);
@@ -736,10 +760,21 @@ kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, 
   kvq_status s = commit_plan(c, KVQ_PREFIX, 0, d_k_blk, d_v_blk, blk_dtype, block_len, h_ntok, h_prot_off,
                              h_prot_idx, plan);
   if (s != KVQ_OK) return s;
+  if (c->cfg.v_rotation_block != 0) {
+    // rotated values: the attention reads a rotated copy of the block, so the
+    // commit (which rotates the raw values itself) is a launch of its own
+    s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
+                        softmax_scale, d_out, out_dtype, stream, false);
+    if (s != KVQ_OK) return s;
+    return commit_run(c, plan, static_cast<hipStream_t>(stream));
+  }
+  // one launch: the workgroup holding each (sequence, kv head)'s block also
+  // commits it
   s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
-                      softmax_scale, d_out, out_dtype, stream, false);
+                      softmax_scale, d_out, out_dtype, stream, false, &plan);
   if (s != KVQ_OK) return s;
-  return commit_run(c, plan, static_cast<hipStream_t>(stream));
+  commit_mirror(c, plan);
+  return KVQ_OK;
 }
 
 kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,

@@ -61,7 +61,7 @@ struct CommitArgs {
 };
 static_assert(sizeof(CommitArgs) <= 4096, "commit launch arguments fit the kernel-argument segment");
 
-constexpr int kMaxWgTable = 512;  // attention workgroups listed in the launch arguments
+constexpr int kMaxWgTable = 256;  // attention workgroups listed in the launch arguments
 
 struct AttnArgs {
   const void* q;        // [B, 32, Hq, D]
@@ -87,6 +87,13 @@ struct AttnArgs {
   const uint32_t* sel_mask;
   int32_t sel_ucap;
   uint16_t nslots[2][KVQ_MAX_BATCH];   // per-sequence slot counts of both segments
+  // Fused commit of the block (commit_blk != 0): after its attention work,
+  // the workgroup that holds the block of (b, kv head) quantizes the block's
+  // first cvalid[b] tokens into prefix slot nslots[0][b], with protected
+  // tokens cmask[b] (rank and token bases follow the previous slot's header).
+  int32_t commit_blk;
+  uint32_t cmask[KVQ_MAX_BATCH];
+  uint8_t cvalid[KVQ_MAX_BATCH];
   // Workgroup list of a one-dimensional grid: entry i = split | kvh << 8 |
   // b << 16 for workgroup i, only splits that hold units.  num_wg == 0: a
   // (splits, Hkv, B) grid instead, whose workgroups past a sequence's splits

@@ -306,7 +306,11 @@ kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void*
  * kvq_commit(c, KVQ_PREFIX, 0, d_k_blk, d_v_blk, blk_dtype, block_len, h_ntok,
  * h_prot_off, h_prot_idx, stream), with the same arguments and results: the
  * output is that of the attention over the cache as it was before the call.
- * The kernels are launched back to back on `stream`.  The commit is checked
+ * It is one launch on `stream`: the workgroup that attends with the block of
+ * (sequence b, kv head h) also quantizes that block's keys and values for kv
+ * head h into the next prefix slot once its attention work is done (the new
+ * slot is one no attention of the call reads).  For a cache with value
+ * rotation the commit is a second launch on `stream`.  The commit is checked
  * before anything is launched: on an error the cache is unchanged.  Calls on
  * one handle must not overlap. */
 kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,

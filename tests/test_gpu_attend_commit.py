@@ -73,3 +73,43 @@ def test_attend_commit_errors_leave_cache_unchanged():
     e, x = attention_error(out, ref, "f32")
     assert x <= 0, e
     compare_commit(cache, ora, 0, c.B)
+
+
+@pytest.mark.parametrize("fmt", ["int", "int_h16", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attend_commit_fused_edges(fmt, dtype):
+    """The one-launch attend-and-commit from an empty cache (the first slot has
+    no previous header), with a sequence that commits nothing, partial blocks,
+    attention-sink protection and caller rows at both ends of the block, in
+    every record format; outputs equal separate calls on a twin cache, records
+    equal the oracle's."""
+    announce("attend_commit fused edges", fmt, dtype)
+    B, H, D, r = 3, 2, 64, 3
+    kb_, vb_, gv = (4, 4, 32) if fmt == "mxfp4" else (4, 2, 32)
+    kvf = {"int": kvq.KVQ_FMT_INT, "int_h16": kvq.KVQ_FMT_INT_H16, "mxfp4": kvq.KVQ_FMT_MXFP4}[fmt]
+    mk = lambda: kvq.KVCache(B, H, D, kb_, vb_, gv, prefix_tokens=6 * 32, prefix_protected=64,   # noqa: E731
+                             max_q_heads=H * r, protect_sink=True, kv_format=kvf)
+    cache, twin = mk(), mk()
+    ora = O.OracleCache(B, H, D, kb_, vb_, gv, protect_sink=True, fmt=fmt)
+    g = np.random.default_rng(11)
+    counts = [[32, 0, 17], [5, 32, 32], [32, 1, 0], [32, 32, 32]]
+    for s, ntok in enumerate(counts):
+        q = g.standard_normal((B, 32, H * r, D)).astype(np.float32)
+        k = g.standard_normal((B, 32, H, D)).astype(np.float32)
+        v = g.standard_normal((B, 32, H, D)).astype(np.float32)
+        if dtype == "bf16":
+            q, k, v = O.to_bf16_f32(q), O.to_bf16_f32(k), O.to_bf16_f32(v)
+        prot = [np.array([p for p in (0, 2, 31) if p < n], np.int64) if (b + s) % 2 else np.array([], np.int64)
+                for b, n in enumerate(ntok)]
+        ref = O.block_attention(ora, q, k, v)
+        dq, dk, dv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+        out = cache.attend_commit(dq, dk, dv, ntok=ntok, protected=prot, out_dtype=torch.float32)
+        out2 = twin.block_attn(dq, dk, dv, out_dtype=torch.float32)
+        twin.commit(dk, dv, ntok=ntok, protected=prot)
+        ora.commit(0, k, v, ntok=ntok, prot=prot)
+        e, x = attention_error(out, ref, "f32")
+        assert x <= 0, (s, e)
+        assert torch.equal(out, out2), f"step {s}: one-launch output differs from block_attn"
+        torch.cuda.synchronize()
+        compare_commit(cache, ora, 0, B)
+    compare_commit(twin, ora, 0, B)
