@@ -33,6 +33,8 @@
 // A split's partial (reference maximum, sum, unnormalised O) goes to the
 // workspace and the combine kernel merges splits with log-sum-exp weights; a
 // single split writes the normalised output itself.
+#include <mutex>
+
 #include "commit_slot.h"
 #include "device_common.h"
 #include "kvq_internal.h"
@@ -1076,6 +1078,30 @@ hipError_t launch_kb(const AttnArgs& a, int grid_splits, int B, int D, hipStream
 }
 
 }  // namespace
+
+// Workspace of kvq_block_attn_noalloc: split partials and rotation staging.
+// Each device holds its own copy for the life of the process; every call on a
+// device shares it, so calls that overlap on one device race.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // the current device's copy
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
                             hipStream_t stream) {

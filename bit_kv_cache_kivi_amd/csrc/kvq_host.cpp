@@ -555,7 +555,7 @@ namespace {
 kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                            const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
                            float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected,
-                           const CommitPlan* fused = nullptr) {
+                           const CommitPlan* fused = nullptr, bool noalloc = false) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
@@ -632,11 +632,35 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
                 max_splits, kMaxSplitUnits);
   const int grid_splits = (max_units + split_units - 1) / split_units;
 
+  // Workspace: split partials [b][kvh][split][head][D+2][32] fp32, then (value
+  // rotation) the block's fp32 K and rotated V and the rotated output.  In
+  // the cache buffer; for the allocation-free call, in the device's scratch
+  // array, with the split stride cut to this launch's split count.
+  const int D = cfg.head_dim;
+  const size_t blk_elems = (size_t)B * kvq::kSlot * H * D;
+  uint8_t* rot_ws = c->dbuf + c->lay.rotation_offset;
+  a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
+  a.max_splits = max_splits;
+  if (noalloc) {
+    const size_t part = grid_splits > 1 ? align256((uint64_t)B * H * grid_splits * (num_q_heads / H) * (D + 2) *
+                                                   kvq::kSlot * 4)
+                                        : 0;
+    const size_t rot = c->rot.block ? align256(2 * blk_elems * 4) + align256((uint64_t)B * kvq::kSlot * num_q_heads * D * 4)
+                                    : 0;
+    if (part + rot > kvq::kNoAllocScratchBytes)
+      return fail(KVQ_ECAPACITY, "this call needs %zu bytes of workspace; the allocation-free scratch holds %zu",
+                  part + rot, kvq::kNoAllocScratchBytes);
+    void* base = nullptr;
+    hipError_t e = kvq::noalloc_scratch(&base);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "scratch address: %s", hipGetErrorString(e));
+    a.partial = static_cast<float*>(base);
+    a.max_splits = grid_splits;
+    rot_ws = static_cast<uint8_t*>(base) + part;
+  }
   a.q = d_q;
   a.k_blk = d_k_blk;
   a.v_blk = d_v_blk;
   a.out = d_out;
-  a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
   a.seg[0] = seg_ptrs(c, 0);
   a.seg[1] = seg_ptrs(c, 1);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -649,7 +673,6 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
   a.gv_log2 = ilog2(cfg.v_group_channels);
   a.record_bytes = (uint32_t)c->lay.record_bytes;
   a.split_units = split_units;
-  a.max_splits = max_splits;
   a.use_suffix = use_suffix ? 1 : 0;
   a.fmt = cfg.kv_format;
   if (fused) {
@@ -688,14 +711,13 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     }
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int D = cfg.head_dim;
   float* rot_o = nullptr;
   if (c->rot.block != 0) {
     // rotated values: the block's values join the cache's basis (keys are
     // converted alongside, so that both block operands are fp32), attention
     // writes R o in fp32, and the transposed rotation gives o
-    float* ws = reinterpret_cast<float*>(c->dbuf + c->lay.rotation_offset);
-    const size_t blk = (size_t)B * kvq::kSlot * H * D;
+    float* ws = reinterpret_cast<float*>(rot_ws);
+    const size_t blk = blk_elems;
     kvq::BlkPrepArgs p;
     memset(&p, 0, sizeof(p));
     p.k = d_k_blk;
@@ -707,7 +729,7 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     p.rot = c->rot;
     hipError_t e = kvq::launch_blk_prep(p, D, st);
     if (e != hipSuccess) return fail(KVQ_EHIP, "block rotation launch: %s", hipGetErrorString(e));
-    rot_o = reinterpret_cast<float*>(c->dbuf + c->lay.rotation_offset + align256(2 * blk * 4));
+    rot_o = reinterpret_cast<float*>(rot_ws + align256(2 * blk * 4));
     a.k_blk = p.k_out;
     a.v_blk = p.v_out;
     a.blk_f32 = 1;
@@ -740,6 +762,14 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix, const void* d_q, int
                           float softmax_scale, void* d_out, int32_t out_dtype, void* stream) {
   return block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
                          softmax_scale, d_out, out_dtype, stream, false);
+}
+
+kvq_status kvq_block_attn_noalloc(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
+                                  int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                                  int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,
+                                  void* stream) {
+  return block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
+                         softmax_scale, d_out, out_dtype, stream, false, nullptr, true);
 }
 
 kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,

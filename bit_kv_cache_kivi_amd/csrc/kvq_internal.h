@@ -192,4 +192,10 @@ hipError_t launch_select(const SelArgs& a, int mode, int grid_splits, int B, int
 hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t stream);
 hipError_t launch_unrotate(const UnrotArgs& a, int D, hipStream_t stream);
 
+// The allocation-free attention's workspace: a file-scope device array of
+// kNoAllocScratchBytes (attn.hip), one per device, whose device address is
+// looked up once per device (hipGetSymbolAddress, with that device current).
+constexpr size_t kNoAllocScratchBytes = KVQ_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace kvq

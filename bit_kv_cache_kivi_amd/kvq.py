@@ -68,6 +68,8 @@ def _load():
                                      c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_select": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
                                  c_float, P(ctypes.c_uint32), c_int32, c_int32, c_void_p]),
+        "kvq_block_attn_noalloc": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                             c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_block_attn_selected": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                               c_int32, c_int32, c_float, c_void_p, c_int32, c_void_p]),
         "kvq_attend_commit": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
@@ -278,6 +280,20 @@ class KVCache:
                                  _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
                                  _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
                                  c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
+        return out
+
+    def block_attn_noalloc(self, q, k_blk, v_blk, use_suffix=False, softmax_scale=None, out_dtype=None,
+                           out=None, stream=None):
+        """block_attn with the workspace in the library's per-device scratch
+        array (kvq_block_attn_noalloc): no allocation inside the call; out must
+        be given to avoid one here as well."""
+        out = self._check_attn(q, k_blk, v_blk, out, out_dtype)
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
+        check(lib.kvq_block_attn_noalloc(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
+                                         _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
+                                         _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
+                                         c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(stream)))
         return out
 
     def attend_commit(self, q, k_blk, v_blk, ntok=None, protected=None, use_suffix=False, softmax_scale=None,

@@ -147,7 +147,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 #define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
 #define KVQ_MAX_BATCH 256
 
@@ -264,6 +264,27 @@ kvq_status kvq_block_attn(kvq_cache* c, int32_t use_suffix,
                           const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
                           int32_t block_len, float softmax_scale,
                           void* d_out, int32_t out_dtype, void* stream);
+
+/* kvq_block_attn for callers that cannot allocate or touch workspace they do
+ * not own (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments, kernels and results (outputs
+ * bit-identical to kvq_block_attn's), but the split partials and, with value
+ * rotation, the rotation staging live in a device array owned by the library,
+ * of KVQ_NOALLOC_SCRATCH_BYTES, that each device holds until the process
+ * ends; the cache buffer's workspace region is not touched.  The call
+ * allocates nothing (no hipMalloc, no host allocation).  Every call on one
+ * device shares that array, so calls that overlap on one device (other
+ * streams, other handles, other threads) race and must be ordered by the
+ * caller.  A launch whose workspace would exceed the array returns
+ * KVQ_ECAPACITY before any device work (the default split plan needs at most
+ * 256 workgroups x (Hq/Hkv) x (D + 2) x 32 x 4 bytes, about 34 MB at Hq/Hkv = 8,
+ * D = 128). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+kvq_status kvq_block_attn_noalloc(kvq_cache* c, int32_t use_suffix,
+                                  const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                                  const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                                  int32_t block_len, float softmax_scale,
+                                  void* d_out, int32_t out_dtype, void* stream);
 
 /* Mask-query selection (MaskAhead / Q-MaskAhead abstract: the current block's
  * mask queries rank the cached KV entries by their estimated contribution to

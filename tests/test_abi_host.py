@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(kvq):
     lib = ctypes.CDLL(SO)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
-    assert kvq.lib.kvq_abi_version() == 5
+    assert kvq.lib.kvq_abi_version() == 6
 
 
 def test_layout_matches_documented_record(kvq):
