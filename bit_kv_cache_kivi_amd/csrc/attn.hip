@@ -44,7 +44,6 @@ namespace {
 
 constexpr int kMaxUnits = 256;     // units per split (the host keeps splits within this)
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kMaxSplitsLds = 256;   // splits the combine can merge (host limit on max_splits)
 constexpr int kProducerWaves = 4;
 constexpr int kProducerThreads = kProducerWaves * 64;
 
@@ -949,14 +948,17 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
 // One workgroup per (query head, sequence, 32-channel chunk): merges the
 // splits of all 32 rows for those channels.  Thread -> (query tokens
 // 4jq..4jq+3, one channel), jq fastest, so each 16-byte load of a wave covers
-// whole 128-byte rows of the partials.  The partial-O loads of the first
-// kBatch splits are issued before the merge weights are computed, and the
-// result is transposed through LDS for row-contiguous output stores.
+// whole 128-byte rows of the partials.  Every thread loads, for a batch of up
+// to kBatch splits at once, its partial O values together with the reference
+// maxima and row sums of its four rows (the 32 threads of a row group load
+// the same maxima and sums: one request per wave), so a batch costs one
+// memory latency and no barrier; batches past the first rescale what has
+// been summed when the maximum grows.  The result is transposed through LDS
+// for row-contiguous output stores.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   constexpr int CW = 32;        // channels per workgroup
   constexpr int kBatch = 8;     // splits loaded at once
-  __shared__ __align__(16) float w_lds[kMaxSplitsLds][kSlot];
   __shared__ __align__(16) float out_lds[kSlot][CW + 4];
   const int hq = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * CW;
   // both counts read unconditionally, so the two loads overlap
@@ -970,64 +972,51 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   const size_t pstride = (size_t)r * (D + 2) * kSlot;           // one split's partial
   const float* p0 = a.partial + ((((size_t)b * a.hkv + kvh) * a.max_splits) * r + hl) * (size_t)(D + 2) * kSlot;
   const int jq = tid & 7, c = tid >> 3;
-  const float* pc = p0 + (size_t)(c0 + c) * kSlot + 4 * jq;
-  float4 v[kBatch];
+  const float* po = p0 + (size_t)(c0 + c) * kSlot + 4 * jq;     // O of channel c0 + c, rows 4jq..
+  const float* pm = p0 + (size_t)D * kSlot + 4 * jq;            // maxima, then sums, of the same rows
+  constexpr float kNegInf = -__builtin_inff();
+  float mst[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  float l[4] = {0.f, 0.f, 0.f, 0.f}, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    float4 v[kBatch], mv[kBatch], lv[kBatch];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u)
-    if (u < nsplit) v[u] = *reinterpret_cast<const float4*>(pc + u * pstride);
-  if (tid < kSlot) {
-    // The maxima and sums of kBatch splits are loaded together (indices
-    // clamped, values masked), so each batch costs one memory latency.
-    float mstar = -__builtin_inff();
-    for (int sp0 = 0; sp0 < nsplit; sp0 += kBatch) {
-      float mv[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) mv[u] = p0[min(sp0 + u, nsplit - 1) * pstride + D * kSlot + tid];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) mstar = fmaxf(mstar, mv[u]);   // clamped repeats change no maximum
+    for (int u = 0; u < kBatch; ++u) {
+      const size_t off = (size_t)min(s0 + u, nsplit - 1) * pstride;   // clamped repeats are masked below
+      v[u] = *reinterpret_cast<const float4*>(po + off);
+      mv[u] = *reinterpret_cast<const float4*>(pm + off);
+      lv[u] = *reinterpret_cast<const float4*>(pm + off + kSlot);
     }
-    float l = 0.f;
-    for (int sp0 = 0; sp0 < nsplit; sp0 += kBatch) {
-      float mv[kBatch], lv[kBatch];
+    float mn[4] = {mst[0], mst[1], mst[2], mst[3]};
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float* pm = p0 + min(sp0 + u, nsplit - 1) * pstride + D * kSlot + tid;
-        mv[u] = pm[0];
-        lv[u] = pm[kSlot];
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (sp0 + u < nsplit) {
-          const float w = __builtin_amdgcn_exp2f(mv[u] - mstar);
-          l = fmaf(lv[u], w, l);
-          w_lds[sp0 + u][tid] = w;
-        }
-      }
+    for (int u = 0; u < kBatch; ++u) {          // clamped repeats change no maximum
+      mn[0] = fmaxf(mn[0], mv[u].x); mn[1] = fmaxf(mn[1], mv[u].y);
+      mn[2] = fmaxf(mn[2], mv[u].z); mn[3] = fmaxf(mn[3], mv[u].w);
     }
-    const float inv = 1.0f / l;
-    for (int sp = 0; sp < nsplit; ++sp) w_lds[sp][tid] *= inv;
-  }
-  __syncthreads();
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp0 = 0; sp0 < nsplit; sp0 += kBatch) {
-    if (sp0 > 0) {
+    // a row whose maximum is still -inf has only empty splits so far: weight 0
+    auto wt = [](float m, float ref) __attribute__((always_inline)) {
+      return ref == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - ref);
+    };
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (sp0 + u < nsplit) v[u] = *reinterpret_cast<const float4*>(pc + (sp0 + u) * pstride);
+    for (int k = 0; k < 4; ++k) {
+      const float sc = wt(mst[k], mn[k]);
+      l[k] *= sc;
+      acc[k] *= sc;
+      mst[k] = mn[k];
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (sp0 + u < nsplit) {
-        const float4 wv = *reinterpret_cast<const float4*>(&w_lds[sp0 + u][4 * jq]);
-        acc.x = fmaf(v[u].x, wv.x, acc.x); acc.y = fmaf(v[u].y, wv.y, acc.y);
-        acc.z = fmaf(v[u].z, wv.z, acc.z); acc.w = fmaf(v[u].w, wv.w, acc.w);
+      if (s0 + u < nsplit) {
+        const float w0 = wt(mv[u].x, mst[0]), w1 = wt(mv[u].y, mst[1]);
+        const float w2 = wt(mv[u].z, mst[2]), w3 = wt(mv[u].w, mst[3]);
+        l[0] = fmaf(lv[u].x, w0, l[0]); l[1] = fmaf(lv[u].y, w1, l[1]);
+        l[2] = fmaf(lv[u].z, w2, l[2]); l[3] = fmaf(lv[u].w, w3, l[3]);
+        acc[0] = fmaf(v[u].x, w0, acc[0]); acc[1] = fmaf(v[u].y, w1, acc[1]);
+        acc[2] = fmaf(v[u].z, w2, acc[2]); acc[3] = fmaf(v[u].w, w3, acc[3]);
       }
     }
   }
-  out_lds[4 * jq + 0][c] = acc.x;
-  out_lds[4 * jq + 1][c] = acc.y;
-  out_lds[4 * jq + 2][c] = acc.z;
-  out_lds[4 * jq + 3][c] = acc.w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out_lds[4 * jq + k][c] = acc[k] / l[k];
   __syncthreads();
   // row jj of this head: channels c0 + 4*(tid % 8) .. +3
   const int jj = tid >> 3, cc = 4 * (tid & 7);
