@@ -107,10 +107,68 @@ def cpu_baseline(cfg, w, steps_blocks, budget_s=20.0):
         t_total += time.perf_counter() - t0
         n_done += 1
     qtok = 32 * n_done
+    # the oracle's prefill commit of sequence 0 (all kv heads), best of three,
+    # with the thread pools as they are and limited to one thread
+    def commit_rate():
+        best = float("inf")
+        for _ in range(3):
+            o = O.OracleCache(1, c.Hkv, c.D, c.k_bits, c.v_bits, c.v_group)
+            t0 = time.perf_counter()
+            o.commit(0, w.k_prefix[:1], w.v_prefix[:1], ntok=w.lengths[:1],
+                     prot=[w.prot_prefix[0]] if c.prot_frac else None)
+            best = min(best, time.perf_counter() - t0)
+        return float(w.lengths[0]) / best
+    commit_tps = commit_rate()
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            commit_tps_1 = commit_rate()
+    except Exception:
+        commit_tps_1 = None
     return {"value": qtok / t_total, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_done} step(s) of sequence 0 of {c.B} (all {c.Hq} query heads, prefix "
                       f"{int(w.lengths[0])} tokens): oracle commit of one 32-token block + fp64 attention; "
-                      f"{t_total:.1f} s"}
+                      f"{t_total:.1f} s",
+            "commit_tokens_per_s": commit_tps, "commit_tokens_per_s_1thread": commit_tps_1,
+            "commit_sample": f"oracle prefill commit of sequence 0 ({int(w.lengths[0])} tokens x {c.Hkv} kv heads), "
+                             f"best of 3"}
+
+
+def measured_peaks(lib, torch, num_cus):
+    """Achievable HBM bandwidth (a streaming copy of 1 GiB, larger than the
+    Infinity Cache) and dense fp16 MFMA rate (a loop of independent MFMAs with
+    no memory traffic), timed with HIP events, from the library's calibration
+    kernels."""
+    import ctypes
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        lib.kvq_calib_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n, sp)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        lib.kvq_calib_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    wgs, iters = 2 * num_cus, 4000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    lib.kvq_calib_mfma(ctypes.c_void_p(out.data_ptr()), wgs, iters, sp)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    lib.kvq_calib_mfma(ctypes.c_void_p(out.data_ptr()), wgs, iters, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    flops = float(wgs) * 4 * iters * 8 * 32 * 32 * 16 * 2
+    mfma_tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"hbm_gbs": copy_gbs, "mfma_f16_tflops": mfma_tflops,
+            "how": "streaming copy of 1 GiB (2 x bytes moved per copy); 2 x CUs workgroups of 4 waves, each wave "
+                   f"{iters} x 8 independent v_mfma_f32_32x32x16_f16"}
 
 
 def main():
@@ -349,6 +407,8 @@ def main():
                "attn_full_ms": attn_ms,
                "attn_selected_query_tokens_per_s": c.B * 32 / (attn_sel_ms * 1e-3)}
 
+    peaks = measured_peaks(lib, torch, torch.cuda.get_device_properties(0).multi_processor_count)
+
     qtok = c.B * 32
     attn_s = attn_ms * 1e-3
     achieved_tflops = a_flops / attn_s / 1e12
@@ -392,12 +452,16 @@ def main():
         "prefill_commit_tokens_per_s": float(np.sum(w.lengths)) / (prefill_ms * 1e-3),
         "prefill_commit_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
         "prefill_commit_hbm_frac": prefill_bytes / (prefill_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "prefill_commit_frac_of_measured_hbm": prefill_bytes / (prefill_ms * 1e-3) / 1e9 / peaks["hbm_gbs"],
         "prefill_commit_host_issue_ms": prefill_host_ms,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
         "roofline": {**roof, "traffic": None if (args.v_rotation or args.kv_format != "int") else measured_traffic(c.name),
                      "kernel": "attention launch (attn_kernel + combine_kernel" +
                                (", with blk_prep_kernel and unrotate_kernel)" if args.v_rotation else ")"),
-                     "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS},
+                     "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS,
+                     "measured_peak": peaks,
+                     "frac_of_measured_peak": (achieved_tflops / peaks["mfma_f16_tflops"]) if roof["bound"] == "mfma"
+                                              else (achieved_gbs / peaks["hbm_gbs"])},
     }
     if sel is not None:
         res["selection"] = sel

@@ -23,6 +23,7 @@ SOURCES = {
     # the value rotation must round exactly as written too
     "rotate.hip": ["-ffp-contract=off"],
     "select.hip": [],
+    "calib.hip": [],
     "kvq_host.cpp": [],
 }
 

@@ -21,11 +21,14 @@
 //     contribution per entry, -1 for slot positions past the valid tokens.
 // A workgroup of eight waves loads a unit's record into LDS (the next unit's
 // loads are issued before the current one is processed), dequantizes the keys
-// into fp16 MFMA operand tiles, and wave w runs S^T = K Q^T
-// (v_mfma_f32_32x32x16_f16) for query head w of the group.  The workgroup
-// barriers order LDS only (a plain workgroup barrier would also wait for the
-// prefetch loads in flight).  The ranking only needs
-// the keys to fp16 precision; both passes see the same rounded scores.
+// into the same operands as the attention kernel -- an fp16 hi tile and an
+// e5m2 lo tile of 2^12 (x - hi) -- and wave w runs S^T = K Q^T for query head w
+// of the group: hi on v_mfma_f32_32x32x16_f16, lo against an e4m3 copy of Q on
+// the scaled fp8 MFMA (E8M0 scale 2^-12 on the lo side).  The scores then
+// carry the keys to about 2^-14 of their size, as in attention, so the ranking
+// follows the exact contributions closely.  The workgroup barriers order LDS
+// only (a plain workgroup barrier would also wait for the prefetch loads in
+// flight).
 //
 // topk_kernel then selects, per (sequence, kv head), the k largest
 // contributions exactly (ties to the lower entry) by a four-digit radix select
@@ -69,6 +72,9 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
   static_assert(record_bytes(D, KB, VB, 32) <= 48 * D, "record fits the stage");
   __shared__ __align__(16) uint8_t rec[48 * D];
   __shared__ __align__(16) half8 kt[KS][64];
+  // key lo tiles (e5m2): byte j of lane l of 64-channel block k holds channel
+  // 64k + 32(l/32) + j of token l%32 (the attention kernel's layout)
+  __shared__ __align__(16) uint4 klt[D / 64][2][64];
   __shared__ __align__(16) uint4 prt[kThreads];          // each thread's protected key chunk
   __shared__ float vn[kSlot];
   __shared__ __align__(16) int4 hdrs[kMaxSelSplit];    // the split's unit headers
@@ -96,17 +102,35 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
   const int ci = min(wave, r - 1);
 
   // Q operand of the wave's head (B operand of S^T: lane = query token j,
-  // half hh holds channels (D/2)*hh + 8s + [0, 8) at k-step s)
+  // half hh holds channels (D/2)*hh + 8s + [0, 8) at k-step s), and its e4m3
+  // copy for the lo product (block k holds channels 64k + 32*hh + [0, 32))
+  constexpr int KB8 = D / 64;
   half8 qop[KS];
+  v8i_t q8[KB8];
   {
-    const size_t base = (((size_t)b * kSlot + j) * hq_all + kvh * r + ci) * D + (D / 2) * hh;
+    const size_t row = (((size_t)b * kSlot + j) * hq_all + kvh * r + ci) * D;
+    const size_t base = row + (D / 2) * hh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       float x[8];
       load8(a.q, base + 8 * s, a.q_f32, x);
       qop[s] = to_half8(x);
     }
+#pragma unroll
+    for (int k = 0; k < KB8; ++k) {
+#pragma unroll
+      for (int w4 = 0; w4 < 8; ++w4) {
+        float x[4];
+        const size_t e0 = row + 64 * k + 32 * hh + 4 * w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = load1(a.q, e0 + e, a.q_f32);
+        uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
+        q8[k][w4] = (int)d;
+      }
+    }
   }
+  const float neg_one = opaque_neg_one();
 
   // running statistics (MODE 0) or the merged normaliser (MODE 1)
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -220,7 +244,10 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], km[e], km[D + e]);
       }
-      kt[kks][t + 32 * khh] = to_half8(x);
+      const int cg = kcg;
+      store_hi_lo8(kt[kks][t + 32 * khh],
+                   reinterpret_cast<uint2*>(&klt[cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1], x,
+                   neg_one);
     }
     if (MODE == 1) {
       // value norms: token t, channels [cs * VCH, +VCH) of one value group
@@ -261,6 +288,14 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
       for (int s = 0; s < KS; ++s)
         sacc = MODE == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(kt[s][lane], qop[s], sacc, 0, 0, 0)
                          : __builtin_amdgcn_mfma_f32_32x32x16_f16(qop[s], kt[s][lane], sacc, 0, 0, 0);
+      // + 2^-12 K_lo' Q8^T (bf8 x e4m3; the E8M0 scale 2^-12 on the lo side)
+#pragma unroll
+      for (int k = 0; k < KB8; ++k) {
+        const uint4 l0 = klt[k][0][lane], l1 = klt[k][1][lane];
+        const v8i_t kl = v8i_t{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+        sacc = MODE == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl, q8[k], sacc, 1, 0, 0, 127 - 12, 0, 127)
+                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q8[k], kl, sacc, 0, 1, 0, 127, 0, 127 - 12);
+      }
       if (MODE == 0) {
         float sv[16], mx = -__builtin_inff();
 #pragma unroll

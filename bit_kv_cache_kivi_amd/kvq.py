@@ -81,6 +81,8 @@ def _load():
         "kvq_status_str": (c_char_p, [c_int32]),
         "kvq_last_error": (c_char_p, []),
         "kvq_abi_version": (c_int32, []),
+        "kvq_calib_copy": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
+        "kvq_calib_mfma": (c_int32, [c_void_p, c_int32, c_int32, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -375,6 +375,20 @@ const char* kvq_status_str(kvq_status s);
 const char* kvq_last_error(void);
 int32_t kvq_abi_version(void);
 
+/* Calibration kernels, used to report measured achievable peaks beside the
+ * published ones; they are not part of the method.
+ *   kvq_calib_copy: copies `bytes` (a multiple of 16; both pointers 16-byte
+ *     aligned device memory) from d_src to d_dst with a streaming grid-stride
+ *     kernel; timing it gives the achievable HBM bandwidth (2 * bytes moved).
+ *   kvq_calib_mfma: `workgroups` workgroups of four waves, each wave issuing
+ *     iters x 8 independent v_mfma_f32_32x32x16_f16 (32768 flops each) with no
+ *     memory traffic, and one float per thread to d_out (workgroups * 256
+ *     floats); timing it gives the achievable dense fp16 MFMA rate.
+ * Asynchronous on `stream`; KVQ_EINVAL for bad arguments, KVQ_EHIP if the
+ * launch fails. */
+kvq_status kvq_calib_copy(void* d_dst, const void* d_src, size_t bytes, void* stream);
+kvq_status kvq_calib_mfma(float* d_out, int32_t workgroups, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,10 +1,12 @@
 """GPU parity of the mask-query selection (MaskAhead / Q-MaskAhead abstract):
-contributions against the fp64 oracle, the top-k selection exact on the GPU's
-own contributions (integer work: masks, unit lists and counts bit-exact against
-a NumPy top-k with ties to the lower entry), the selection valid against the
-oracle's ranking up to the contribution tolerance, and attention over the
-selection within the attention gate of the oracle's attention over the same
-entries."""
+contributions against the fp64 oracle (within 2e-3 relative: the scores use
+the attention kernel's hi + lo key operands), the top-k selection exact on the
+GPU's own contributions (integer work: masks, unit lists and counts bit-exact
+against a NumPy top-k with ties to the lower entry), the selection equal to the
+oracle's exact top-k wherever the k-th and (k+1)-th oracle values are further
+apart than twice the measured contribution error (and valid within that error
+elsewhere), and attention over the selection within the attention gate of the
+oracle's attention over the same entries."""
 import dataclasses
 
 import numpy as np
@@ -44,10 +46,13 @@ def check_selection(cache, ora, w, budget, use_suffix, qmask, granularity=1):
             got = contrib[ids].astype(np.float64)
             scale = max(cref.max(), 1e-30)
             err = np.abs(got - cref)
-            assert np.all(err <= 1e-2 * cref + 1e-4 * scale), (b, h, float((err - 1e-2 * cref).max() / scale))
+            assert np.all(err <= 2e-3 * cref + 1e-5 * scale), (b, h, float((err - 2e-3 * cref).max() / scale))
+            eabs = float(err.max())
             # unit sums against the oracle's sums of its entry contributions
             uref = np.bincount(ids // SLOT, weights=cref, minlength=nu)
-            assert np.all(np.abs(usums.astype(np.float64) - uref) <= 1e-2 * uref + 1e-4 * uref.max()), (b, h)
+            uerr = np.abs(usums.astype(np.float64) - uref)
+            assert np.all(uerr <= 2e-3 * uref + 1e-5 * uref.max()), (b, h)
+            ueabs = float(uerr.max())
             sel = np.flatnonzero(np.unpackbits(masks.view(np.uint8), bitorder="little"))
             nz = np.flatnonzero(masks != 0)
             assert np.array_equal(units, nz), (b, h)
@@ -55,11 +60,17 @@ def check_selection(cache, ora, w, budget, use_suffix, qmask, granularity=1):
                 # the GPU's top-k of its own contributions: bit-exact
                 want = select_topk(ids, got, budget)
                 assert np.array_equal(sel, want), (b, h, len(sel), len(want))
-                # valid against the oracle: nothing left out is clearly better than what was kept
+                # against the oracle's exact top-k: equal where the cut is wider
+                # than the contribution error, and otherwise nothing left out
+                # beats what was kept by more than that error
                 if 0 < len(sel) < len(ids):
+                    srt = np.sort(cref)[::-1]
+                    k = len(sel)
+                    if srt[k - 1] - srt[k] > 2 * eabs:
+                        assert np.array_equal(sel, select_topk(ids, cref, budget)), (b, h, "oracle top-k")
                     kept = cref[np.isin(ids, sel)]
                     left = cref[~np.isin(ids, sel)]
-                    assert kept.min() >= left.max() - 2e-2 * scale, (b, h, kept.min(), left.max())
+                    assert kept.min() >= left.max() - 2 * eabs, (b, h, kept.min(), left.max())
             else:
                 # top units of the GPU's own unit sums (ties to the lower unit), all their valid entries
                 order = np.lexsort((np.arange(nu), -usums.astype(np.float64)))
@@ -67,9 +78,14 @@ def check_selection(cache, ora, w, budget, use_suffix, qmask, granularity=1):
                 want = np.sort(ids[np.isin(ids // SLOT, keep)])
                 assert np.array_equal(sel, want), (b, h, len(sel), len(want))
                 if 0 < len(keep) < nu:
+                    srt = np.sort(uref)[::-1]
+                    k = len(keep)
+                    if srt[k - 1] - srt[k] > 2 * ueabs:
+                        ok = np.sort(np.lexsort((np.arange(nu), -uref))[:k])
+                        assert np.array_equal(keep, ok), (b, h, "oracle top units")
                     kept = uref[keep]
                     left = np.delete(uref, keep)
-                    assert kept.min() >= left.max() - 2e-2 * uref.max(), (b, h)
+                    assert kept.min() >= left.max() - 2 * ueabs, (b, h)
             selected[(b, h)] = sel
     return selected
 
