@@ -50,6 +50,15 @@ constexpr int kProducerThreads = kProducerWaves * 64;
 template <class T>
 __device__ __forceinline__ T pick(bool c, T x, T y) { return c ? x : y; }
 
+// A split's partial for a 16-bit output: O normalised by the split's sum, as
+// fp16 quads [D / 4][32 rows][4 channels], then per row the reference
+// maximum, the sum and the power of two the row was scaled by (int32).
+template <int D>
+struct PartialH16 {
+  static constexpr size_t kStats = (size_t)D * kSlot * 2;
+  static constexpr size_t kBytes = kStats + 3 * kSlot * 4;
+};
+
 template <int D>
 struct Shape {
   static constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
@@ -927,6 +936,40 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + c) = w;
         }
       }
+  } else if (!a.out_f32) {
+    // 16-bit output: the split's O normalised by its own sum and scaled by a
+    // power of two per row (row maximum in [2^14, 2^15)), in fp16, so the
+    // hand-off to the combine costs half the bytes of fp32 and its rounding
+    // (at most 2^-11 of the row maximum) stays below the bf16 output's
+    const size_t pidx = (((size_t)b * hkv + kvh) * a.max_splits + split) * r + ci;
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.partial) + pidx * PartialH16<D>::kBytes;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    float mx = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(o[ct][i]));
+    const int sh = 15 - __builtin_amdgcn_frexp_expf(max_halves(mx) * inv);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int cq = 8 * ct + 2 * qd + hh;      // channels 4cq .. 4cq+3
+        const _Float16 h0 = (_Float16)__builtin_amdgcn_ldexpf(o[ct][4 * qd] * inv, sh);
+        const _Float16 h1 = (_Float16)__builtin_amdgcn_ldexpf(o[ct][4 * qd + 1] * inv, sh);
+        const _Float16 h2 = (_Float16)__builtin_amdgcn_ldexpf(o[ct][4 * qd + 2] * inv, sh);
+        const _Float16 h3 = (_Float16)__builtin_amdgcn_ldexpf(o[ct][4 * qd + 3] * inv, sh);
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+        *reinterpret_cast<uint2*>(base + ((size_t)cq * kSlot + j) * 8) = w;
+      }
+    if (hh == 0) {
+      float* stats = reinterpret_cast<float*>(base + PartialH16<D>::kStats);
+      stats[j] = m_ref;
+      stats[kSlot + j] = l_tot;
+      stats[2 * kSlot + j] = __int_as_float(-sh);
+    }
   } else {
     const size_t pidx = (((size_t)b * hkv + kvh) * a.max_splits + split) * r + ci;
     float* base = a.partial + pidx * (size_t)(D + 2) * kSlot;
@@ -1032,6 +1075,81 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   }
 }
 
+// The same merge over fp16 partials (16-bit output).  Thread -> (query token
+// j, channel quad q), j fastest, so each 8-byte load of a wave covers two
+// whole quads of 32 rows (512 contiguous bytes).  A split's weight is its sum
+// times 2^(m - max), times the power of two its row was scaled by.
+template <int D>
+__global__ __launch_bounds__(256) void combine_h16_kernel(const AttnArgs a) {
+  constexpr int CW = 32;        // channels per workgroup
+  constexpr int kBatch = 8;     // splits loaded at once
+  __shared__ __align__(16) float out_lds[kSlot][CW + 4];
+  const int hq = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * CW;
+  const int np = a.nslots[0][b], ns_all = a.nslots[1][b];
+  const int ns = a.use_suffix ? ns_all : 0;
+  const int r = a.r, kvh = hq / r, hl = hq % r;
+  const int U = (a.sel_count ? a.sel_count[b * a.hkv + kvh] : np + ns) + 1;
+  const int nsplit = (U + a.split_units - 1) / a.split_units;
+  if (nsplit <= 1) return;
+  const int tid = threadIdx.x;
+  const int j = tid & 31, q = tid >> 5;
+  const size_t pstride = (size_t)r * PartialH16<D>::kBytes;     // one split's partials
+  const uint8_t* p0 = reinterpret_cast<const uint8_t*>(a.partial) +
+                      ((((size_t)b * a.hkv + kvh) * a.max_splits) * r + hl) * PartialH16<D>::kBytes;
+  const uint8_t* po = p0 + ((size_t)(c0 / 4 + q) * kSlot + j) * 8;
+  const float* ps = reinterpret_cast<const float*>(p0 + PartialH16<D>::kStats) + j;
+  constexpr float kNegInf = -__builtin_inff();
+  float mst = kNegInf, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto wt = [](float m, float ref) __attribute__((always_inline)) {
+    return ref == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - ref);
+  };
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    uint2 v[kBatch];
+    float mv[kBatch], lv[kBatch];
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const size_t off = (size_t)min(s0 + u, nsplit - 1) * pstride;   // clamped repeats are masked below
+      v[u] = *reinterpret_cast<const uint2*>(po + off);
+      const float* st = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ps) + off);
+      mv[u] = st[0];
+      lv[u] = st[kSlot];
+      ev[u] = __float_as_int(st[2 * kSlot]);
+    }
+    float mn = mst;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mn = fmaxf(mn, mv[u]);   // clamped repeats change no maximum
+    const float sc = wt(mst, mn);
+    l *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] *= sc;
+    mst = mn;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + u < nsplit) {
+        const float w = wt(mv[u], mst) * lv[u];
+        const float wo = __builtin_amdgcn_ldexpf(w, ev[u]);
+        l += w;
+        acc[0] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu)), wo, acc[0]);
+        acc[1] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x >> 16)), wo, acc[1]);
+        acc[2] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y & 0xFFFFu)), wo, acc[2]);
+        acc[3] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y >> 16)), wo, acc[3]);
+      }
+    }
+  }
+  const float inv = 1.0f / l;
+  *reinterpret_cast<float4*>(&out_lds[j][4 * q]) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  __syncthreads();
+  // row jj of this head: channels c0 + 4*(tid % 8) .. +3
+  const int jj = tid >> 3, cc = 4 * (tid & 7);
+  const size_t o = (((size_t)b * kSlot + jj) * a.hq + hq) * D + c0 + cc;
+  const float4 res = *reinterpret_cast<const float4*>(&out_lds[jj][cc]);
+  uint2 w;
+  w.x = f32_to_bf16_bits(res.x) | (f32_to_bf16_bits(res.y) << 16);
+  w.y = f32_to_bf16_bits(res.z) | (f32_to_bf16_bits(res.w) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
+}
+
 template <int KB, int VB, int D>
 hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
   const dim3 grid = a.num_wg ? dim3(a.num_wg) : dim3(grid_splits, a.hkv, B);
@@ -1057,7 +1175,8 @@ hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_splits <= 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
+  if (a.out_f32) hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
+  else           hipLaunchKernelGGL((combine_h16_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

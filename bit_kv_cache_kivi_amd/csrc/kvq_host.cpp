@@ -701,13 +701,33 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     for (int b = 0; b < B; ++b) n += (int64_t)H * ((ub[b] + split_units - 1) / split_units);
     a.num_wg = 0;
     if (n <= kvq::kMaxWgTable && grid_splits <= 256 && H <= 256) {
-      int i = 0;
+      // Workgroup i starts on XCD i % kXcds.  All splits of one (sequence,
+      // kv head) go to one XCD, so the block's queries (read by every split)
+      // come from HBM once and from that XCD's L2 after: each (sequence, kv
+      // head) joins the XCD with the fewest workgroups so far, and the table
+      // interleaves the XCDs' lists (a list that runs out early is filled
+      // from the longest one).
+      constexpr int kXcds = 8;
+      uint32_t bin[kXcds][kvq::kMaxWgTable];
+      int cnt[kXcds] = {0}, next[kXcds] = {0};
       for (int b = 0; b < B; ++b) {
         const int ns = (ub[b] + split_units - 1) / split_units;
-        for (int h = 0; h < H; ++h)
-          for (int sp = 0; sp < ns; ++sp) a.wg[i++] = (uint32_t)sp | ((uint32_t)h << 8) | ((uint32_t)b << 16);
+        for (int h = 0; h < H; ++h) {
+          int x = 0;
+          for (int y = 1; y < kXcds; ++y)
+            if (cnt[y] < cnt[x]) x = y;
+          for (int sp = 0; sp < ns; ++sp) bin[x][cnt[x]++] = (uint32_t)sp | ((uint32_t)h << 8) | ((uint32_t)b << 16);
+        }
       }
-      a.num_wg = i;
+      for (int i = 0; i < (int)n; ++i) {
+        int x = i % kXcds;
+        if (next[x] == cnt[x]) {
+          for (int y = 0; y < kXcds; ++y)
+            if (cnt[y] - next[y] > cnt[x] - next[x]) x = y;
+        }
+        a.wg[i] = bin[x][next[x]++];
+      }
+      a.num_wg = (int32_t)n;
     }
   }
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -239,3 +239,38 @@ def test_sink_protection():
     out = cache.block_attn(dev(q, "f32"), dev(kb, "f32"), dev(vb, "f32"), use_suffix=True, out_dtype=torch.float32)
     e, x = attention_error(out, ref, "f32")
     assert x <= 0, e
+
+
+@pytest.mark.parametrize("vscale_log2", [0, 13, -10])
+def test_bf16_output_split_partials_at_any_magnitude(vscale_log2):
+    """With a 16-bit output the splits hand their normalised O to the combine
+    in fp16, each row scaled by a power of two: values scaled by 2^13 (near
+    the top of the fp16 operand range the inputs must keep to) and by 2^-10
+    come out with the same relative error as unit values, over several split
+    counts.  (Far smaller values keep the absolute bound only: the value
+    operand itself is fp16, whose normal range ends at 2^-14.)"""
+    announce("bf16 split partials, values x 2^", vscale_log2)
+    g = np.random.default_rng(40 + vscale_log2)
+    B, H, r, D, T = 2, 2, 4, 128, 700
+    sc = np.float32(2.0 ** vscale_log2)
+    k = g.standard_normal((B, T, H, D)).astype(np.float32)
+    v = (g.standard_normal((B, T, H, D)) * sc).astype(np.float32)
+    q = g.standard_normal((B, 32, H * r, D)).astype(np.float32)
+    kb = g.standard_normal((B, 32, H, D)).astype(np.float32)
+    vb = (g.standard_normal((B, 32, H, D)) * sc).astype(np.float32)
+    # one query row with a peaked softmax: its O is one value row, the
+    # largest |O| a split can hand over
+    q[0, 5, 0] = 12.0 * k[0, 100, 0]
+    k, v, q, kb, vb = (O.to_bf16_f32(x) for x in (k, v, q, kb, vb))
+    cache = kvq.KVCache(B, H, D, 4, 4, 128, prefix_tokens=T + 32, max_q_heads=H * r)
+    ora = O.OracleCache(B, H, D, 4, 4, 128)
+    cache.commit(dev(k, "bf16"), dev(v, "bf16"))
+    ora.commit(0, k, v)
+    ref = O.block_attention(ora, q, kb, vb) / float(sc)
+    for split in (1, 2, 3, 7, 0):
+        cache.set_split_slots(split)
+        out = cache.block_attn(dev(q, "bf16"), dev(kb, "bf16"), dev(vb, "bf16"), out_dtype=torch.bfloat16)
+        assert torch.isfinite(out).all()
+        e, x = attention_error(out.float() / float(sc), ref, "bf16")
+        print(f"x2^{vscale_log2} split={split}: err/scale={e:.2e}")
+        assert x <= 0, (split, e)
