@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -129,21 +130,9 @@ struct kvq_cache {
   uint8_t* dbuf;
   SegMirror seg[2];
   int32_t split_slots = 0;
-  // Ring of kStageRing task tables in pinned host memory (created by the first
-  // commit of more than kInlineTasks slots): such a commit's kernel reads its
-  // table straight from host memory (each workgroup's first tasks in one
-  // parallel read), so no copy operation sits on the stream ahead of the
-  // kernel.  ev[k] marks the end of the last kernel that read table k; a
-  // commit blocks the calling thread only when it needs a table whose kernel
-  // has not finished, i.e. when kStageRing large commits are still in flight.
-  static constexpr int kStageRing = 4;
   bool dev_ready = false;
-  bool stage_ready = false;
-  uint8_t* h_stage = nullptr;
-  size_t task_bytes = 0;           // one table: B * max(slot capacity) tasks
-  hipEvent_t ev[kStageRing] = {};
-  bool ev_used[kStageRing] = {};
-  int next_stage = 0;
+  int device = 0;                  // the device current at the first device call
+  size_t task_bytes = 0;           // the largest task table of this handle
   int num_cus = 0;                 // compute units of the device (sizes the grids)
   std::vector<CommitTask> tasks;
   kvq::RotParams rot{};            // value rotation (rot.block == 0 until set)
@@ -155,53 +144,90 @@ struct kvq_cache {
 
 namespace {
 
+
+// Task tables of large commits, in pinned host memory shared by every handle
+// on a device: the commit kernel reads its table straight from host memory
+// (each workgroup's first tasks in one parallel read), so no copy operation
+// sits on the stream ahead of it.  One ring per device, so that the tables a
+// process rewrites stay in the CPU's caches however many handles (one per
+// layer, say) take turns: a table written cold costs a memory round trip per
+// line, tens of microseconds for a prefill's table.  ev[k] marks the end of
+// the last kernel that read table k; a commit blocks its thread only when the
+// table it needs is still being read, i.e. when kSlots large commits are in
+// flight on the device.  Grown (after every table's kernel has finished) to
+// the largest table a handle can need; held until the process ends.
+struct StageRing {
+  static constexpr int kSlots = 8;
+  std::mutex mu;
+  uint8_t* h = nullptr;
+  size_t slot_bytes = 0;
+  hipEvent_t ev[kSlots] = {};
+  bool used[kSlots] = {};
+  int next = 0;
+};
+constexpr int kMaxDevices = 64;
+
+StageRing& stage_ring(int dev) {
+  static StageRing rings[kMaxDevices];
+  return rings[dev];
+}
+
+// With R.mu held: a slot of at least `bytes`, free for rewriting.
+kvq_status ring_slot(StageRing& R, size_t bytes, uint8_t** slot, int* k) {
+  hipError_t e = hipSuccess;
+  if (!R.ev[0]) {
+    for (int i = 0; i < StageRing::kSlots; ++i) {
+      e = hipEventCreateWithFlags(&R.ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(R.ev[j]);
+        for (int j = 0; j < StageRing::kSlots; ++j) R.ev[j] = nullptr;
+        return fail(KVQ_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+      }
+    }
+  }
+  if (bytes > R.slot_bytes) {
+    for (int i = 0; i < StageRing::kSlots; ++i) {
+      if (R.used[i]) {
+        e = hipEventSynchronize(R.ev[i]);
+        if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+        R.used[i] = false;
+      }
+    }
+    if (R.h) (void)hipHostFree(R.h);
+    R.h = nullptr;
+    R.slot_bytes = 0;
+    e = hipHostMalloc(reinterpret_cast<void**>(&R.h), StageRing::kSlots * bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      R.h = nullptr;
+      return fail(KVQ_EHIP, "hipHostMalloc: %s", hipGetErrorString(e));
+    }
+    R.slot_bytes = bytes;
+    R.next = 0;
+  }
+  const int i = R.next;
+  if (R.used[i]) {
+    e = hipEventSynchronize(R.ev[i]);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    R.used[i] = false;
+  }
+  *slot = R.h + (size_t)i * R.slot_bytes;
+  *k = i;
+  return KVQ_OK;
+}
+
 // Device properties the launches need; allocates nothing.
 kvq_status ensure_device(kvq_cache* c) {
   if (c->dev_ready) return KVQ_OK;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c->num_cus <= 0)
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_EUNSUPPORTED, "device %d (this library handles 0..%d)", dev, kMaxDevices - 1);
+  if (hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c->num_cus <= 0)
     c->num_cus = 256;
-  c->dev_ready = true;
-  return KVQ_OK;
-}
-
-void release_stage(kvq_cache* c) {
-  for (int i = 0; i < kvq_cache::kStageRing; ++i) {
-    if (c->ev[i]) {
-      if (c->ev_used[i]) hipEventSynchronize(c->ev[i]);
-      hipEventDestroy(c->ev[i]);
-      c->ev[i] = nullptr;
-    }
-    c->ev_used[i] = false;
-  }
-  if (c->h_stage) hipHostFree(c->h_stage);
-  c->h_stage = nullptr;
-  c->stage_ready = false;
-}
-
-// The pinned task-table ring of large commits (allocated once per handle;
-// on failure nothing stays allocated).
-kvq_status ensure_stage(kvq_cache* c) {
-  if (c->stage_ready) return KVQ_OK;
   const size_t maxcap = std::max(c->cfg.prefix_slots, c->cfg.suffix_slots);
   c->task_bytes = ((size_t)c->cfg.batch * maxcap * sizeof(CommitTask) + 255) & ~(size_t)255;
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&c->h_stage), kvq_cache::kStageRing * c->task_bytes,
-                               hipHostMallocDefault);
-  if (e != hipSuccess) {
-    c->h_stage = nullptr;
-    return fail(KVQ_EHIP, "hipHostMalloc: %s", hipGetErrorString(e));
-  }
-  for (int i = 0; i < kvq_cache::kStageRing; ++i) {
-    e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
-    if (e != hipSuccess) {
-      c->ev[i] = nullptr;
-      release_stage(c);
-      return fail(KVQ_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
-    }
-  }
-  c->next_stage = 0;
-  c->stage_ready = true;
+  c->device = dev;
+  c->dev_ready = true;
   return KVQ_OK;
 }
 
@@ -278,7 +304,6 @@ kvq_status kvq_create(const kvq_config* cfg, void* d_buf, size_t buf_bytes, kvq_
 
 kvq_status kvq_destroy(kvq_cache* c) {
   if (!c) return KVQ_OK;
-  release_stage(c);
   delete c;
   return KVQ_OK;
 }
@@ -375,11 +400,22 @@ kvq_status commit_plan(kvq_cache* c, int32_t segment, int32_t reset_segment, con
     for (int b = 0; b < B; ++b) {
       if (h_prot_off[b + 1] < h_prot_off[b]) return fail(KVQ_EINVAL, "h_prot_off decreases at %d", b);
       if (h_prot_off[b + 1] > h_prot_off[b] && !h_prot_idx) return fail(KVQ_EINVAL, "h_prot_idx is NULL");
+      // one branch-free pass: position i must lie in prev + 1 .. ntok - 1
+      uint32_t bad = 0;
+      int lo = 0;
       for (int i = h_prot_off[b]; i < h_prot_off[b + 1]; ++i) {
         const int p = h_prot_idx[i];
-        if (p < 0 || p >= ntok[b]) return fail(KVQ_EINVAL, "protected position %d of sequence %d outside 0..%d", p, b, ntok[b] - 1);
-        if (i > h_prot_off[b] && p <= h_prot_idx[i - 1])
-          return fail(KVQ_EINVAL, "protected positions of sequence %d are not strictly increasing", b);
+        bad |= (uint32_t)((uint32_t)p - (uint32_t)lo >= (uint32_t)ntok[b] - (uint32_t)lo);
+        lo = p + 1;
+      }
+      if (bad) {
+        for (int i = h_prot_off[b]; i < h_prot_off[b + 1]; ++i) {
+          const int p = h_prot_idx[i];
+          if (p < 0 || p >= ntok[b])
+            return fail(KVQ_EINVAL, "protected position %d of sequence %d outside 0..%d", p, b, ntok[b] - 1);
+          if (i > h_prot_off[b] && p <= h_prot_idx[i - 1])
+            return fail(KVQ_EINVAL, "protected positions of sequence %d are not strictly increasing", b);
+        }
       }
     }
   }
@@ -416,32 +452,40 @@ kvq_status commit_plan(kvq_cache* c, int32_t segment, int32_t reset_segment, con
   }
 
   // ---- task table
+  // one task per 32-token slot; the protected positions (validated above)
+  // set their slot's mask bits, and a slot's first rank is the running count
   auto& tasks = c->tasks;
-  tasks.clear();
+  size_t ntasks = 0;
+  for (int b = 0; b < B; ++b) ntasks += (size_t)((ntok[b] + kvq::kSlot - 1) / kvq::kSlot);
+  tasks.resize(ntasks);
+  size_t t0 = 0;
   for (int b = 0; b < B; ++b) {
     const int base_slots = reset_segment ? 0 : m.nslots[b];
-    int rank = reset_segment ? 0 : m.nprot[b];
     const int tok0 = reset_segment ? 0 : m.ntok[b];
-    const int* pidx = h_prot_off ? h_prot_idx + h_prot_off[b] : nullptr;
-    const int np = h_prot_off ? h_prot_off[b + 1] - h_prot_off[b] : 0;
-    int pi = 0;
-    for (int j = 0; j * kvq::kSlot < ntok[b]; ++j) {
-      CommitTask t;
+    const int nsl = (ntok[b] + kvq::kSlot - 1) / kvq::kSlot;
+    CommitTask* tb = tasks.data() + t0;
+    for (int j = 0; j < nsl; ++j) {
+      CommitTask& t = tb[j];
       t.b = b;
       t.dst_slot = base_slots + j;
       t.src_tok = j * kvq::kSlot;
       t.nvalid = std::min(kvq::kSlot, ntok[b] - t.src_tok);
       t.mask = 0;
-      t.rank_base = rank;
       t.token_base = tok0 + t.src_tok;
       t.pad = 0;
-      while (pi < np && pidx[pi] < t.src_tok + t.nvalid) {
-        t.mask |= 1u << (pidx[pi] - t.src_tok);
-        ++pi;
-        ++rank;
-      }
-      tasks.push_back(t);
     }
+    if (h_prot_off) {
+      for (int i = h_prot_off[b]; i < h_prot_off[b + 1]; ++i) {
+        const int p = h_prot_idx[i];
+        tb[p / kvq::kSlot].mask |= 1u << (p % kvq::kSlot);
+      }
+    }
+    int rank = reset_segment ? 0 : m.nprot[b];
+    for (int j = 0; j < nsl; ++j) {
+      tb[j].rank_base = rank;
+      rank += __builtin_popcount(tb[j].mask);
+    }
+    t0 += (size_t)nsl;
   }
   plan.segment = segment;
   plan.reset = reset_segment;
@@ -470,25 +514,25 @@ kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
   if (!tasks.empty()) {
     kvq_status s = ensure_device(c);
     if (s != KVQ_OK) return s;
-    if ((int)tasks.size() > kvq::kInlineTasks) {
-      s = ensure_stage(c);
-      if (s != KVQ_OK) return s;
-    }
     kvq::CommitArgs a;          // about 2 KB with the inline task table; the launch copies it
     memset(&a, 0, sizeof(a));
     hipError_t e = hipSuccess;
+    // large commits: the ring's lock is held from taking a table to recording
+    // its event, so tables and events are handed out in launch order
+    std::unique_lock<std::mutex> lock;
+    StageRing* ring = nullptr;
+    int slot = -1;
     if ((int)tasks.size() <= kvq::kInlineTasks) {
       // small commits (one block per sequence) pass the tasks by value
       a.use_inline = 1;
       memcpy(a.inline_tasks, tasks.data(), tasks.size() * sizeof(CommitTask));
       a.tasks = nullptr;
     } else {
-      const int k = c->next_stage;
-      if (c->ev_used[k]) {
-        e = hipEventSynchronize(c->ev[k]);
-        if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventSynchronize: %s", hipGetErrorString(e));
-      }
-      uint8_t* hs = c->h_stage + k * c->task_bytes;
+      ring = &stage_ring(c->device);
+      lock = std::unique_lock<std::mutex>(ring->mu);
+      uint8_t* hs = nullptr;
+      s = ring_slot(*ring, std::max(c->task_bytes, tasks.size() * sizeof(CommitTask)), &hs, &slot);
+      if (s != KVQ_OK) return s;
       memcpy(hs, tasks.data(), tasks.size() * sizeof(CommitTask));
       a.use_inline = 0;
       a.tasks = reinterpret_cast<const CommitTask*>(hs);   // device-accessible pinned memory
@@ -505,12 +549,11 @@ kvq_status commit_run(kvq_cache* c, const CommitPlan& plan, hipStream_t st) {
     a.record_bytes = (uint32_t)c->lay.record_bytes;
     e = kvq::launch_commit(a, (int)tasks.size(), cfg.head_dim, cfg.k_bits, cfg.v_bits, in_dtype == KVQ_F32, st);
     if (e != hipSuccess) return fail(KVQ_EHIP, "commit launch: %s", hipGetErrorString(e));
-    if (!a.use_inline) {
-      const int k = c->next_stage;
-      e = hipEventRecord(c->ev[k], st);
+    if (ring) {
+      e = hipEventRecord(ring->ev[slot], st);
       if (e != hipSuccess) return fail(KVQ_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-      c->ev_used[k] = true;
-      c->next_stage = (k + 1) % kvq_cache::kStageRing;
+      ring->used[slot] = true;
+      ring->next = (slot + 1) % StageRing::kSlots;
     }
   }
 

@@ -45,17 +45,22 @@
  * ------------------------------------------------------------------------
  *  - The caller owns all device memory: the cache buffer handed to kvq_create
  *    (kvq_required_bytes bytes, 256-byte aligned), inputs and outputs.  The
- *    library never allocates device memory.  The first commit of more than 64
- *    slots on a handle allocates a small pinned host ring of four commit task
- *    tables (read by the commit kernel directly from host memory) and four
- *    events; kvq_destroy frees them.  No other call allocates anything.
+ *    library never allocates device memory.  Commits of more than 64 slots
+ *    take their task table from a ring of eight pinned host tables (read by
+ *    the commit kernel directly from host memory) with eight events, one ring
+ *    per device shared by every handle and thread (calls on it are
+ *    serialised by a lock), created by the first such commit, grown to the
+ *    largest table a handle needs (32 bytes x batch x the larger segment's
+ *    slot capacity, per table) and held until the process ends.  No other
+ *    call allocates anything.
  *  - Pointers named d_* are device pointers; h_* are host pointers read only
  *    during the call.  `stream` is a hipStream_t (NULL = default stream).
  *  - Calls are asynchronous and stream-ordered, with one exception: a commit of
- *    more than 64 slots (a prefill) reuses one of the four pinned task tables
+ *    more than 64 slots (a prefill) reuses one of the eight pinned task tables
  *    and blocks the calling thread until the kernel that last read that table
- *    has finished, i.e. only while four such commits on the handle are still
- *    in flight on the device.  All calls on one handle must be
+ *    has finished, i.e. only while eight such commits (of any handle) are
+ *    still in flight on the device; growing the ring waits for all eight.
+ *    All calls on one handle must be
  *    issued on one stream or be ordered by the caller.  A handle is not
  *    thread-safe.
  *  - Every call returns a kvq_status.  All argument checks run on the host
@@ -230,8 +235,8 @@ kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out);
  * starts empty; nothing in d_buf needs initialising. */
 kvq_status kvq_create(const kvq_config* cfg, void* d_buf, size_t buf_bytes, kvq_cache** out);
 
-/* Frees the host-side handle and its pinned task-table ring.  Waits for the
- * handle's outstanding commit kernels that read the ring.  NULL is accepted. */
+/* Frees the host-side handle (host memory only; the device's shared task-table
+ * ring stays).  Waits for nothing.  NULL is accepted. */
 kvq_status kvq_destroy(kvq_cache* c);
 
 /* Quantize-on-commit.  Appends, for every sequence b, the first h_ntok[b]
