@@ -47,9 +47,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "769bceb69f4dd72284d5741e1ca6fd076ebe4272aac43a5975d64d0755f2924d",
-        "kib": {"attn_kernel": {"fetch": 33525, "write": 29120},
-                "combine_kernel": {"fetch": 14609, "write": 1792}},
+        "attn_source_sha256": "18928d504c737e05f71043846e9894fb971b44f1f5ef9dc6d074939f428c353e",
+        "kib": {"attn_kernel": {"fetch": 27226, "write": 15010},
+                "combine_h16_kernel": {"fetch": 7535.5, "write": 1792}},
     },
 }
 
@@ -456,7 +456,7 @@ def main():
         "prefill_commit_host_issue_ms": prefill_host_ms,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
         "roofline": {**roof, "traffic": None if (args.v_rotation or args.kv_format != "int") else measured_traffic(c.name),
-                     "kernel": "attention launch (attn_kernel + combine_kernel" +
+                     "kernel": "attention launch (attn_kernel + combine_h16_kernel" +
                                (", with blk_prep_kernel and unrotate_kernel)" if args.v_rotation else ")"),
                      "mfma_frac": achieved_tflops / PEAK_F16_TFLOPS, "hbm_frac": achieved_gbs / PEAK_HBM_GBS,
                      "measured_peak": peaks,

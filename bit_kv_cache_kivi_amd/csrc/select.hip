@@ -60,7 +60,7 @@ __device__ __forceinline__ float sum32(float x) {
 }
 
 template <int KB, int VB, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
   constexpr int KS = D / 16;
   constexpr int NPAIR = kSlot * (D / 8);                 // (token, 8-channel group) pairs of a unit
   static_assert(NPAIR <= kThreads, "one pair per thread");
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
   __shared__ float hsum[kWaves][kSlot];                  // per wave (head): P summed over the mask queries
   __shared__ __align__(16) float mq[kWaves][kSlot];      // MODE 1: per head and query, the maximum
   __shared__ __align__(16) float lq[kWaves][kSlot];      // and the weight 1/sum (0 outside the mask)
+  __shared__ __align__(32) v8i_t q8s[kWaves][D / 64][64];  // per wave: Q's e4m3 copy, lane-major
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int np = a.nslots[0][b], ns = a.use_suffix ? a.nslots[1][b] : 0;
@@ -106,7 +107,10 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
   // copy for the lo product (block k holds channels 64k + 32*hh + [0, 32))
   constexpr int KB8 = D / 64;
   half8 qop[KS];
-  v8i_t q8[KB8];
+  // the e4m3 copy stays in LDS (read once per unit, just before its MFMA):
+  // in registers it would cost the occupancy that lets two workgroups share
+  // a CU
+  v8i_t (&q8)[KB8][64] = q8s[wave];
   {
     const size_t row = (((size_t)b * kSlot + j) * hq_all + kvh * r + ci) * D;
     const size_t base = row + (D / 2) * hh;
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
         for (int e = 0; e < 4; ++e) x[e] = load1(a.q, e0 + e, a.q_f32);
         uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
-        q8[k][w4] = (int)d;
+        q8[k][lane][w4] = (int)d;
       }
     }
   }
@@ -293,22 +297,23 @@ __global__ __launch_bounds__(kThreads) void sel_kernel(const SelArgs a) {
       for (int k = 0; k < KB8; ++k) {
         const uint4 l0 = klt[k][0][lane], l1 = klt[k][1][lane];
         const v8i_t kl = v8i_t{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
-        sacc = MODE == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl, q8[k], sacc, 1, 0, 0, 127 - 12, 0, 127)
-                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q8[k], kl, sacc, 0, 1, 0, 127, 0, 127 - 12);
+        const v8i_t qk = q8[k][lane];
+        sacc = MODE == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl, qk, sacc, 1, 0, 0, 127 - 12, 0, 127)
+                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qk, kl, sacc, 0, 1, 0, 127, 0, 127 - 12);
       }
       if (MODE == 0) {
-        float sv[16], mx = -__builtin_inff();
+        float mx = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16; ++i) {   // scaled scores in place
           const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
-          sv[i] = tok < h.x ? sacc[i] * c2 : -__builtin_inff();
-          mx = fmaxf(mx, sv[i]);
+          sacc[i] = tok < h.x ? sacc[i] * c2 : -__builtin_inff();
+          mx = fmaxf(mx, sacc[i]);
         }
         const float mn = fmaxf(m_run, mx);
         if (mn > -__builtin_inff()) {
           float l = l_run * __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(sv[i] - mn);
+          for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(sacc[i] - mn);
           l_run = l;
           m_run = mn;
         }
