@@ -905,12 +905,13 @@ kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t
     max_nc = std::max(max_nc, np + ns);
     total_nc += np + ns;
   }
-  // split lengths: about four workgroups per compute unit over all
-  // (sequence, kv head) pairs, at least 4 units, and the stats pass within
-  // the partial capacity of max_splits per pair
+  // split lengths: one workgroup per compute unit over all (sequence, kv
+  // head) pairs (each workgroup pipelines its units; one fits a CU at D =
+  // 128), at least 4 units, and the stats pass within the partial capacity of
+  // max_splits per pair
   const int64_t cus = c->num_cus;
   auto split_len = [&](int64_t total, int maxu) {
-    int su = (int)std::max<int64_t>(4, (total * H + 4 * cus - 1) / (4 * cus));
+    int su = (int)std::max<int64_t>(4, (total * H + cus - 1) / cus);
     return std::min(std::max(su, (maxu + max_splits - 1) / max_splits), kvq::kMaxSelSplit);
   };
   const int su_stats = split_len(total_nc + B, max_nc + 1);

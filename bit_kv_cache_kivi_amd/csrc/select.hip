@@ -60,7 +60,7 @@ __device__ __forceinline__ float sum32(float x) {
 }
 
 template <int KB, int VB, int D, int MODE>
-__global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
   constexpr int KS = D / 16;
   constexpr int NPAIR = kSlot * (D / 8);                 // (token, 8-channel group) pairs of a unit
   static_assert(NPAIR <= kThreads, "one pair per thread");
@@ -70,18 +70,19 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
   static_assert(VLANES == 16 && VCH % 4 == 0, "value-norm mapping");
   constexpr uint32_t KC = kc_bytes(D, KB), VC = vc_bytes(D, VB), KM = kmeta_bytes(D);
   static_assert(record_bytes(D, KB, VB, 32) <= 48 * D, "record fits the stage");
-  __shared__ __align__(16) uint8_t rec[48 * D];
-  __shared__ __align__(16) half8 kt[KS][64];
+  // double-buffered by unit parity: unit u's record and protected chunks are
+  // staged in [u & 1], its key operand tiles in [u & 1]
+  __shared__ __align__(16) uint8_t rec[2][48 * D];
+  __shared__ __align__(16) half8 kt[2][KS][64];
   // key lo tiles (e5m2): byte j of lane l of 64-channel block k holds channel
   // 64k + 32(l/32) + j of token l%32 (the attention kernel's layout)
-  __shared__ __align__(16) uint4 klt[D / 64][2][64];
-  __shared__ __align__(16) uint4 prt[kThreads];          // each thread's protected key chunk
-  __shared__ float vn[kSlot];
+  __shared__ __align__(16) uint4 klt[2][D / 64][2][64];
+  __shared__ __align__(16) uint4 prt[2][kThreads];       // each thread's protected key chunk
+  __shared__ float vn[3][kSlot];                         // MODE 1: value norms, by unit % 3
   __shared__ __align__(16) int4 hdrs[kMaxSelSplit];    // the split's unit headers
-  __shared__ float hsum[kWaves][kSlot];                  // per wave (head): P summed over the mask queries
+  __shared__ float hsum[2][kWaves][kSlot];               // MODE 1: per head, P summed over the mask queries
   __shared__ __align__(16) float mq[kWaves][kSlot];      // MODE 1: per head and query, the maximum
   __shared__ __align__(16) float lq[kWaves][kSlot];      // and the weight 1/sum (0 outside the mask)
-  __shared__ __align__(32) v8i_t q8s[kWaves][D / 64][64];  // per wave: Q's e4m3 copy, lane-major
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int np = a.nslots[0][b], ns = a.use_suffix ? a.nslots[1][b] : 0;
@@ -107,10 +108,7 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
   // copy for the lo product (block k holds channels 64k + 32*hh + [0, 32))
   constexpr int KB8 = D / 64;
   half8 qop[KS];
-  // the e4m3 copy stays in LDS (read once per unit, just before its MFMA):
-  // in registers it would cost the occupancy that lets two workgroups share
-  // a CU
-  v8i_t (&q8)[KB8][64] = q8s[wave];
+  v8i_t q8[KB8];
   {
     const size_t row = (((size_t)b * kSlot + j) * hq_all + kvh * r + ci) * D;
     const size_t base = row + (D / 2) * hh;
@@ -130,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
         for (int e = 0; e < 4; ++e) x[e] = load1(a.q, e0 + e, a.q_f32);
         uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
-        q8[k][lane][w4] = (int)d;
+        q8[k][w4] = (int)d;
       }
     }
   }
@@ -173,9 +171,9 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
   // ---- unit loads: the record (16-byte chunks) and this thread's protected
   // key chunk.  Buffer loads: a unit past the split (or the block) gets empty
   // resources, so its loads return zeros without memory traffic and every
-  // path writes the same registers.
-  // two units in flight: a unit's loads are issued two units before it is
-  // processed (register sets indexed by the unrolled position)
+  // path writes the same registers.  Two register sets, indexed by the
+  // unrolled position: a unit's loads are issued two iterations before its
+  // record is staged.
   constexpr int NPF = 2;
   struct Pre { uint4 rc[RPT]; uint4 pc; int4 hd; };
   Pre pre[NPF];
@@ -199,6 +197,112 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
     const int off = (kpair && ((hd.y >> kt0) & 1)) ? (rank * D + 8 * kcg) * 2 : 0x7ff00000;
     p.pc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr_, off, 0, 0));
   };
+  // the block's keys (the stats pass's last split), read before the loop: a
+  // global load inside it would make every unit wait for the prefetch loads
+  // issued before it
+  float xblk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) xblk[e] = 0.f;
+  if (MODE == 0 && u1 > NC && kpair)
+    load8(a.k_blk, (((size_t)b * kSlot + kt0) * hkv + kvh) * D + 8 * kcg, a.blk_f32, xblk);
+  // a staged unit's header: the block has 32 valid tokens and no protected rows
+  auto header = [&](int u) __attribute__((always_inline)) {
+    return (MODE == 0 && u == NC) ? make_int4(kSlot, 0, 0, 0) : hdrs[u - u0];
+  };
+  // stage unit u's record and protected chunk (a cached unit; the block reads
+  // its keys straight from the block tensor)
+  // Wait for this unit's loads only: the next unit's RPT + 1 loads (and, for
+  // the wave writing contributions, its two stores of the last iteration,
+  // issued after them) stay in flight.  Stated once, before the conditional
+  // stores, so that the compiler adds no wait of its own there.
+  constexpr int kLoadsPerUnit = RPT + 1;
+  static_assert(kLoadsPerUnit + 2 < 16, "vmcnt field");
+  auto stage = [&](int u, const Pre& p) __attribute__((always_inline)) {
+    if (MODE == 1 && wave == kWaves - 1)
+      __builtin_amdgcn_s_waitcnt(0xF70 | (kLoadsPerUnit + 2));
+    else
+      __builtin_amdgcn_s_waitcnt(0xF70 | kLoadsPerUnit);
+    if (MODE == 0 && u == NC) return;
+    uint8_t* rs = rec[u & 1];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      const uint32_t off = (uint32_t)(q * kThreads + tid) * 16u;
+      if (off < rbytes) *reinterpret_cast<uint4*>(rs + off) = p.rc[q];
+    }
+    prt[u & 1][tid] = p.pc;
+  };
+  // keys of unit u -> fp16 hi / e5m2 lo operand tiles: token kt0 of channel
+  // group kcg
+  auto dequant = [&](int u) __attribute__((always_inline)) {
+    if (!kpair) return;
+    const int4 h = header(u);
+    const uint8_t* rs = rec[u & 1];
+    const float* km = reinterpret_cast<const float*>(rs + KC + VC) + 8 * kcg;
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(rs);
+    const int t = kt0;
+    float x[8];
+    if (MODE == 0 && u == NC) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = xblk[e];
+    } else if ((h.y >> t) & 1) {
+      const uint4 w = prt[u & 1][tid];
+      x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+      x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    } else {
+      float code[8];
+      const uint32_t w = KB == 4 ? words[kcg * 32 + t] : words[(kcg >> 1) * 32 + t] >> (16 * (kcg & 1));
+      unpack8<KB>(w, code);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], km[e], km[D + e]);
+    }
+    const int cg = kcg;
+    store_hi_lo8(kt[u & 1][kks][t + 32 * khh],
+                 reinterpret_cast<uint2*>(&klt[u & 1][cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1], x,
+                 neg_one);
+  };
+  // MODE 1: value norms of unit u: token t, channels [cs * VCH, +VCH) of one
+  // value group
+  auto norms = [&](int u) __attribute__((always_inline)) {
+    const uint8_t* rs = rec[u & 1];
+    const int t = tid / VLANES, cs = tid % VLANES, c0 = cs * VCH;
+    const int mm = t / 16, th = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2);
+    const int wj = VB == 4 ? 2 * mm + th : th;
+    const int bit = VB == 4 ? 4 * e : 2 * (8 * mm + e);
+    const float* vm = reinterpret_cast<const float*>(rs + KC + VC + KM + (c0 >> a.gv_log2) * 256);
+    const float sc = vm[t], zr = vm[kSlot + t];
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(rs + KC) + wj * D + c0;
+    float acc = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < VCH; cc += 4) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(vw + cc);
+      const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = fmaf((float)((w[k] >> bit) & ((1u << VB) - 1u)), sc, zr);
+        acc = fmaf(x, x, acc);
+      }
+    }
+    acc = add_dpp<0xB1>(acc);
+    acc = add_dpp<0x4E>(acc);
+    acc = add_dpp<0x141>(acc);
+    acc = add_dpp<0x140>(acc);
+    if (cs == 0) vn[u % 3][t] = sqrtf(acc);
+  };
+  // MODE 1, wave 0: entry contributions of unit u (lanes 0..31) and the
+  // unit's sum over its valid entries (a butterfly over those lanes)
+  auto contribute = [&](int u) __attribute__((always_inline)) {
+    const int4 h = header(u);
+    float cv = 0.f;
+    if (lane < kSlot) {
+      float acc = 0.f;
+      for (int w = 0; w < r; ++w) acc += hsum[u & 1][w][lane];
+      const bool ok = lane < h.x;
+      cv = ok ? vn[u % 3][lane] * acc : 0.f;
+      a.contrib[(((size_t)b * hkv + kvh) * a.ucap + u) * kSlot + lane] = ok ? cv : -1.0f;
+    }
+    const float us = sum32(cv);
+    if (lane == 0) a.unit_contrib[((size_t)b * hkv + kvh) * a.ucap + u] = us;
+  };
 
   // the split's headers, read once: a unit's protected-row loads depend on its
   // header, and a global read of it per unit would stall the prefetch
@@ -210,97 +314,66 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
     hdrs[i] = *reinterpret_cast<const int4*>((s1 ? seg1.headers : seg0.headers) + ((size_t)b * cap + sl) * kHeaderBytes);
   }
   lds_barrier();
-#pragma unroll
-  for (int k = 0; k < NPF; ++k) load(u0 + k, pre[k]);
-  for (int ub = u0; ub < u1; ub += NPF)
-#pragma unroll
-  for (int k = 0; k < NPF; ++k) {
-    const int u = ub + k;
-    if (u >= u1) break;
-    const bool blk = MODE == 0 && u == NC;
-    const int4 h = blk ? make_int4(kSlot, 0, 0, 0) : pre[k].hd;
-    if (!blk) {
-#pragma unroll
-      for (int q = 0; q < RPT; ++q) {
-        const uint32_t off = (uint32_t)(q * kThreads + tid) * 16u;
-        if (off < rbytes) *reinterpret_cast<uint4*>(rec + off) = pre[k].rc[q];
+  // Pipeline.  Before iteration u: unit u's operand tiles are in kt[u & 1]
+  // (and, MODE 1, its value norms in vn[u % 3]); unit u + 1's record is
+  // staged in rec[(u + 1) & 1]; the loads of unit u + 2 are in flight in
+  // pre[(u - u0) % 2] and those of unit u + 3 in the other set.  Iteration u
+  // issues the score MFMAs of unit u, dequantizes unit u + 1 (and its value
+  // norms) while they run, stages unit u + 2 and issues the loads of unit
+  // u + 4, then turns unit u's scores into statistics or per-token sums; one
+  // barrier ends it.
+  load(u0, pre[0]);
+  load(u0 + 1, pre[1]);
+  stage(u0, pre[0]);
+  load(u0 + 2, pre[0]);
+  stage(u0 + 1, pre[1]);
+  load(u0 + 3, pre[1]);
+  lds_barrier();
+  dequant(u0);
+  if (MODE == 1) norms(u0);
+  lds_barrier();
+  // one iteration; pk holds the loads of unit u + 2 (the two register sets
+  // alternate, named statically so that both stay in registers)
+  auto iteration = [&](int u, Pre& pk) __attribute__((always_inline)) {
+    const int4 h = header(u);
+    // Waves 4..7 dequantize and stage first and then issue their MFMAs;
+    // waves 0..3 (one per SIMD, as are 4..7) the other way round.  So on each
+    // SIMD one wave's MFMA chain runs while the other issues vector work,
+    // instead of both waves reaching their MFMAs together after the barrier.
+    const bool late = wave >= 4;
+    auto produce = [&]() __attribute__((always_inline)) {
+      if (u + 1 < u1) {
+        dequant(u + 1);
+        if (MODE == 1) norms(u + 1);
       }
-      prt[tid] = pre[k].pc;
-    }
-    lds_barrier();
-    load(u + NPF, pre[k]);
-    // keys -> fp16 operand tiles: token kt0 of channel group kcg
-    if (kpair) {
-      const float* km = reinterpret_cast<const float*>(rec + KC + VC) + 8 * kcg;
-      const uint32_t* words = reinterpret_cast<const uint32_t*>(rec);
-      const int t = kt0;
-      float x[8];
-      if (blk) {
-        load8(a.k_blk, (((size_t)b * kSlot + t) * hkv + kvh) * D + 8 * kcg, a.blk_f32, x);
-      } else if ((h.y >> t) & 1) {
-        const uint4 w = prt[tid];
-        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-      } else {
-        float code[8];
-        const uint32_t w = KB == 4 ? words[kcg * 32 + t] : words[(kcg >> 1) * 32 + t] >> (16 * (kcg & 1));
-        unpack8<KB>(w, code);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], km[e], km[D + e]);
-      }
-      const int cg = kcg;
-      store_hi_lo8(kt[kks][t + 32 * khh],
-                   reinterpret_cast<uint2*>(&klt[cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1], x,
-                   neg_one);
-    }
-    if (MODE == 1) {
-      // value norms: token t, channels [cs * VCH, +VCH) of one value group
-      const int t = tid / VLANES, cs = tid % VLANES, c0 = cs * VCH;
-      const int mm = t / 16, th = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2);
-      const int wj = VB == 4 ? 2 * mm + th : th;
-      const int bit = VB == 4 ? 4 * e : 2 * (8 * mm + e);
-      const float* vm = reinterpret_cast<const float*>(rec + KC + VC + KM + (c0 >> a.gv_log2) * 256);
-      const float sc = vm[t], zr = vm[kSlot + t];
-      const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + KC) + wj * D + c0;
-      float acc = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < VCH; cc += 4) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(vw + cc);
-        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x = fmaf((float)((w[k] >> bit) & ((1u << VB) - 1u)), sc, zr);
-          acc = fmaf(x, x, acc);
-        }
-      }
-      acc = add_dpp<0xB1>(acc);
-      acc = add_dpp<0x4E>(acc);
-      acc = add_dpp<0x141>(acc);
-      acc = add_dpp<0x140>(acc);
-      if (cs == 0) vn[t] = sqrtf(acc);
-    }
-    lds_barrier();
-    // scores of the wave's head
+      if (u + 2 < u1) stage(u + 2, pk);
+      load(u + 4, pk);
+    };
+    if (late) produce();
+    floatx16 sacc;
     if (head) {
-      floatx16 sacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
       // MODE 0: S^T = K Q^T, sacc[i] = S[query j][token 8*(i/4) + 4*hh + i%4];
       // MODE 1: S = Q K^T (the same operand registers, swapped),
       // sacc[i] = S[query 8*(i/4) + 4*hh + i%4][token j]
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sacc = MODE == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(kt[s][lane], qop[s], sacc, 0, 0, 0)
-                         : __builtin_amdgcn_mfma_f32_32x32x16_f16(qop[s], kt[s][lane], sacc, 0, 0, 0);
+      for (int s2 = 0; s2 < KS; ++s2)
+        sacc = MODE == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(kt[u & 1][s2][lane], qop[s2], sacc, 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_f16(qop[s2], kt[u & 1][s2][lane], sacc, 0, 0, 0);
       // + 2^-12 K_lo' Q8^T (bf8 x e4m3; the E8M0 scale 2^-12 on the lo side)
 #pragma unroll
-      for (int k = 0; k < KB8; ++k) {
-        const uint4 l0 = klt[k][0][lane], l1 = klt[k][1][lane];
+      for (int kk = 0; kk < KB8; ++kk) {
+        const uint4 l0 = klt[u & 1][kk][0][lane], l1 = klt[u & 1][kk][1][lane];
         const v8i_t kl = v8i_t{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
-        const v8i_t qk = q8[k][lane];
-        sacc = MODE == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl, qk, sacc, 1, 0, 0, 127 - 12, 0, 127)
-                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qk, kl, sacc, 0, 1, 0, 127, 0, 127 - 12);
+        sacc = MODE == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl, q8[kk], sacc, 1, 0, 0, 127 - 12, 0, 127)
+                         : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q8[kk], kl, sacc, 0, 1, 0, 127, 0, 127 - 12);
       }
+    }
+    // (waves 0..3) while the MFMAs run: the next unit's operands, the record
+    // after it, and the loads two units further
+    if (!late) produce();
+    if (head) {
       if (MODE == 0) {
         float mx = -__builtin_inff();
 #pragma unroll
@@ -332,25 +405,25 @@ __global__ __launch_bounds__(kThreads, 4) void sel_kernel(const SelArgs a) {
           acc = fmaf(__builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 3], c2, -m4.w)), l4.w, acc);
         }
         const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-        if (hh == 0) hsum[wave][j] = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+        if (hh == 0) hsum[u & 1][wave][j] = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
       }
     }
+    // the previous unit's contributions (its per-head sums were complete at
+    // the last barrier)
+    if (MODE == 1 && wave == kWaves - 1 && u > u0) contribute(u - 1);
     lds_barrier();
-    if (MODE == 1 && wave == 0) {
-      // entry contributions (lanes 0..31), and the unit's sum over its valid
-      // entries (a butterfly over those lanes)
-      float cv = 0.f;
-      if (lane < kSlot) {
-        float acc = 0.f;
-        for (int w = 0; w < r; ++w) acc += hsum[w][lane];
-        const bool ok = lane < h.x;
-        cv = ok ? vn[lane] * acc : 0.f;
-        a.contrib[(((size_t)b * hkv + kvh) * a.ucap + u) * kSlot + lane] = ok ? cv : -1.0f;
-      }
-      const float us = sum32(cv);
-      if (lane == 0) a.unit_contrib[((size_t)b * hkv + kvh) * a.ucap + u] = us;
-    }
+  };
+  static_assert(NPF == 2, "two register sets");
+  // whole pairs, so that the loop is only re-entered after the second set's
+  // loads (the compiler then keeps the first set's wait at two loads), and an
+  // odd last unit
+  int ub = u0;
+  for (; ub + 1 < u1; ub += 2) {
+    iteration(ub, pre[0]);
+    iteration(ub + 1, pre[1]);
   }
+  if (ub < u1) iteration(ub, pre[0]);
+  if (MODE == 1 && wave == kWaves - 1) contribute(u1 - 1);
   if (MODE == 0) {
     // merge the two halves (the same query's two token sets) and write the partials
     const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_run), __float_as_uint(m_run), false, false);
