@@ -48,7 +48,7 @@ _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
         "attn_source_sha256": "18928d504c737e05f71043846e9894fb971b44f1f5ef9dc6d074939f428c353e",
-        "kib": {"attn_kernel": {"fetch": 27226, "write": 15010},
+        "kib": {"attn_kernel": {"fetch": 27226, "write": 15008},
                 "combine_h16_kernel": {"fetch": 7535.5, "write": 1792}},
     },
 }
