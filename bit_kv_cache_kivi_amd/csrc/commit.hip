@@ -6,12 +6,12 @@
 // one slot of one kv head is in commit_slot.h; this kernel runs it over every
 // new slot of a commit.
 //
-// One workgroup = four waves per kv head, looping over new slots (task i,
-// i + gridDim.x, ...).  Each lane loads the next slot's 16-byte row pieces
-// before quantizing the current one, so HBM reads stay in flight while a slot
-// is processed; the record buffers alternate, so a slot's stores into one
-// buffer never race the previous slot's copy-out of the other.  This file is
-// compiled with -ffp-contract=off.
+// A persistent grid of four-wave workgroups; each takes a contiguous range of
+// (slot, kv head) items and loops over it.  Each lane loads the next item's
+// 16-byte row pieces before quantizing the current one, so HBM reads stay in
+// flight while a slot is processed; the record buffers alternate, so an item's
+// stores into one buffer never race the previous item's copy-out of the
+// other.  This file is compiled with -ffp-contract=off.
 #include <algorithm>
 
 #include "commit_slot.h"
