@@ -40,8 +40,10 @@
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 8;                 // one query head per wave
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 8;                 // consumer waves: one query head per wave
+constexpr int kProd = 4;                  // producer waves (one per SIMD)
+constexpr int kPThreads = 64 * kProd;
+constexpr int kThreads = 64 * (kProd + kWaves);
 constexpr int kMaxHeads = 8;   // query heads per kv head
 
 template <int CTRL>
@@ -60,14 +62,15 @@ __device__ __forceinline__ float sum32(float x) {
 }
 
 template <int KB, int VB, int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void sel_kernel(const SelArgs a) {
   constexpr int KS = D / 16;
   constexpr int NPAIR = kSlot * (D / 8);                 // (token, 8-channel group) pairs of a unit
-  static_assert(NPAIR <= kThreads, "one pair per thread");
-  constexpr int RPT = (48 * D / 16 + kThreads - 1) / kThreads;
-  constexpr int VLANES = kThreads / kSlot;               // threads per token for the value norms
+  constexpr int PPT = NPAIR / kPThreads;                 // pairs per producer thread
+  static_assert(PPT >= 1 && PPT * kPThreads == NPAIR, "pairs per producer thread");
+  constexpr int RPT = (48 * D / 16 + kPThreads - 1) / kPThreads;   // 16-byte record chunks per producer thread
+  constexpr int VLANES = kPThreads / kSlot;              // producer threads per token for the value norms
   constexpr int VCH = D / VLANES;                        // channels per thread
-  static_assert(VLANES == 16 && VCH % 4 == 0, "value-norm mapping");
+  static_assert(VLANES == 8 && VCH % 4 == 0, "value-norm mapping");
   constexpr uint32_t KC = kc_bytes(D, KB), VC = vc_bytes(D, VB), KM = kmeta_bytes(D);
   static_assert(record_bytes(D, KB, VB, 32) <= 48 * D, "record fits the stage");
   // double-buffered by unit parity: unit u's record and protected chunks are
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
   // key lo tiles (e5m2): byte j of lane l of 64-channel block k holds channel
   // 64k + 32(l/32) + j of token l%32 (the attention kernel's layout)
   __shared__ __align__(16) uint4 klt[2][D / 64][2][64];
-  __shared__ __align__(16) uint4 prt[2][kThreads];       // each thread's protected key chunk
+  __shared__ __align__(16) uint4 prt[2][PPT][kPThreads];  // each producer thread's protected key chunks
   __shared__ float vn[3][kSlot];                         // MODE 1: value norms, by unit % 3
   __shared__ __align__(16) int4 hdrs[kMaxSelSplit];    // the split's unit headers
   __shared__ float hsum[2][kWaves][kSlot];               // MODE 1: per head, P summed over the mask queries
@@ -91,18 +94,232 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
   const int nsplit = (U + a.split_units - 1) / a.split_units;
   if (split >= nsplit) return;
   const int u0 = split * a.split_units, u1 = min(U, u0 + a.split_units);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hkv = a.hkv, r = a.r, hq_all = a.hq;
-  const uint32_t rbytes = a.record_bytes;
-  const float c2 = a.scale_log2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < kProd;
+  const int hkv = a.hkv, r = a.r;
   const int j = lane & 31, hh = lane >> 5;
-  const bool kpair = tid < NPAIR;                  // this thread dequantizes (token kt0, group kcg)
-  const int kt0 = tid % kSlot, kcg = tid / kSlot;
-  const int khh = kcg / (D / 16), kks = kcg % (D / 16);
   const SegPtrs seg0 = a.seg[0], seg1 = a.seg[1];
-  const bool head = wave < r;                      // wave w runs query head w of the group
-  const int ci = min(wave, r - 1);
 
+  // the split's headers, read once: a unit's protected-row loads depend on its
+  // header, and a global read of it per unit would stall the prefetch
+  for (int i = tid; i < min(u1, NC) - u0; i += kThreads) {
+    const int u = u0 + i;
+    const bool s1 = u >= np;
+    const int sl = s1 ? u - np : u;
+    const int cap = s1 ? seg1.slot_cap : seg0.slot_cap;
+    hdrs[i] = *reinterpret_cast<const int4*>((s1 ? seg1.headers : seg0.headers) + ((size_t)b * cap + sl) * kHeaderBytes);
+  }
+
+  const int writer_wave = r < kWaves ? kProd + r : kProd - 1;
+  const bool writer = MODE == 1 && wave == writer_wave;
+  // MODE 1, the writer wave: entry contributions of unit u (lanes 0..31)
+  // and the unit's sum over its valid entries (a butterfly over those lanes).
+  // The writer is the consumer wave left without a query head when r < 8
+  // (it has no MFMA work), else the last producer wave.  The heads' sums are
+  // read all at once (independent LDS reads) and the unused ones dropped.
+  auto contribute = [&](int u) __attribute__((always_inline)) {
+    const int4 h = hdrs[u - u0];
+    float cv = 0.f;
+    if (lane < kSlot) {
+      float hs[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) hs[w] = hsum[u & 1][w][lane];
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) acc += w < r ? hs[w] : 0.f;
+      const bool ok = lane < h.x;
+      cv = ok ? vn[u % 3][lane] * acc : 0.f;
+      a.contrib[(((size_t)b * hkv + kvh) * a.ucap + u) * kSlot + lane] = ok ? cv : -1.0f;
+    }
+    const float us = sum32(cv);
+    if (lane == 0) a.unit_contrib[((size_t)b * hkv + kvh) * a.ucap + u] = us;
+  };
+
+  // Pipeline, one barrier per unit.  In interval u the consumer waves (one per
+  // query head) score unit u from the operand tiles kt[u & 1] while the
+  // producer waves dequantize unit u + 1 into the other tiles (and, MODE 1,
+  // compute its value norms), stage unit u + 2's record from the registers its
+  // loads arrived in, issue the loads of unit u + 4, and write unit u - 1's
+  // contributions.  Prologue: the headers, then units u0 and u0 + 1 staged,
+  // then unit u0 dequantized (three barriers on both sides).
+  if (producer) {
+    const int ptid = tid;                          // 0 .. kPThreads - 1
+    const uint32_t rbytes = a.record_bytes;
+    const float neg_one = opaque_neg_one();
+    // the block's keys (the stats pass's last split), read before the loop:
+    // a global load inside it would make every unit wait for the prefetch
+    // loads issued before it
+    float xblk[PPT][8];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xblk[q][e] = 0.f;
+    if (MODE == 0 && u1 > NC) {
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) {
+        const int p = ptid + kPThreads * q, t = p % kSlot, cg = p / kSlot;
+        load8(a.k_blk, (((size_t)b * kSlot + t) * hkv + kvh) * D + 8 * cg, a.blk_f32, xblk[q]);
+      }
+    }
+    struct Pre { uint4 rc[RPT]; uint4 pc[PPT]; };
+    Pre pre[2];
+    // buffer loads: a unit past the split (or the block) gets empty
+    // resources, so its loads return zeros without memory traffic
+    auto load = [&](int u, Pre& pr) __attribute__((always_inline)) {
+      const bool valid = u < min(u1, NC);
+      const bool s1 = u >= np;
+      const int sl = valid ? (s1 ? u - np : u) : 0;
+      const int cap = s1 ? seg1.slot_cap : seg0.slot_cap;
+      const int pcap = s1 ? seg1.prot_cap : seg0.prot_cap;
+      const uint8_t* recp = (s1 ? seg1.records : seg0.records) + (((size_t)b * hkv + kvh) * cap + sl) * rbytes;
+      const uint16_t* prot = (s1 ? seg1.prot_rows : seg0.prot_rows) + ((size_t)b * hkv + kvh) * pcap * D;
+      const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)recp, 0, valid ? (int)rbytes : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t pr_ = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)prot, 0, valid ? (int)min((size_t)pcap * D * 2, (size_t)0x7fffffff) : 0, 0x00020000);
+      const int4 hd = valid ? hdrs[u - u0] : make_int4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < RPT; ++q)
+        pr.rc[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, (q * kPThreads + ptid) * 16, 0, 0));
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) {
+        const int p = ptid + kPThreads * q, t = p % kSlot, cg = p / kSlot;
+        const int rank = hd.z + __popc((uint32_t)hd.y & ((1u << t) - 1u));
+        const int off = ((hd.y >> t) & 1) ? (rank * D + 8 * cg) * 2 : 0x7ff00000;
+        pr.pc[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr_, off, 0, 0));
+      }
+    };
+    // Wait for this unit's loads only: the next unit's RPT + PPT loads (and,
+    // for the wave writing contributions, its two stores of the last
+    // interval, issued after them) stay in flight.  Stated once, before the
+    // conditional stores, so that the compiler adds no wait of its own there.
+    constexpr int kLoadsPerUnit = RPT + PPT;
+    static_assert(kLoadsPerUnit + 2 < 16, "vmcnt field");
+    auto stage = [&](int u, const Pre& pr) __attribute__((always_inline)) {
+      if (writer) __builtin_amdgcn_s_waitcnt(0xF70 | (kLoadsPerUnit + 2));
+      else        __builtin_amdgcn_s_waitcnt(0xF70 | kLoadsPerUnit);
+      if (MODE == 0 && u == NC) return;
+      uint8_t* rs = rec[u & 1];
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const uint32_t off = (uint32_t)(q * kPThreads + ptid) * 16u;
+        if (off < rbytes) *reinterpret_cast<uint4*>(rs + off) = pr.rc[q];
+      }
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) prt[u & 1][q][ptid] = pr.pc[q];
+    };
+    // keys of unit u -> fp16 hi / e5m2 lo operand tiles, one (token, channel
+    // group) pair at a time
+    // Branch-free: every LDS read of both pairs (code word, scales, zeros,
+    // protected chunk) is issued before any arithmetic, so the pairs share one
+    // LDS latency; a protected token then takes its bf16 row instead of the
+    // dequantized codes.
+    auto dequant = [&](int u) __attribute__((always_inline)) {
+      const bool blk = MODE == 0 && u == NC;       // uniform
+      const uint32_t pmask = blk ? 0u : (uint32_t)hdrs[u - u0].y;
+      const uint8_t* rs = rec[u & 1];
+      const uint32_t* words = reinterpret_cast<const uint32_t*>(rs);
+      uint32_t cw[PPT];
+      uint4 pw[PPT];
+      float4 sc0[PPT], sc1[PPT], zr0[PPT], zr1[PPT];
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) {
+        const int p = ptid + kPThreads * q, t = p % kSlot, cg = p / kSlot;
+        const float* km = reinterpret_cast<const float*>(rs + KC + VC) + 8 * cg;
+        cw[q] = KB == 4 ? words[cg * 32 + t] : words[(cg >> 1) * 32 + t] >> (16 * (cg & 1));
+        pw[q] = prt[u & 1][q][ptid];
+        sc0[q] = *reinterpret_cast<const float4*>(km);
+        sc1[q] = *reinterpret_cast<const float4*>(km + 4);
+        zr0[q] = *reinterpret_cast<const float4*>(km + D);
+        zr1[q] = *reinterpret_cast<const float4*>(km + D + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) {
+        const int p = ptid + kPThreads * q, t = p % kSlot, cg = p / kSlot;
+        const int khh = cg / (D / 16), kks = cg % (D / 16);
+        float code[8], x[8];
+        unpack8<KB>(cw[q], code);
+        const float sc[8] = {sc0[q].x, sc0[q].y, sc0[q].z, sc0[q].w, sc1[q].x, sc1[q].y, sc1[q].z, sc1[q].w};
+        const float zr[8] = {zr0[q].x, zr0[q].y, zr0[q].z, zr0[q].w, zr1[q].x, zr1[q].y, zr1[q].z, zr1[q].w};
+        const uint4 w = pw[q];
+        const float pr[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+        const bool prot = (pmask >> t) & 1u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = blk ? xblk[q][e] : prot ? pr[e] : fmaf(code[e], sc[e], zr[e]);
+        store_hi_lo8(kt[u & 1][kks][t + 32 * khh],
+                     reinterpret_cast<uint2*>(&klt[u & 1][cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1], x,
+                     neg_one);
+      }
+    };
+    // MODE 1: value norms of unit u: token t, channels [cs * VCH, +VCH) of
+    // one value group, summed over the token's VLANES adjacent lanes
+    auto norms = [&](int u) __attribute__((always_inline)) {
+      const uint8_t* rs = rec[u & 1];
+      const int t = ptid / VLANES, cs = ptid % VLANES, c0 = cs * VCH;
+      const int mm = t / 16, th = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2);
+      const int wj = VB == 4 ? 2 * mm + th : th;
+      const int bit = VB == 4 ? 4 * e : 2 * (8 * mm + e);
+      const float* vm = reinterpret_cast<const float*>(rs + KC + VC + KM + (c0 >> a.gv_log2) * 256);
+      const float sc = vm[t], zr = vm[kSlot + t];
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(rs + KC) + wj * D + c0;
+      float acc = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < VCH; cc += 4) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(vw + cc);
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = fmaf((float)((w[k] >> bit) & ((1u << VB) - 1u)), sc, zr);
+          acc = fmaf(x, x, acc);
+        }
+      }
+      acc = add_dpp<0xB1>(acc);    // quad_perm [1,0,3,2]
+      acc = add_dpp<0x4E>(acc);    // quad_perm [2,3,0,1]
+      acc = add_dpp<0x141>(acc);   // row_half_mirror: the 8 lanes of the token
+      if (cs == 0) vn[u % 3][t] = sqrtf(acc);
+    };
+    lds_barrier();                                   // headers
+    load(u0, pre[0]);
+    load(u0 + 1, pre[1]);
+    stage(u0, pre[0]);
+    load(u0 + 2, pre[0]);
+    stage(u0 + 1, pre[1]);
+    load(u0 + 3, pre[1]);
+    lds_barrier();                                   // units u0, u0 + 1 staged
+    dequant(u0);
+    if (MODE == 1) norms(u0);
+    lds_barrier();                                   // unit u0's operands
+    // pk holds the loads of unit u + 2 (the two register sets alternate, named
+    // statically so that both stay in registers)
+    auto interval = [&](int u, Pre& pk) __attribute__((always_inline)) {
+      if (u + 1 < u1) {
+        dequant(u + 1);
+        if (MODE == 1) norms(u + 1);
+      }
+      if (u + 2 < u1) stage(u + 2, pk);
+      load(u + 4, pk);
+      if (writer && u > u0) contribute(u - 1);
+      lds_barrier();
+    };
+    // whole pairs, so that the loop is re-entered only after the second set's
+    // loads (the compiler then keeps the first set's wait at one unit's
+    // loads), and an odd last unit
+    int ub = u0;
+    for (; ub + 1 < u1; ub += 2) {
+      interval(ub, pre[0]);
+      interval(ub + 1, pre[1]);
+    }
+    if (ub < u1) interval(ub, pre[0]);
+    if (writer) contribute(u1 - 1);
+    return;
+  }
+
+  // ---- consumer waves: query head kvh * r + ci
+  const int ci = wave - kProd;
+  const bool head = ci < r;
+  const int cq = min(ci, r - 1);
+  const float c2 = a.scale_log2;
   // Q operand of the wave's head (B operand of S^T: lane = query token j,
   // half hh holds channels (D/2)*hh + 8s + [0, 8) at k-step s), and its e4m3
   // copy for the lo product (block k holds channels 64k + 32*hh + [0, 32))
@@ -110,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
   half8 qop[KS];
   v8i_t q8[KB8];
   {
-    const size_t row = (((size_t)b * kSlot + j) * hq_all + kvh * r + ci) * D;
+    const size_t row = (((size_t)b * kSlot + j) * a.hq + kvh * r + cq) * D;
     const size_t base = row + (D / 2) * hh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -121,18 +338,18 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
 #pragma unroll
     for (int k = 0; k < KB8; ++k) {
 #pragma unroll
-      for (int w4 = 0; w4 < 8; ++w4) {
-        float x[4];
-        const size_t e0 = row + 64 * k + 32 * hh + 4 * w4;
+      for (int w8 = 0; w8 < 4; ++w8) {
+        float x[8];
+        load8(a.q, row + 64 * k + 32 * hh + 8 * w8, a.q_f32, x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = load1(a.q, e0 + e, a.q_f32);
-        uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
-        d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
-        q8[k][w4] = (int)d;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h2], x[4 * h2 + 1], 0u, false);
+          d = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h2 + 2], x[4 * h2 + 3], d, true);
+          q8[k][2 * w8 + h2] = (int)d;
+        }
       }
     }
   }
-  const float neg_one = opaque_neg_one();
 
   // running statistics (MODE 0) or the merged normaliser (MODE 1)
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -148,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
       float mv[kBatch], lv[kBatch];
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const float* pp = a.partial + (((pbase + min(sp0 + q, nstat - 1)) * kMaxHeads + ci) * 2) * kSlot + j;
+        const float* pp = a.partial + (((pbase + min(sp0 + q, nstat - 1)) * kMaxHeads + cq) * 2) * kSlot + j;
         mv[q] = pp[0];
         lv[q] = pp[kSlot];
       }
@@ -163,204 +380,26 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
     }
     // queries outside the mask get weight 0
     if (hh == 0) {
-      mq[wave][j] = M;
-      lq[wave][j] = ((a.qmask[b] >> j) & 1u) ? 1.0f / L : 0.f;
+      mq[ci][j] = M;
+      lq[ci][j] = ((a.qmask[b] >> j) & 1u) ? 1.0f / L : 0.f;
     }
   }
-
-  // ---- unit loads: the record (16-byte chunks) and this thread's protected
-  // key chunk.  Buffer loads: a unit past the split (or the block) gets empty
-  // resources, so its loads return zeros without memory traffic and every
-  // path writes the same registers.  Two register sets, indexed by the
-  // unrolled position: a unit's loads are issued two iterations before its
-  // record is staged.
-  constexpr int NPF = 2;
-  struct Pre { uint4 rc[RPT]; uint4 pc; int4 hd; };
-  Pre pre[NPF];
-  auto load = [&](int u, Pre& p) __attribute__((always_inline)) {
-    const bool valid = u < min(u1, NC);
-    const bool s1 = u >= np;
-    const int sl = valid ? (s1 ? u - np : u) : 0;
-    const int cap = s1 ? seg1.slot_cap : seg0.slot_cap;
-    const int pcap = s1 ? seg1.prot_cap : seg0.prot_cap;
-    const uint8_t* recp = (s1 ? seg1.records : seg0.records) + (((size_t)b * hkv + kvh) * cap + sl) * rbytes;
-    const uint16_t* prot = (s1 ? seg1.prot_rows : seg0.prot_rows) + ((size_t)b * hkv + kvh) * pcap * D;
-    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)recp, 0, valid ? (int)rbytes : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t pr_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)prot, 0, valid ? (int)min((size_t)pcap * D * 2, (size_t)0x7fffffff) : 0, 0x00020000);
-    const int4 hd = valid ? hdrs[u - u0] : make_int4(0, 0, 0, 0);
-    p.hd = hd;
-#pragma unroll
-    for (int q = 0; q < RPT; ++q)
-      p.rc[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, (q * kThreads + tid) * 16, 0, 0));
-    const int rank = hd.z + __popc((uint32_t)hd.y & ((1u << kt0) - 1u));
-    const int off = (kpair && ((hd.y >> kt0) & 1)) ? (rank * D + 8 * kcg) * 2 : 0x7ff00000;
-    p.pc = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr_, off, 0, 0));
-  };
-  // the block's keys (the stats pass's last split), read before the loop: a
-  // global load inside it would make every unit wait for the prefetch loads
-  // issued before it
-  float xblk[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) xblk[e] = 0.f;
-  if (MODE == 0 && u1 > NC && kpair)
-    load8(a.k_blk, (((size_t)b * kSlot + kt0) * hkv + kvh) * D + 8 * kcg, a.blk_f32, xblk);
-  // a staged unit's header: the block has 32 valid tokens and no protected rows
-  auto header = [&](int u) __attribute__((always_inline)) {
-    return (MODE == 0 && u == NC) ? make_int4(kSlot, 0, 0, 0) : hdrs[u - u0];
-  };
-  // stage unit u's record and protected chunk (a cached unit; the block reads
-  // its keys straight from the block tensor)
-  // Wait for this unit's loads only: the next unit's RPT + 1 loads (and, for
-  // the wave writing contributions, its two stores of the last iteration,
-  // issued after them) stay in flight.  Stated once, before the conditional
-  // stores, so that the compiler adds no wait of its own there.
-  constexpr int kLoadsPerUnit = RPT + 1;
-  static_assert(kLoadsPerUnit + 2 < 16, "vmcnt field");
-  auto stage = [&](int u, const Pre& p) __attribute__((always_inline)) {
-    if (MODE == 1 && wave == kWaves - 1)
-      __builtin_amdgcn_s_waitcnt(0xF70 | (kLoadsPerUnit + 2));
-    else
-      __builtin_amdgcn_s_waitcnt(0xF70 | kLoadsPerUnit);
-    if (MODE == 0 && u == NC) return;
-    uint8_t* rs = rec[u & 1];
-#pragma unroll
-    for (int q = 0; q < RPT; ++q) {
-      const uint32_t off = (uint32_t)(q * kThreads + tid) * 16u;
-      if (off < rbytes) *reinterpret_cast<uint4*>(rs + off) = p.rc[q];
-    }
-    prt[u & 1][tid] = p.pc;
-  };
-  // keys of unit u -> fp16 hi / e5m2 lo operand tiles: token kt0 of channel
-  // group kcg
-  auto dequant = [&](int u) __attribute__((always_inline)) {
-    if (!kpair) return;
-    const int4 h = header(u);
-    const uint8_t* rs = rec[u & 1];
-    const float* km = reinterpret_cast<const float*>(rs + KC + VC) + 8 * kcg;
-    const uint32_t* words = reinterpret_cast<const uint32_t*>(rs);
-    const int t = kt0;
-    float x[8];
-    if (MODE == 0 && u == NC) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = xblk[e];
-    } else if ((h.y >> t) & 1) {
-      const uint4 w = prt[u & 1][tid];
-      x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-      x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-    } else {
-      float code[8];
-      const uint32_t w = KB == 4 ? words[kcg * 32 + t] : words[(kcg >> 1) * 32 + t] >> (16 * (kcg & 1));
-      unpack8<KB>(w, code);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = fmaf(code[e], km[e], km[D + e]);
-    }
-    const int cg = kcg;
-    store_hi_lo8(kt[u & 1][kks][t + 32 * khh],
-                 reinterpret_cast<uint2*>(&klt[u & 1][cg >> 3][(cg >> 1) & 1][t + 32 * ((cg >> 2) & 1)])[cg & 1], x,
-                 neg_one);
-  };
-  // MODE 1: value norms of unit u: token t, channels [cs * VCH, +VCH) of one
-  // value group
-  auto norms = [&](int u) __attribute__((always_inline)) {
-    const uint8_t* rs = rec[u & 1];
-    const int t = tid / VLANES, cs = tid % VLANES, c0 = cs * VCH;
-    const int mm = t / 16, th = (t / 4) % 2, e = (t % 4) + 4 * ((t / 8) % 2);
-    const int wj = VB == 4 ? 2 * mm + th : th;
-    const int bit = VB == 4 ? 4 * e : 2 * (8 * mm + e);
-    const float* vm = reinterpret_cast<const float*>(rs + KC + VC + KM + (c0 >> a.gv_log2) * 256);
-    const float sc = vm[t], zr = vm[kSlot + t];
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(rs + KC) + wj * D + c0;
-    float acc = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < VCH; cc += 4) {
-      const uint4 w4 = *reinterpret_cast<const uint4*>(vw + cc);
-      const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x = fmaf((float)((w[k] >> bit) & ((1u << VB) - 1u)), sc, zr);
-        acc = fmaf(x, x, acc);
-      }
-    }
-    acc = add_dpp<0xB1>(acc);
-    acc = add_dpp<0x4E>(acc);
-    acc = add_dpp<0x141>(acc);
-    acc = add_dpp<0x140>(acc);
-    if (cs == 0) vn[u % 3][t] = sqrtf(acc);
-  };
-  // MODE 1, wave 0: entry contributions of unit u (lanes 0..31) and the
-  // unit's sum over its valid entries (a butterfly over those lanes)
-  auto contribute = [&](int u) __attribute__((always_inline)) {
-    const int4 h = header(u);
-    float cv = 0.f;
-    if (lane < kSlot) {
-      float acc = 0.f;
-      for (int w = 0; w < r; ++w) acc += hsum[u & 1][w][lane];
-      const bool ok = lane < h.x;
-      cv = ok ? vn[u % 3][lane] * acc : 0.f;
-      a.contrib[(((size_t)b * hkv + kvh) * a.ucap + u) * kSlot + lane] = ok ? cv : -1.0f;
-    }
-    const float us = sum32(cv);
-    if (lane == 0) a.unit_contrib[((size_t)b * hkv + kvh) * a.ucap + u] = us;
-  };
-
-  // the split's headers, read once: a unit's protected-row loads depend on its
-  // header, and a global read of it per unit would stall the prefetch
-  for (int i = tid; i < min(u1, NC) - u0; i += kThreads) {
-    const int u = u0 + i;
-    const bool s1 = u >= np;
-    const int sl = s1 ? u - np : u;
-    const int cap = s1 ? seg1.slot_cap : seg0.slot_cap;
-    hdrs[i] = *reinterpret_cast<const int4*>((s1 ? seg1.headers : seg0.headers) + ((size_t)b * cap + sl) * kHeaderBytes);
-  }
-  lds_barrier();
-  // Pipeline.  Before iteration u: unit u's operand tiles are in kt[u & 1]
-  // (and, MODE 1, its value norms in vn[u % 3]); unit u + 1's record is
-  // staged in rec[(u + 1) & 1]; the loads of unit u + 2 are in flight in
-  // pre[(u - u0) % 2] and those of unit u + 3 in the other set.  Iteration u
-  // issues the score MFMAs of unit u, dequantizes unit u + 1 (and its value
-  // norms) while they run, stages unit u + 2 and issues the loads of unit
-  // u + 4, then turns unit u's scores into statistics or per-token sums; one
-  // barrier ends it.
-  load(u0, pre[0]);
-  load(u0 + 1, pre[1]);
-  stage(u0, pre[0]);
-  load(u0 + 2, pre[0]);
-  stage(u0 + 1, pre[1]);
-  load(u0 + 3, pre[1]);
-  lds_barrier();
-  dequant(u0);
-  if (MODE == 1) norms(u0);
-  lds_barrier();
-  // one iteration; pk holds the loads of unit u + 2 (the two register sets
-  // alternate, named statically so that both stay in registers)
-  auto iteration = [&](int u, Pre& pk) __attribute__((always_inline)) {
-    const int4 h = header(u);
-    // Waves 4..7 dequantize and stage first and then issue their MFMAs;
-    // waves 0..3 (one per SIMD, as are 4..7) the other way round.  So on each
-    // SIMD one wave's MFMA chain runs while the other issues vector work,
-    // instead of both waves reaching their MFMAs together after the barrier.
-    const bool late = wave >= 4;
-    auto produce = [&]() __attribute__((always_inline)) {
-      if (u + 1 < u1) {
-        dequant(u + 1);
-        if (MODE == 1) norms(u + 1);
-      }
-      if (u + 2 < u1) stage(u + 2, pk);
-      load(u + 4, pk);
-    };
-    if (late) produce();
-    floatx16 sacc;
+  lds_barrier();                                     // headers
+  lds_barrier();                                     // units u0, u0 + 1 staged
+  lds_barrier();                                     // unit u0's operands
+  for (int u = u0; u < u1; ++u) {
+    const int4 h = (MODE == 0 && u == NC) ? make_int4(kSlot, 0, 0, 0) : hdrs[u - u0];
     if (head) {
+      floatx16 sacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
       // MODE 0: S^T = K Q^T, sacc[i] = S[query j][token 8*(i/4) + 4*hh + i%4];
       // MODE 1: S = Q K^T (the same operand registers, swapped),
       // sacc[i] = S[query 8*(i/4) + 4*hh + i%4][token j]
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2)
-        sacc = MODE == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(kt[u & 1][s2][lane], qop[s2], sacc, 0, 0, 0)
-                         : __builtin_amdgcn_mfma_f32_32x32x16_f16(qop[s2], kt[u & 1][s2][lane], sacc, 0, 0, 0);
+      for (int s = 0; s < KS; ++s)
+        sacc = MODE == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(kt[u & 1][s][lane], qop[s], sacc, 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_f16(qop[s], kt[u & 1][s][lane], sacc, 0, 0, 0);
       // + 2^-12 K_lo' Q8^T (bf8 x e4m3; the E8M0 scale 2^-12 on the lo side)
 #pragma unroll
       for (int kk = 0; kk < KB8; ++kk) {
@@ -369,11 +408,6 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
         sacc = MODE == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kl, q8[kk], sacc, 1, 0, 0, 127 - 12, 0, 127)
                          : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q8[kk], kl, sacc, 0, 1, 0, 127, 0, 127 - 12);
       }
-    }
-    // (waves 0..3) while the MFMAs run: the next unit's operands, the record
-    // after it, and the loads two units further
-    if (!late) produce();
-    if (head) {
       if (MODE == 0) {
         float mx = -__builtin_inff();
 #pragma unroll
@@ -405,25 +439,13 @@ __global__ __launch_bounds__(kThreads, 2) void sel_kernel(const SelArgs a) {
           acc = fmaf(__builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 3], c2, -m4.w)), l4.w, acc);
         }
         const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-        if (hh == 0) hsum[u & 1][wave][j] = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+        if (hh == 0) hsum[u & 1][ci][j] = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
       }
     }
-    // the previous unit's contributions (its per-head sums were complete at
-    // the last barrier)
-    if (MODE == 1 && wave == kWaves - 1 && u > u0) contribute(u - 1);
+    if (writer && u > u0) contribute(u - 1);
     lds_barrier();
-  };
-  static_assert(NPF == 2, "two register sets");
-  // whole pairs, so that the loop is only re-entered after the second set's
-  // loads (the compiler then keeps the first set's wait at two loads), and an
-  // odd last unit
-  int ub = u0;
-  for (; ub + 1 < u1; ub += 2) {
-    iteration(ub, pre[0]);
-    iteration(ub + 1, pre[1]);
   }
-  if (ub < u1) iteration(ub, pre[0]);
-  if (MODE == 1 && wave == kWaves - 1) contribute(u1 - 1);
+  if (writer) contribute(u1 - 1);
   if (MODE == 0) {
     // merge the two halves (the same query's two token sets) and write the partials
     const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_run), __float_as_uint(m_run), false, false);
@@ -449,21 +471,38 @@ __device__ __forceinline__ uint32_t entry_key(float c) {
   return c >= 0.f ? __float_as_uint(c) + 1u : 0u;   // valid entries above every invalid one
 }
 
-// exclusive prefix sum over the workgroup; returns the total in *total
-__device__ uint32_t block_scan(uint32_t v, uint32_t* buf, uint32_t* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTopkThreads; off <<= 1) {
-    const uint32_t add = tid >= off ? buf[tid - off] : 0u;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+// inclusive prefix sum over the 64 lanes of a wave (lane i gets the sum of
+// lanes 0..i), by six shuffle-and-add steps
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_up((int)v, off, 64);
+    v += lane >= off ? u : 0u;
   }
-  const uint32_t incl = buf[tid];
-  *total = buf[kTopkThreads - 1];
+  return v;
+}
+
+// exclusive prefix sum over the workgroup (wave scans, then a scan of the
+// wave totals by wave 0); returns the total in *total.  buf holds at least
+// kTopkThreads / 64 + 1 words.
+__device__ uint32_t block_scan(uint32_t v, uint32_t* buf, uint32_t* total) {
+  constexpr int kW = kTopkThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t incl = wave_scan(v);
+  if (lane == 63) buf[wave] = incl;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    const uint32_t t = lane < kW ? buf[lane] : 0u;
+    const uint32_t ti = wave_scan(t);
+    if (lane < kW) buf[lane] = ti - t;      // exclusive offset of wave `lane`
+    if (lane == kW - 1) buf[kW] = ti;       // the total
+  }
+  __syncthreads();
+  const uint32_t r = buf[wave] + incl - v;
+  *total = buf[kW];
+  __syncthreads();
+  return r;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
@@ -500,26 +539,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
         if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      // counts per digit, then suffix sums (digits above d) by a log-step scan
-      // over 256 threads; the digit d with above(d) < remaining <= above(d) +
-      // count(d) holds the k-th key
-      uint32_t cnt = 0;
-      if (tid < 256) {
-        for (int w = 0; w < kTopkWaves; ++w) cnt += hist[w][tid];
-        scan[tid] = cnt;
-      }
-      __syncthreads();
-      for (int off = 1; off < 256; off <<= 1) {
-        const uint32_t add = (tid < 256 && tid + off < 256) ? scan[tid + off] : 0u;
-        __syncthreads();
-        if (tid < 256) scan[tid] += add;
-        __syncthreads();
-      }
-      if (tid < 256) {
-        const uint32_t incl = scan[tid], above = incl - cnt;
-        if (above < remaining && remaining <= incl) {
-          sh[0] = prefix | ((uint32_t)tid << shift);
-          sh[1] = remaining - above;
+      // counts per digit, then, in wave 0 (lane l holds digits 255 - 4l ..
+      // 252 - 4l, highest first), the counts of the digits above each one; the
+      // digit d with above(d) < remaining <= above(d) + count(d) holds the
+      // k-th key
+      if (wave == 0) {
+        uint32_t cnt[4], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 255 - 4 * (tid & 63) - e;
+          cnt[e] = 0;
+          for (int w = 0; w < kTopkWaves; ++w) cnt[e] += hist[w][d];
+          sum += cnt[e];
+        }
+        uint32_t above = wave_scan(sum) - sum;   // counts of the lanes holding higher digits
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 255 - 4 * (tid & 63) - e;
+          if (above < remaining && remaining <= above + cnt[e]) {
+            sh[0] = prefix | ((uint32_t)d << shift);
+            sh[1] = remaining - above;
+          }
+          above += cnt[e];
         }
       }
       __syncthreads();
