@@ -466,6 +466,8 @@ __global__ __launch_bounds__(kThreads, 1) void sel_kernel(const SelArgs a) {
 
 // ---- exact top-k per (sequence, kv head)
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkLdsKeys = 32 * 1024;   // keys kept in LDS (128 KB); more are re-read from memory
+constexpr int kTopkSmallN = 512;          // up to this many keys, ranks are counted directly
 
 __device__ __forceinline__ uint32_t entry_key(float c) {
   return c >= 0.f ? __float_as_uint(c) + 1u : 0u;   // valid entries above every invalid one
@@ -510,6 +512,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   __shared__ uint32_t hist[kTopkWaves][256];   // per-wave histograms: same-digit keys do not all contend for one word
   __shared__ uint32_t scan[kTopkThreads];
   __shared__ uint32_t sh[4];   // prefix, remaining, candidates
+  __shared__ __align__(16) uint32_t keys[kTopkLdsKeys];
+  __shared__ uint8_t selb[kTopkSmallN];        // few keys: selected or not
   const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
   const int nu = a.nunits[b];
   const size_t pair = (size_t)b * a.hkv + kvh;
@@ -521,21 +525,60 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   uint32_t* mask_out = a.sel_mask + pair * a.ucap;
   int32_t* units_out = a.sel_units + pair * a.ucap;
 
+  // the keys, read from global memory once: in LDS when they fit, so the four
+  // radix passes and the tie pass do not each pay a memory latency
+  const bool in_lds = N <= kTopkLdsKeys;
+  auto key_at = [&](int i) __attribute__((always_inline)) {
+    return in_lds ? keys[i] : entry_key(key_src[i]);
+  };
   if (tid == 0) sh[2] = 0;
-  __syncthreads();
   uint32_t nv = 0;
-  for (int i = tid; i < N; i += kTopkThreads) nv += entry_key(key_src[i]) != 0u;
+  for (int i = tid; i < N; i += kTopkThreads) {
+    const uint32_t key = entry_key(key_src[i]);
+    if (in_lds) keys[i] = key;
+    nv += key != 0u;
+  }
+  __syncthreads();
   atomicAdd(&sh[2], nv);
   __syncthreads();
   const uint32_t k = min((uint32_t)max(a.budget, 0), sh[2]);
-  // radix select of the k-th largest key, most significant digit first
+  // Few keys (unit granularity): each key's rank counted against every other
+  // key in LDS (broadcast reads), kept when the rank is below k.  Otherwise a
+  // radix select of the k-th largest key, most significant digit first.
+  // (The keys are read four at a time, sixteen per iteration, and past N the
+  // array holds zeros, which rank below every valid key.)
+  const bool small = in_lds && N <= kTopkSmallN;
+  if (small) {
+    for (int i = N + tid; i < ((N + 15) & ~15); i += kTopkThreads) keys[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < N; i += kTopkThreads) {
+      const uint32_t ki = keys[i];
+      uint32_t rk = 0;
+      for (int q0 = 0; q0 < N; q0 += 16) {
+        uint4 kv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) kv[g] = *reinterpret_cast<const uint4*>(&keys[q0 + 4 * g]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t kq[4] = {kv[g].x, kv[g].y, kv[g].z, kv[g].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = q0 + 4 * g + e;
+            rk += (kq[e] > ki || (kq[e] == ki && q < i)) ? 1u : 0u;
+          }
+        }
+      }
+      selb[i] = (ki != 0u && rk < k) ? 1 : 0;
+    }
+    __syncthreads();
+  }
   uint32_t prefix = 0, pmask = 0, remaining = k;
-  if (k > 0) {
+  if (k > 0 && !small) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
       __syncthreads();
       for (int i = tid; i < N; i += kTopkThreads) {
-        const uint32_t key = entry_key(key_src[i]);
+        const uint32_t key = key_at(i);
         if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -575,11 +618,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   const int UPT = (nu + kTopkThreads - 1) / kTopkThreads;
   const int ub = tid * UPT, ue = min(nu, ub + UPT);
   uint32_t ties = 0;
-  if (k > 0) {
+  if (k > 0 && !small) {
     if (units) {
-      for (int u = ub; u < ue; ++u) ties += entry_key(key_src[u]) == T;
+      for (int u = ub; u < ue; ++u) ties += key_at(u) == T;
     } else {
-      for (int i = ub * kSlot; i < ue * kSlot; ++i) ties += entry_key(c[i]) == T;
+      for (int i = ub * kSlot; i < ue * kSlot; ++i) ties += key_at(i) == T;
     }
   }
   uint32_t tot;
@@ -589,16 +632,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
     uint32_t m = 0;
     if (k > 0) {
       if (units) {
-        const uint32_t key = entry_key(key_src[u]);
-        bool s = key > T;
-        if (key == T) { s = rank < need; ++rank; }
+        bool s;
+        if (small) {
+          s = selb[u] != 0;
+        } else {
+          const uint32_t key = key_at(u);
+          s = key > T;
+          if (key == T) { s = rank < need; ++rank; }
+        }
         if (s)
           for (int t = 0; t < kSlot; ++t) m |= (c[u * kSlot + t] >= 0.f ? 1u : 0u) << t;
       } else {
         for (int t = 0; t < kSlot; ++t) {
-          const uint32_t key = entry_key(c[u * kSlot + t]);
-          bool s = key > T;
-          if (key == T) { s = rank < need; ++rank; }
+          bool s;
+          if (small) {
+            s = selb[u * kSlot + t] != 0;
+          } else {
+            const uint32_t key = key_at(u * kSlot + t);
+            s = key > T;
+            if (key == T) { s = rank < need; ++rank; }
+          }
           m |= (s ? 1u : 0u) << t;
         }
       }
