@@ -401,9 +401,15 @@ def main():
         def do_attn_sel(i):
             kvq.check(lib.kvq_block_attn_selected(caches[i % L].handle, use_suf, qp, c.Hq, dtc, kbp, vbp, dtc, 32,
                                                   scale, op, kvq.KVQ_BF16, sptr))
+        def do_attend_select(i):
+            kvq.check(lib.kvq_attend_select(caches[i % L].handle, use_suf, qp, c.Hq, dtc, kbp, vbp, dtc, 32, scale,
+                                            op, kvq.KVQ_BF16, None, args.select_budget, args.select_granularity,
+                                            sptr))
         select_ms = timed(do_select, 2 * L, 0)
+        attend_select_ms = timed(do_attend_select, 2 * L, 0)
         attn_sel_ms = timed(do_attn_sel, args.steps, 0)
-        sel = {"budget": args.select_budget, "granularity": args.select_granularity, "select_ms": select_ms, "attn_selected_ms": attn_sel_ms,
+        sel = {"budget": args.select_budget, "granularity": args.select_granularity, "select_ms": select_ms,
+               "attend_select_ms": attend_select_ms, "attn_selected_ms": attn_sel_ms,
                "attn_full_ms": attn_ms,
                "attn_selected_query_tokens_per_s": c.B * 32 / (attn_sel_ms * 1e-3)}
 

@@ -936,6 +936,11 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + c) = w;
         }
       }
+    if (a.row_stats && hh == 0) {
+      float* rs = a.row_stats + (((size_t)b * hkv + kvh) * kSelHeads + ci) * 2 * kSlot + j;
+      rs[0] = m_ref;
+      rs[kSlot] = l_tot;
+    }
   } else if (!a.out_f32) {
     // 16-bit output: the split's O normalised by its own sum and scaled by a
     // power of two per row (row maximum in [2^14, 2^15)), in fp16, so the
@@ -1060,6 +1065,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) out_lds[4 * jq + k][c] = acc[k] / l[k];
+  if (a.row_stats && blockIdx.z == 0 && c == 0) {
+    float* rs = a.row_stats + (((size_t)b * a.hkv + kvh) * kSelHeads + hl) * 2 * kSlot + 4 * jq;
+    *reinterpret_cast<float4*>(rs) = make_float4(mst[0], mst[1], mst[2], mst[3]);
+    *reinterpret_cast<float4*>(rs + kSlot) = make_float4(l[0], l[1], l[2], l[3]);
+  }
   __syncthreads();
   // row jj of this head: channels c0 + 4*(tid % 8) .. +3
   const int jj = tid >> 3, cc = 4 * (tid & 7);
@@ -1138,6 +1148,11 @@ __global__ __launch_bounds__(256) void combine_h16_kernel(const AttnArgs a) {
     }
   }
   const float inv = 1.0f / l;
+  if (a.row_stats && blockIdx.z == 0 && q == 0) {
+    float* rs = a.row_stats + (((size_t)b * a.hkv + kvh) * kSelHeads + hl) * 2 * kSlot + j;
+    rs[0] = mst;
+    rs[kSlot] = l;
+  }
   *reinterpret_cast<float4*>(&out_lds[j][4 * q]) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   __syncthreads();
   // row jj of this head: channels c0 + 4*(tid % 8) .. +3

@@ -115,6 +115,8 @@ void compute_layout(const kvq_config* c, kvq_layout* L) {
   L->sel_mask_offset = off;    off += align256(B * H * ucap * 4);
   L->sel_units_offset = off;   off += align256(B * H * ucap * 4);
   L->sel_count_offset = off;   off += align256(B * H * 4);
+  // kvq_attend_select: the attention's softmax statistics per query row
+  L->sel_stats_offset = off;   off += align256(B * H * kvq::kSelHeads * 2 * kvq::kSlot * 4);
   L->total_bytes = off;
 }
 
@@ -598,7 +600,7 @@ namespace {
 kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                            const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype, int32_t block_len,
                            float softmax_scale, void* d_out, int32_t out_dtype, void* stream, bool selected,
-                           const CommitPlan* fused = nullptr, bool noalloc = false) {
+                           const CommitPlan* fused = nullptr, bool noalloc = false, float* row_stats = nullptr) {
   if (!c) return fail(KVQ_EINVAL, "handle is NULL");
   const kvq_config& cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
@@ -718,6 +720,7 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
   a.split_units = split_units;
   a.use_suffix = use_suffix ? 1 : 0;
   a.fmt = cfg.kv_format;
+  a.row_stats = row_stats;
   if (fused) {
     // one task per committing sequence: slot nslots[0][b], first token 0
     a.commit_blk = 1;
@@ -816,6 +819,120 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
   return KVQ_OK;
 }
 
+// Argument checks of a selection (kvq_select, kvq_attend_select).
+kvq_status select_check(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                        const void* d_k_blk, int32_t blk_dtype, int32_t block_len, float softmax_scale,
+                        int32_t budget, int32_t granularity) {
+  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
+  if (granularity != 1 && granularity != kvq::kSlot) return fail(KVQ_EINVAL, "granularity %d (1 or 32)", granularity);
+  const kvq_config& cfg = c->cfg;
+  const int H = cfg.num_kv_heads;
+  if (use_suffix && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
+  if (block_len != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "block_len %d (supported: 32)", block_len);
+  if (num_q_heads < H || num_q_heads % H != 0 || num_q_heads > cfg.max_q_heads)
+    return fail(KVQ_EINVAL, "num_q_heads %d must be a multiple of %d and <= %d", num_q_heads, H, cfg.max_q_heads);
+  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (blk_dtype != KVQ_F32 && blk_dtype != KVQ_BF16))
+    return fail(KVQ_EINVAL, "dtype must be KVQ_F32 or KVQ_BF16");
+  if (!d_q || !d_k_blk) return fail(KVQ_EINVAL, "q and k_blk must be non-NULL");
+  if (!aligned16(d_q) || !aligned16(d_k_blk)) return fail(KVQ_EINVAL, "q and k_blk must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
+  if (budget < 0) return fail(KVQ_EINVAL, "budget %d", budget);
+  if (cfg.kv_format != KVQ_FMT_INT) return fail(KVQ_EUNSUPPORTED, "selection reads integer-format records only");
+  return ensure_device(c);
+}
+
+// The selection's launches: the statistics pass (unless row_stats holds the
+// attention's per-row softmax statistics), the scoring pass and the top-k.
+kvq_status select_run(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
+                      const void* d_k_blk, int32_t blk_dtype, float softmax_scale, const uint32_t* h_query_mask,
+                      int32_t budget, int32_t granularity, void* stream, float* row_stats) {
+  const kvq_config& cfg = c->cfg;
+  const int B = cfg.batch, H = cfg.num_kv_heads;
+  const int max_splits = cfg.max_splits ? cfg.max_splits : 32;
+  const int ucap = cfg.prefix_slots + cfg.suffix_slots;
+  kvq::SelArgs a;
+  memset(&a, 0, sizeof(a));
+  int max_nc = 0;
+  int64_t total_nc = 0;
+  for (int b = 0; b < B; ++b) {
+    const int np = c->seg[0].nslots[b], ns = use_suffix ? c->seg[1].nslots[b] : 0;
+    a.nslots[0][b] = (uint16_t)np;
+    a.nslots[1][b] = (uint16_t)ns;
+    a.qmask[b] = h_query_mask ? h_query_mask[b] : 0xFFFFFFFFu;
+    max_nc = std::max(max_nc, np + ns);
+    total_nc += np + ns;
+  }
+  // split lengths: one workgroup per compute unit over all (sequence, kv
+  // head) pairs (each workgroup pipelines its units; one fits a CU at D =
+  // 128), at least 4 units, and the stats pass within the partial capacity of
+  // max_splits per pair
+  const int64_t cus = c->num_cus;
+  auto split_len = [&](int64_t total, int maxu) {
+    int su = (int)std::max<int64_t>(4, (total * H + cus - 1) / cus);
+    return std::min(std::max(su, (maxu + max_splits - 1) / max_splits), kvq::kMaxSelSplit);
+  };
+  const int su_stats = split_len(total_nc + B, max_nc + 1);
+  const int su_score = split_len(total_nc, max_nc);
+  if (!row_stats && (int64_t)su_stats * max_splits < max_nc + 1)
+    return fail(KVQ_EUNSUPPORTED, "%d cached units per sequence exceed max_splits %d x %d units", max_nc, max_splits,
+                kvq::kMaxSelSplit);
+  a.q = d_q;
+  a.k_blk = d_k_blk;
+  a.seg[0] = seg_ptrs(c, 0);
+  a.seg[1] = seg_ptrs(c, 1);
+  a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
+  a.contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_contrib_offset);
+  a.unit_contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_unit_offset);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.hq = num_q_heads;
+  a.hkv = H;
+  a.r = num_q_heads / H;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.blk_f32 = blk_dtype == KVQ_F32;
+  a.gv_log2 = ilog2(cfg.v_group_channels);
+  a.record_bytes = (uint32_t)c->lay.record_bytes;
+  a.stats_split_units = su_stats;
+  a.max_splits = max_splits;
+  a.use_suffix = use_suffix ? 1 : 0;
+  a.ucap = ucap;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int D = cfg.head_dim;
+  hipError_t e = hipSuccess;
+  if (row_stats) {
+    // the attention's statistics: one "split" that covers every unit
+    a.partial = row_stats;
+    a.max_splits = 1;
+    a.stats_split_units = max_nc + 1;
+  } else {
+    a.split_units = su_stats;
+    e = kvq::launch_select(a, 0, (max_nc + 1 + su_stats - 1) / su_stats, B, D, cfg.k_bits, cfg.v_bits, st);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "selection stats launch: %s", hipGetErrorString(e));
+  }
+  a.split_units = su_score;
+  e = kvq::launch_select(a, 1, (max_nc + su_score - 1) / su_score, B, D, cfg.k_bits, cfg.v_bits, st);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "selection score launch: %s", hipGetErrorString(e));
+  kvq::TopkArgs t;
+  memset(&t, 0, sizeof(t));
+  t.contrib = a.contrib;
+  t.unit_contrib = a.unit_contrib;
+  t.granularity = granularity;
+  t.sel_mask = reinterpret_cast<uint32_t*>(c->dbuf + c->lay.sel_mask_offset);
+  t.sel_units = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_units_offset);
+  t.sel_count = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_count_offset);
+  t.hkv = H;
+  t.ucap = ucap;
+  t.budget = budget;
+  for (int b = 0; b < B; ++b) t.nunits[b] = (uint16_t)(a.nslots[0][b] + a.nslots[1][b]);
+  e = kvq::launch_topk(t, B, st);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "top-k launch: %s", hipGetErrorString(e));
+  c->sel_valid = true;
+  c->sel_gen = c->commit_gen;
+  c->sel_use_suffix = use_suffix ? 1 : 0;
+  c->sel_budget = budget;
+  return KVQ_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -873,98 +990,28 @@ kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, 
 kvq_status kvq_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads, int32_t q_dtype,
                       const void* d_k_blk, int32_t blk_dtype, int32_t block_len, float softmax_scale,
                       const uint32_t* h_query_mask, int32_t budget, int32_t granularity, void* stream) {
-  if (!c) return fail(KVQ_EINVAL, "handle is NULL");
-  if (granularity != 1 && granularity != kvq::kSlot) return fail(KVQ_EINVAL, "granularity %d (1 or 32)", granularity);
-  const kvq_config& cfg = c->cfg;
-  const int B = cfg.batch, H = cfg.num_kv_heads;
-  if (use_suffix && cfg.suffix_slots == 0) return fail(KVQ_EINVAL, "cache has no suffix segment");
-  if (block_len != kvq::kSlot) return fail(KVQ_EUNSUPPORTED, "block_len %d (supported: 32)", block_len);
-  if (num_q_heads < H || num_q_heads % H != 0 || num_q_heads > cfg.max_q_heads)
-    return fail(KVQ_EINVAL, "num_q_heads %d must be a multiple of %d and <= %d", num_q_heads, H, cfg.max_q_heads);
-  if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (blk_dtype != KVQ_F32 && blk_dtype != KVQ_BF16))
-    return fail(KVQ_EINVAL, "dtype must be KVQ_F32 or KVQ_BF16");
-  if (!d_q || !d_k_blk) return fail(KVQ_EINVAL, "q and k_blk must be non-NULL");
-  if (!aligned16(d_q) || !aligned16(d_k_blk)) return fail(KVQ_EINVAL, "q and k_blk must be 16-byte aligned");
-  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(KVQ_EINVAL, "softmax_scale must be finite and > 0");
-  if (budget < 0) return fail(KVQ_EINVAL, "budget %d", budget);
-  if (cfg.kv_format != KVQ_FMT_INT) return fail(KVQ_EUNSUPPORTED, "selection reads integer-format records only");
-  kvq_status hs = ensure_device(c);
-  if (hs != KVQ_OK) return hs;
+  kvq_status s = select_check(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, blk_dtype, block_len, softmax_scale,
+                              budget, granularity);
+  if (s != KVQ_OK) return s;
+  return select_run(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, blk_dtype, softmax_scale, h_query_mask, budget,
+                    granularity, stream, nullptr);
+}
 
-  const int max_splits = cfg.max_splits ? cfg.max_splits : 32;
-  const int ucap = cfg.prefix_slots + cfg.suffix_slots;
-  kvq::SelArgs a;
-  memset(&a, 0, sizeof(a));
-  int max_nc = 0;
-  int64_t total_nc = 0;
-  for (int b = 0; b < B; ++b) {
-    const int np = c->seg[0].nslots[b], ns = use_suffix ? c->seg[1].nslots[b] : 0;
-    a.nslots[0][b] = (uint16_t)np;
-    a.nslots[1][b] = (uint16_t)ns;
-    a.qmask[b] = h_query_mask ? h_query_mask[b] : 0xFFFFFFFFu;
-    max_nc = std::max(max_nc, np + ns);
-    total_nc += np + ns;
-  }
-  // split lengths: one workgroup per compute unit over all (sequence, kv
-  // head) pairs (each workgroup pipelines its units; one fits a CU at D =
-  // 128), at least 4 units, and the stats pass within the partial capacity of
-  // max_splits per pair
-  const int64_t cus = c->num_cus;
-  auto split_len = [&](int64_t total, int maxu) {
-    int su = (int)std::max<int64_t>(4, (total * H + cus - 1) / cus);
-    return std::min(std::max(su, (maxu + max_splits - 1) / max_splits), kvq::kMaxSelSplit);
-  };
-  const int su_stats = split_len(total_nc + B, max_nc + 1);
-  const int su_score = split_len(total_nc, max_nc);
-  if ((int64_t)su_stats * max_splits < max_nc + 1)
-    return fail(KVQ_EUNSUPPORTED, "%d cached units per sequence exceed max_splits %d x %d units", max_nc, max_splits,
-                kvq::kMaxSelSplit);
-  a.q = d_q;
-  a.k_blk = d_k_blk;
-  a.seg[0] = seg_ptrs(c, 0);
-  a.seg[1] = seg_ptrs(c, 1);
-  a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
-  a.contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_contrib_offset);
-  a.unit_contrib = reinterpret_cast<float*>(c->dbuf + c->lay.sel_unit_offset);
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.hq = num_q_heads;
-  a.hkv = H;
-  a.r = num_q_heads / H;
-  a.q_f32 = q_dtype == KVQ_F32;
-  a.blk_f32 = blk_dtype == KVQ_F32;
-  a.gv_log2 = ilog2(cfg.v_group_channels);
-  a.record_bytes = (uint32_t)c->lay.record_bytes;
-  a.stats_split_units = su_stats;
-  a.max_splits = max_splits;
-  a.use_suffix = use_suffix ? 1 : 0;
-  a.ucap = ucap;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int D = cfg.head_dim;
-  a.split_units = su_stats;
-  hipError_t e = kvq::launch_select(a, 0, (max_nc + 1 + su_stats - 1) / su_stats, B, D, cfg.k_bits, cfg.v_bits, st);
-  if (e != hipSuccess) return fail(KVQ_EHIP, "selection stats launch: %s", hipGetErrorString(e));
-  a.split_units = su_score;
-  e = kvq::launch_select(a, 1, (max_nc + su_score - 1) / su_score, B, D, cfg.k_bits, cfg.v_bits, st);
-  if (e != hipSuccess) return fail(KVQ_EHIP, "selection score launch: %s", hipGetErrorString(e));
-  kvq::TopkArgs t;
-  memset(&t, 0, sizeof(t));
-  t.contrib = a.contrib;
-  t.unit_contrib = a.unit_contrib;
-  t.granularity = granularity;
-  t.sel_mask = reinterpret_cast<uint32_t*>(c->dbuf + c->lay.sel_mask_offset);
-  t.sel_units = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_units_offset);
-  t.sel_count = reinterpret_cast<int32_t*>(c->dbuf + c->lay.sel_count_offset);
-  t.hkv = H;
-  t.ucap = ucap;
-  t.budget = budget;
-  for (int b = 0; b < B; ++b) t.nunits[b] = (uint16_t)(a.nslots[0][b] + a.nslots[1][b]);
-  e = kvq::launch_topk(t, B, st);
-  if (e != hipSuccess) return fail(KVQ_EHIP, "top-k launch: %s", hipGetErrorString(e));
-  c->sel_valid = true;
-  c->sel_gen = c->commit_gen;
-  c->sel_use_suffix = use_suffix ? 1 : 0;
-  c->sel_budget = budget;
-  return KVQ_OK;
+kvq_status kvq_attend_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
+                             int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                             int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,
+                             const uint32_t* h_query_mask, int32_t budget, int32_t granularity, void* stream) {
+  // the selection's arguments are checked before the attention launches;
+  // the attention checks its own before any of its launches
+  kvq_status s = select_check(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, blk_dtype, block_len, softmax_scale,
+                              budget, granularity);
+  if (s != KVQ_OK) return s;
+  float* stats = reinterpret_cast<float*>(c->dbuf + c->lay.sel_stats_offset);
+  s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
+                      softmax_scale, d_out, out_dtype, stream, false, nullptr, false, stats);
+  if (s != KVQ_OK) return s;
+  return select_run(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, blk_dtype, softmax_scale, h_query_mask, budget,
+                    granularity, stream, stats);
 }
 
 }  // extern "C"

@@ -99,6 +99,12 @@ struct AttnArgs {
   // (splits, Hkv, B) grid instead, whose workgroups past a sequence's splits
   // exit at once.
   int32_t num_wg;
+  // Row statistics (null: not written): per (b, kv head, head of the group,
+  // query token) the softmax reference maximum (log2 units, scores times
+  // scale_log2) and the sum of exp2(score - maximum) over every attended
+  // token, fp32 [B][Hkv][kSelHeads][2][32], written by the workgroup that
+  // finishes the row (the attention itself with one split, else the combine)
+  float* row_stats;
   uint32_t wg[kMaxWgTable];
 };
 static_assert(sizeof(AttnArgs) <= 4096, "attention launch arguments fit the kernel-argument segment");
@@ -126,6 +132,7 @@ struct UnrotArgs {
 };
 
 constexpr int kMaxSelSplit = 64;  // units per split of a selection pass
+constexpr int kSelHeads = 8;      // query heads per kv head in the selection's row statistics
 
 // Mask-query selection: the stats pass (MODE 0) and the score pass (MODE 1)
 // run over the cached units of every (sequence, kv head) in splits of

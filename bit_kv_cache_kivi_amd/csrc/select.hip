@@ -44,7 +44,7 @@ constexpr int kWaves = 8;                 // consumer waves: one query head per 
 constexpr int kProd = 4;                  // producer waves (one per SIMD)
 constexpr int kPThreads = 64 * kProd;
 constexpr int kThreads = 64 * (kProd + kWaves);
-constexpr int kMaxHeads = 8;   // query heads per kv head
+constexpr int kMaxHeads = kSelHeads;   // query heads per kv head
 
 template <int CTRL>
 __device__ __forceinline__ float add_dpp(float x) {

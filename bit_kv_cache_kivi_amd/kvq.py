@@ -42,6 +42,7 @@ class KvqLayout(ctypes.Structure):
         ("sel_contrib_offset", c_uint64), ("sel_unit_offset", c_uint64), ("sel_mask_offset", c_uint64),
         ("sel_units_offset", c_uint64),
         ("sel_count_offset", c_uint64),
+        ("sel_stats_offset", c_uint64),
     ]
 
 
@@ -75,6 +76,9 @@ def _load():
         "kvq_attend_commit": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                         c_int32, c_int32, c_float, c_void_p, c_int32, P(c_int32), P(c_int32),
                                         P(c_int32), c_void_p]),
+        "kvq_attend_select": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_int32, c_int32, c_float, c_void_p, c_int32, P(ctypes.c_uint32), c_int32,
+                                        c_int32, c_void_p]),
         "kvq_segment_info": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_int32)]),
         "kvq_set_split_slots": (c_int32, [c_void_p, c_int32]),
         "kvq_set_v_rotation": (c_int32, [c_void_p, P(c_int32), P(c_float)]),
@@ -142,6 +146,13 @@ def _stream_ptr(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return c_void_p(s.cuda_stream)
+
+
+def _mask_array(query_mask):
+    """Per-sequence 32-bit query masks as a host uint32 array (None = all)."""
+    if query_mask is None:
+        return None
+    return (ctypes.c_uint32 * len(query_mask))(*[int(x) & 0xFFFFFFFF for x in query_mask])
 
 
 def _csr(protected):
@@ -332,10 +343,25 @@ class KVCache:
         _on_device(self.buffer, q=q, k_blk=k_blk)
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
-        qm = None if query_mask is None else (ctypes.c_uint32 * len(query_mask))(*[int(x) & 0xFFFFFFFF for x in query_mask])
         check(lib.kvq_select(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]), _dtype_code(q),
                              c_void_p(k_blk.data_ptr()), _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
-                             qm, int(budget), int(granularity), _stream_ptr(stream)))
+                             _mask_array(query_mask), int(budget), int(granularity), _stream_ptr(stream)))
+
+    def attend_select(self, q, k_blk, v_blk, budget, use_suffix=False, query_mask=None, softmax_scale=None,
+                      granularity=1, out_dtype=None, out=None, stream=None):
+        """block_attn over the whole cache, then select as select() does,
+        with each query row's softmax normaliser taken from that attention.
+        Returns out [B, 32, Hq, D]."""
+        out = self._check_attn(q, k_blk, v_blk, out, out_dtype)
+        _per_sequence("query_mask", query_mask, self.cfg.batch)
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.cfg.head_dim)
+        check(lib.kvq_attend_select(self._h, int(bool(use_suffix)), c_void_p(q.data_ptr()), int(q.shape[2]),
+                                    _dtype_code(q), c_void_p(k_blk.data_ptr()), c_void_p(v_blk.data_ptr()),
+                                    _dtype_code(k_blk), int(q.shape[1]), float(softmax_scale),
+                                    c_void_p(out.data_ptr()), _dtype_code(out), _mask_array(query_mask),
+                                    int(budget), int(granularity), _stream_ptr(stream)))
+        return out
 
     def block_attn_selected(self, q, k_blk, v_blk, use_suffix=False, softmax_scale=None, out_dtype=None,
                             out=None, stream=None):

@@ -152,7 +152,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 #define KVQ_SLOT_TOKENS 32   /* K group size along tokens = block length */
 #define KVQ_MAX_BATCH 256
 
@@ -219,6 +219,11 @@ typedef struct {
   uint64_t sel_units_offset;   /* int32 [B][Hkv][ucap] units with a selected
                                   token, ascending                             */
   uint64_t sel_count_offset;   /* int32 [B][Hkv] length of that list          */
+  uint64_t sel_stats_offset;   /* fp32 [B][Hkv][8][2][32] kvq_attend_select's
+                                  softmax statistics per (query head of the
+                                  group, query token): reference maximum of
+                                  score * softmax_scale * log2(e), then the
+                                  sum of exp2(that - maximum)                 */
 } kvq_layout;
 
 typedef struct kvq_cache kvq_cache;
@@ -323,6 +328,28 @@ kvq_status kvq_block_attn_selected(kvq_cache* c, int32_t use_suffix, const void*
                                    int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
                                    int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,
                                    void* stream);
+
+/* Full attention and selection from one pass over the cache: the first
+ * denoising step of a block attends to the whole cache and, from the same
+ * softmax, ranks the entries that its later steps attend to (MaskAhead /
+ * Q-MaskAhead abstract: the mask queries' attention mass decides which KV
+ * entries the block keeps).  Equivalent to kvq_block_attn(c, use_suffix, d_q,
+ * ..., d_out, out_dtype, stream) followed by kvq_select(c, use_suffix, d_q,
+ * ..., h_query_mask, budget, granularity, stream) with the same arguments: the
+ * output is kvq_block_attn's (bit-identical), and the selection follows
+ * kvq_select's definition, except that the softmax normaliser of each query
+ * row is the one the attention computed (its reference maximum and its sum
+ * of the probabilities as rounded to fp16 for the PV product: each term
+ * within 2^-11 relative or 2^-25 absolute of its exact value) instead of one
+ * from a separate statistics pass over the cache.  The attention
+ * writes these statistics to the sel_stats region of the cache buffer, then
+ * the selection's scoring pass and its top-k run on `stream`.  Arguments are
+ * checked before anything is launched; the cache's records must be in the
+ * integer format (as for kvq_select).  Calls on one handle must not overlap. */
+kvq_status kvq_attend_select(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
+                             int32_t q_dtype, const void* d_k_blk, const void* d_v_blk, int32_t blk_dtype,
+                             int32_t block_len, float softmax_scale, void* d_out, int32_t out_dtype,
+                             const uint32_t* h_query_mask, int32_t budget, int32_t granularity, void* stream);
 
 /* Attend, then commit the same block, in one call (SoloQ summary page,
  * commit-time KV quantization paragraph: the block being denoised stays in

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(kvq):
     lib = ctypes.CDLL(SO)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
-    assert kvq.lib.kvq_abi_version() == 6
+    assert kvq.lib.kvq_abi_version() == 7
 
 
 def test_layout_matches_documented_record(kvq):
@@ -206,8 +206,22 @@ def test_selection_validation(kvq):
     assert L["sel_mask_offset"] - L["sel_unit_offset"] >= 2 * 2 * ucap * 4
     assert L["sel_units_offset"] - L["sel_mask_offset"] >= 2 * 2 * ucap * 4
     assert L["sel_count_offset"] - L["sel_units_offset"] >= 2 * 2 * ucap * 4
-    assert L["total_bytes"] - L["sel_count_offset"] >= 2 * 2 * 4
+    assert L["sel_stats_offset"] - L["sel_count_offset"] >= 2 * 2 * 4
+    assert L["total_bytes"] - L["sel_stats_offset"] >= 2 * 2 * 8 * 2 * 32 * 4
+    # the attention-and-selection call checks the selection's arguments (and
+    # the attention's) before any launch
+    for kw, status in cases:
+        a = dict(dict(suf=0, q=p, hq=4, qd=1, kb=p, bd=1, L=32, scale=0.125, budget=8), **kw)
+        if status == 0:
+            continue
+        st = kvq.lib.kvq_attend_select(h, a["suf"], a["q"], a["hq"], a["qd"], a["kb"], p, a["bd"], a["L"],
+                                       a["scale"], p, 1, None, a["budget"], a.get("gran", 1), None)
+        assert st == status, (kw, st, kvq.last_error())
     kvq.lib.kvq_destroy(h)
+    h16 = _handle(kvq, kv_format=2)
+    assert kvq.lib.kvq_attend_select(h16, 0, p, 4, 1, p, p, 1, 32, 0.125, p, 1, None, 8, 1, None) == 2
+    assert "integer-format" in kvq.last_error()
+    kvq.lib.kvq_destroy(h16)
 
 
 def test_sink_protection_counts_against_capacity(kvq):

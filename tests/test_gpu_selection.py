@@ -136,3 +136,52 @@ def test_selection_splits_and_rotation():
         e, x = attention_error(out, ref, "f32")
         print(f"rotated, split={split}: err={e:.2e}")
         assert x <= 0, e
+
+
+@pytest.mark.parametrize("name,T,B,budget,use_suffix,qmask,gran,split,odt", [
+    ("dream7b_4bit", 300, 2, 64, False, [0xFFFF0000, 0x0F0F0F0F], 1, 64, "bf16"),   # one split per row
+    ("dream7b_4bit", 300, 2, 64, False, None, 1, 2, "bf16"),       # split partials, fp16 combine
+    ("dual_long", 400, 2, 150, True, None, 1, 3, "f32"),           # split partials, fp32 combine
+    ("serve_b32", 384, 6, 10_000, False, None, 1, 0, "bf16"),
+    ("dual_long", 400, 2, 5, True, [0x0000FFFF, 0xFFFFFFFF], 32, 0, "f32"),
+    ("tiny", None, None, 40, False, None, 1, 0, "f32"),
+])
+def test_attend_select(name, T, B, budget, use_suffix, qmask, gran, split, odt):
+    """One pass of full attention whose softmax statistics feed the selection:
+    the output bit-identical to kvq_block_attn's, the selection checked as
+    kvq_select's against the oracle.  A first call with other queries leaves
+    statistics that the second must replace."""
+    announce("attend+select", name, T, B, budget, use_suffix, gran, split, odt)
+    w, cache, ora = build_case(W.CONFIGS[name], T, B)
+    c = w.cfg
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    out_dt = torch.float32 if odt == "f32" else torch.bfloat16
+    cache.set_split_slots(split)
+    cache.attend_select((q.float() * 1.7 - 0.3).to(q.dtype), kb, vb, budget, use_suffix=use_suffix, out_dtype=out_dt)
+    out = cache.attend_select(q, kb, vb, budget, use_suffix=use_suffix, query_mask=qmask, granularity=gran,
+                              out_dtype=out_dt)
+    ref = cache.block_attn(q, kb, vb, use_suffix=use_suffix, out_dtype=out_dt)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16) if odt == "bf16" else out.view(torch.int32),
+                       ref.view(torch.int16) if odt == "bf16" else ref.view(torch.int32))
+    selected = check_selection(cache, ora, w, budget, use_suffix, qmask, gran)
+    oref = block_attention_selected(ora, w.q, w.k_blk, w.v_blk, selected, use_suffix=use_suffix)
+    att = cache.block_attn_selected(q, kb, vb, use_suffix=use_suffix, out_dtype=torch.float32)
+    e, x = attention_error(att, oref, "f32")
+    print(f"{name} split={split} {odt}: {sum(len(v) for v in selected.values())} selected, attention err={e:.2e}")
+    assert x <= 0, e
+
+
+def test_attend_select_rotated():
+    """Rotated values: the statistics come from the attention over the rotated
+    basis (scores are unaffected) and the norms from the stored rotated rows."""
+    announce("attend+select rotated")
+    cfg = dataclasses.replace(W.CONFIGS["dream7b_4bit"], v_bits=2, v_group=128)
+    w, cache, ora = build_case(cfg, T=300, B=2, v_rot_block=64)
+    c = w.cfg
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    out = cache.attend_select(q, kb, vb, 100, out_dtype=torch.float32)
+    ref = cache.block_attn(q, kb, vb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    check_selection(cache, ora, w, 100, False, None)
