@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   constexpr int kTopkWaves = kTopkThreads / 64;
   __shared__ uint32_t hist[kTopkWaves][256];   // per-wave histograms: same-digit keys do not all contend for one word
   __shared__ uint32_t scan[kTopkThreads];
-  __shared__ uint32_t sh[4];   // prefix, remaining, candidates
+  __shared__ uint32_t sh[5];   // prefix and remaining of even and odd radix passes, then the valid count
   __shared__ __align__(16) uint32_t keys[kTopkLdsKeys];
   __shared__ uint8_t selb[kTopkSmallN];        // few keys: selected or not
   const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
@@ -531,17 +531,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   auto key_at = [&](int i) __attribute__((always_inline)) {
     return in_lds ? keys[i] : entry_key(key_src[i]);
   };
-  if (tid == 0) sh[2] = 0;
+  if (tid == 0) sh[4] = 0;
   uint32_t nv = 0;
   for (int i = tid; i < N; i += kTopkThreads) {
     const uint32_t key = entry_key(key_src[i]);
     if (in_lds) keys[i] = key;
     nv += key != 0u;
   }
+  nv = wave_scan(nv);          // the wave's count in lane 63: one LDS atomic per wave
   __syncthreads();
-  atomicAdd(&sh[2], nv);
+  if ((tid & 63) == 63) atomicAdd(&sh[4], nv);
   __syncthreads();
-  const uint32_t k = min((uint32_t)max(a.budget, 0), sh[2]);
+  const uint32_t k = min((uint32_t)max(a.budget, 0), sh[4]);
   // Few keys (unit granularity): each key's rank counted against every other
   // key in LDS (broadcast reads), kept when the rank is below k.  Otherwise a
   // radix select of the k-th largest key, most significant digit first.
@@ -574,9 +575,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   }
   uint32_t prefix = 0, pmask = 0, remaining = k;
   if (k > 0 && !small) {
+    // Two barriers per pass: each wave clears and fills its own histogram (in
+    // order, so without a barrier between), and the passes alternate between
+    // two result slots, so that a pass's search never overwrites the slot
+    // the previous pass's result is still read from.
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
-      __syncthreads();
+      const int slot = (shift >> 2) & 2;        // 24, 8 -> 2; 16, 0 -> 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hist[wave][(tid & 63) + 64 * i] = 0;
       for (int i = tid; i < N; i += kTopkThreads) {
         const uint32_t key = key_at(i);
         if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
@@ -600,17 +606,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int d = 255 - 4 * (tid & 63) - e;
           if (above < remaining && remaining <= above + cnt[e]) {
-            sh[0] = prefix | ((uint32_t)d << shift);
-            sh[1] = remaining - above;
+            sh[slot] = prefix | ((uint32_t)d << shift);
+            sh[slot + 1] = remaining - above;
           }
           above += cnt[e];
         }
       }
       __syncthreads();
-      prefix = sh[0];
-      remaining = sh[1];
+      prefix = sh[slot];
+      remaining = sh[slot + 1];
       pmask |= 255u << shift;
-      __syncthreads();
     }
   }
   const uint32_t T = prefix, need = remaining;   // keys > T, and the first `need` keys == T
@@ -626,7 +631,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
     }
   }
   uint32_t tot;
-  uint32_t rank = block_scan(ties, scan, &tot);
+  // (the direct ranking leaves no ties to order: no scan)
+  uint32_t rank = (k > 0 && !small) ? block_scan(ties, scan, &tot) : 0u;
+  // each thread's masks, for its unit-list pass: in LDS (the histograms are
+  // no longer read) when they fit, else read back from memory
+  uint32_t* mlds = &hist[0][0];
+  const bool m_in_lds = nu <= kTopkWaves * 256;
   uint32_t nonzero = 0;
   for (int u = ub; u < ue; ++u) {
     uint32_t m = 0;
@@ -640,8 +650,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
           s = key > T;
           if (key == T) { s = rank < need; ++rank; }
         }
-        if (s)
-          for (int t = 0; t < kSlot; ++t) m |= (c[u * kSlot + t] >= 0.f ? 1u : 0u) << t;
+        if (s) {
+          // the unit's valid tokens (contribution >= 0), eight 16-byte loads
+          const float4* c4 = reinterpret_cast<const float4*>(c + (size_t)u * kSlot);
+          float4 cv[kSlot / 4];
+#pragma unroll
+          for (int g = 0; g < kSlot / 4; ++g) cv[g] = c4[g];
+#pragma unroll
+          for (int g = 0; g < kSlot / 4; ++g)
+            m |= ((cv[g].x >= 0.f ? 1u : 0u) | (cv[g].y >= 0.f ? 2u : 0u) | (cv[g].z >= 0.f ? 4u : 0u) |
+                  (cv[g].w >= 0.f ? 8u : 0u)) << (4 * g);
+        }
       } else {
         for (int t = 0; t < kSlot; ++t) {
           bool s;
@@ -657,11 +676,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
       }
     }
     mask_out[u] = m;
+    if (m_in_lds) mlds[u] = m;
     nonzero += m != 0u;
   }
   uint32_t pos = block_scan(nonzero, scan, &tot);
   for (int u = ub; u < ue; ++u)
-    if (mask_out[u] != 0u) units_out[pos++] = u;
+    if ((m_in_lds ? mlds[u] : mask_out[u]) != 0u) units_out[pos++] = u;
   if (tid == 0) a.sel_count[pair] = (int32_t)tot;
 }
 
