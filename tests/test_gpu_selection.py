@@ -185,3 +185,41 @@ def test_attend_select_rotated():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
     check_selection(cache, ora, w, 100, False, None)
+
+
+def test_attend_select_empty_cache_and_zero_budget():
+    """An empty cache: the attention covers the block alone, nothing is
+    selected, and attention over the (empty) selection equals it.  Then a
+    budget of 0 on a filled cache: no unit listed, no token kept."""
+    announce("attend+select empty cache, budget 0")
+    from bit_kv_cache_kivi_amd import kvq
+    B, H, Hq, D = 2, 2, 4, 64
+    g = np.random.default_rng(41)
+    cache = kvq.KVCache(B, H, D, 4, 4, 64, prefix_tokens=320, prefix_protected=8, max_q_heads=Hq)
+    q = dev(g.standard_normal((B, SLOT, Hq, D)), "bf16")
+    kb = dev(g.standard_normal((B, SLOT, H, D)), "bf16")
+    vb = dev(g.standard_normal((B, SLOT, H, D)), "bf16")
+    out = cache.attend_select(q, kb, vb, 5, out_dtype=torch.float32)
+    ref = cache.block_attn(q, kb, vb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for b in range(B):
+        for h in range(H):
+            _, _, units, _ = cache.selection(b, h, 0)
+            assert units.numel() == 0
+    sel = cache.block_attn_selected(q, kb, vb, out_dtype=torch.float32)
+    assert torch.allclose(sel, ref, rtol=0, atol=1e-6)
+    k = g.standard_normal((B, 200, H, D)).astype(np.float32)
+    v = g.standard_normal((B, 200, H, D)).astype(np.float32)
+    cache.commit(dev(k, "bf16"), dev(v, "bf16"), ntok=[200, 137])
+    out = cache.attend_select(q, kb, vb, 0, out_dtype=torch.float32)
+    ref = cache.block_attn(q, kb, vb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for b, n in enumerate([200, 137]):
+        nu = -(-n // SLOT)
+        for h in range(H):
+            contrib, masks, units, _ = cache.selection(b, h, nu)
+            assert units.numel() == 0 and int((masks != 0).sum()) == 0
+            c = contrib.cpu().numpy()
+            assert np.all(c[:n] >= 0) and np.all(c[n:] == -1.0)
