@@ -96,3 +96,23 @@ def test_full_size_attend_commit_steps():
         assert x <= 0, (s, e)
     compare_commit(cache, ora, 0, c.B)
     cache.close()
+
+
+def test_full_size_attend_select_entries():
+    """kvq_attend_select at full size in the benchmark's launch configuration
+    (bf16 output, split partials merged by the fp16 combine, which also writes
+    the row statistics): the output within the bf16 gate of the oracle's
+    attention, then a per-entry selection of 1024 of the 8224 entries of each
+    (sequence, kv head) -- the radix path of the top-k -- checked as
+    kvq_select's is."""
+    announce("full size attend_select, entries")
+    w, cache, ora = build_case(CFG, extra_slots=2)
+    c = w.cfg
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    budget = 1024
+    out = cache.attend_select(q, kb, vb, budget, out_dtype=torch.bfloat16)
+    e, x = attention_error(out, O.block_attention(ora, w.q, w.k_blk, w.v_blk), "bf16")
+    print(f"attend_select output: err={e:.2e}", flush=True)
+    assert x <= 0, e
+    check_selection(cache, ora, w, budget, False, None, 1)
+    cache.close()
