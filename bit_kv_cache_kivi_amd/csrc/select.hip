@@ -263,21 +263,27 @@ __global__ __launch_bounds__(kThreads, 1) void sel_kernel(const SelArgs a) {
       const float* vm = reinterpret_cast<const float*>(rs + KC + VC + KM + (c0 >> a.gv_log2) * 256);
       const float sc = vm[t], zr = vm[kSlot + t];
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(rs + KC) + wj * D + c0;
-      float acc = 0.f;
+      // sum over the lane's channels of (code * sc + zr)^2 = sc^2 S2 + 2 sc zr
+      // S1 + VCH zr^2, with the code sums S1 and S2 exact in integers (one
+      // bit-field extract, one add and one 24-bit multiply-add per code)
+      uint32_t s1 = 0, s2 = 0;
 #pragma unroll
       for (int cc = 0; cc < VCH; cc += 4) {
         const uint4 w4 = *reinterpret_cast<const uint4*>(vw + cc);
         const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float x = fmaf((float)((w[k] >> bit) & ((1u << VB) - 1u)), sc, zr);
-          acc = fmaf(x, x, acc);
+          const uint32_t cd = __builtin_amdgcn_ubfe(w[k], (uint32_t)bit, (uint32_t)VB);
+          s1 += cd;
+          s2 += cd * cd;
         }
       }
+      float acc = fmaf(sc * sc, (float)s2, fmaf(2.0f * sc * zr, (float)s1, (float)VCH * zr * zr));
       acc = add_dpp<0xB1>(acc);    // quad_perm [1,0,3,2]
       acc = add_dpp<0x4E>(acc);    // quad_perm [2,3,0,1]
       acc = add_dpp<0x141>(acc);   // row_half_mirror: the 8 lanes of the token
-      if (cs == 0) vn[u % 3][t] = sqrtf(acc);
+      // (the sum of squares cannot be negative; rounding of the expanded form can make it so)
+      if (cs == 0) vn[u % 3][t] = sqrtf(fmaxf(acc, 0.f));
     };
     lds_barrier();                                   // headers
     load(u0, pre[0]);
