@@ -33,6 +33,7 @@
 // A split's partial (reference maximum, sum, unnormalised O) goes to the
 // workspace and the combine kernel merges splits with log-sum-exp weights; a
 // single split writes the normalised output itself.
+#include <cstring>
 #include <mutex>
 
 #include "commit_slot.h"
@@ -917,7 +918,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       for (int i = 0; i < 16; ++i) o[ct][i] += z;
     }
   }
-  if (nsplit == 1) {
+  if (nsplit == 1 && !a.force_partials) {
     const float inv = 1.0f / l_tot;
     const size_t row = ((size_t)b * kSlot + j) * hq_all + hq;
 #pragma unroll
@@ -1165,8 +1166,134 @@ __global__ __launch_bounds__(256) void combine_h16_kernel(const AttnArgs a) {
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
 }
 
+// The fp16-partial merge of a cache with rotated values (16-bit output): one
+// workgroup per (query head, sequence) holds all D channels of the head's 32
+// rows, so after the merge it applies the transposed rotation R^T = P^T
+// (I kron H) (mix^T kron I) to each row in LDS and writes the output in the
+// caller's basis (one partial when the pair has one split).  A row belongs to
+// D / 4 consecutive lanes of one wave, so the Hadamard stages need only
+// wave-level ordering.
+struct RotCombineArgs {
+  const float* partial;
+  void* out;
+  float* row_stats;
+  const int32_t* sel_count;
+  int32_t hq, hkv, r, split_units, max_splits, use_suffix;
+  uint16_t nslots[2][KVQ_MAX_BATCH];
+  int32_t block;                 // Hadamard block b
+  float mix[64];                 // k x k, k = D / b
+  uint8_t perm_inv[128];         // output channel c takes rotated coordinate perm_inv[c]
+};
+
+__device__ __forceinline__ void row_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * D / 8) void combine_rot_kernel(const RotCombineArgs a) {
+  constexpr int kBatch = 8;     // splits loaded at once
+  constexpr int TPR = D / 4;    // threads per row in the rotation (four channels each)
+  __shared__ __align__(16) float zb[kSlot][D + 4];   // merged rows (rotated basis)
+  __shared__ __align__(16) float yb[kSlot][D + 4];   // after the transposed mix
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int np = a.nslots[0][b], ns_all = a.nslots[1][b];
+  const int ns = a.use_suffix ? ns_all : 0;
+  const int r = a.r, kvh = hq / r, hl = hq % r;
+  const int U = (a.sel_count ? a.sel_count[b * a.hkv + kvh] : np + ns) + 1;
+  const int nsplit = (U + a.split_units - 1) / a.split_units;
+  const int chunk = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int j = tid & 31, q = tid >> 5;
+  const int c0 = chunk * 32;
+  const size_t pstride = (size_t)r * PartialH16<D>::kBytes;
+  const uint8_t* p0 = reinterpret_cast<const uint8_t*>(a.partial) +
+                      ((((size_t)b * a.hkv + kvh) * a.max_splits) * r + hl) * PartialH16<D>::kBytes;
+  const uint8_t* po = p0 + ((size_t)(c0 / 4 + q) * kSlot + j) * 8;
+  const float* ps = reinterpret_cast<const float*>(p0 + PartialH16<D>::kStats) + j;
+  float mst = -__builtin_inff(), l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto wt = [](float m, float ref) __attribute__((always_inline)) {
+    return ref == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - ref);
+  };
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    uint2 v[kBatch];
+    float mv[kBatch], lv[kBatch];
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const size_t off = (size_t)min(s0 + u, nsplit - 1) * pstride;   // clamped repeats are masked below
+      v[u] = *reinterpret_cast<const uint2*>(po + off);
+      const float* st = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ps) + off);
+      mv[u] = st[0];
+      lv[u] = st[kSlot];
+      ev[u] = __float_as_int(st[2 * kSlot]);
+    }
+    float mn = mst;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mn = fmaxf(mn, mv[u]);
+    const float sc = wt(mst, mn);
+    l *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] *= sc;
+    mst = mn;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + u < nsplit) {
+        const float w = wt(mv[u], mst) * lv[u];
+        const float wo = __builtin_amdgcn_ldexpf(w, ev[u]);
+        l += w;
+        acc[0] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu)), wo, acc[0]);
+        acc[1] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x >> 16)), wo, acc[1]);
+        acc[2] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y & 0xFFFFu)), wo, acc[2]);
+        acc[3] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y >> 16)), wo, acc[3]);
+      }
+    }
+  }
+  const float inv = 1.0f / l;
+  if (a.row_stats && chunk == 0 && q == 0) {
+    float* rs = a.row_stats + (((size_t)b * a.hkv + kvh) * kSelHeads + hl) * 2 * kSlot + j;
+    rs[0] = mst;
+    rs[kSlot] = l;
+  }
+  *reinterpret_cast<float4*>(&zb[j][c0 + 4 * q]) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  __syncthreads();
+  // row rr, lane-in-row e0 (TPR lanes of one wave per row)
+  const int rr = threadIdx.x / TPR, e0 = threadIdx.x % TPR;
+  const int blk = a.block, k = D / blk;
+  // transposed mix: y[l*b + i] = sum over m of mix[m][l] * z[m*b + i]
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int e = e0 + TPR * t, lb = e / blk, i = e % blk;
+    float acc_m = 0.f;
+    for (int m = 0; m < k; ++m) acc_m = fmaf(a.mix[m * k + lb], zb[rr][m * blk + i], acc_m);
+    yb[rr][e] = acc_m;
+  }
+  row_sync();
+  for (int h = 1; h < blk; h *= 2) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int p = e0 + TPR * t;                // pair index
+      const int i = (p / h) * 2 * h + p % h;
+      const float x = yb[rr][i], y = yb[rr][i + h];
+      yb[rr][i] = x + y;
+      yb[rr][i + h] = x - y;
+    }
+    row_sync();
+  }
+  // output channels c .. c + 3 of the row: x[c] = y[perm_inv[c]] / sqrt(b)
+  const float inv_sqrt_b = blk == 16 ? 0.25f : 0.125f;
+  const int c = 4 * e0;
+  const float x0 = yb[rr][a.perm_inv[c]] * inv_sqrt_b, x1 = yb[rr][a.perm_inv[c + 1]] * inv_sqrt_b;
+  const float x2 = yb[rr][a.perm_inv[c + 2]] * inv_sqrt_b, x3 = yb[rr][a.perm_inv[c + 3]] * inv_sqrt_b;
+  uint2 w;
+  w.x = f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16);
+  w.y = f32_to_bf16_bits(x2) | (f32_to_bf16_bits(x3) << 16);
+  const size_t o = (((size_t)b * kSlot + rr) * a.hq + hq) * D + c;
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = w;
+}
+
 template <int KB, int VB, int D>
-hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) {
+hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s, const RotParams* unrot) {
   const dim3 grid = a.num_wg ? dim3(a.num_wg) : dim3(grid_splits, a.hkv, B);
   const dim3 block((kProducerWaves + a.r) * 64);   // producers + one consumer per query head
   bool done = false;
@@ -1189,15 +1316,33 @@ hipError_t launch_kbd(const AttnArgs& a, int grid_splits, int B, hipStream_t s) 
     else          hipLaunchKernelGGL((attn_kernel<KB, VB, D, 8, false, 0>), grid, block, 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || grid_splits <= 1) return e;
+  if (e != hipSuccess) return e;
+  if (a.force_partials) {
+    RotCombineArgs c;
+    std::memset(&c, 0, sizeof(c));
+    c.partial = a.partial;
+    c.out = a.out;
+    c.row_stats = a.row_stats;
+    c.sel_count = a.sel_count;
+    c.hq = a.hq; c.hkv = a.hkv; c.r = a.r;
+    c.split_units = a.split_units; c.max_splits = a.max_splits; c.use_suffix = a.use_suffix;
+    std::memcpy(c.nslots, a.nslots, sizeof(c.nslots));
+    c.block = unrot->block;
+    const int k = D / unrot->block;
+    for (int i = 0; i < k * k; ++i) c.mix[i] = unrot->mix[i];
+    for (int i = 0; i < D; ++i) c.perm_inv[unrot->perm[i]] = (uint8_t)i;
+    hipLaunchKernelGGL((combine_rot_kernel<D>), dim3(a.hq, B), dim3(64 * D / 8), 0, s, c);
+    return hipGetLastError();
+  }
+  if (grid_splits <= 1) return e;
   if (a.out_f32) hipLaunchKernelGGL((combine_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
   else           hipLaunchKernelGGL((combine_h16_kernel<D>), dim3(a.hq, B, D / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
-hipError_t launch_kb(const AttnArgs& a, int grid_splits, int B, int D, hipStream_t s) {
-  return D == 64 ? launch_kbd<KB, VB, 64>(a, grid_splits, B, s) : launch_kbd<KB, VB, 128>(a, grid_splits, B, s);
+hipError_t launch_kb(const AttnArgs& a, int grid_splits, int B, int D, hipStream_t s, const RotParams* unrot) {
+  return D == 64 ? launch_kbd<KB, VB, 64>(a, grid_splits, B, s, unrot) : launch_kbd<KB, VB, 128>(a, grid_splits, B, s, unrot);
 }
 
 }  // namespace
@@ -1227,11 +1372,12 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
-                            hipStream_t stream) {
-  if (kb == 4 && vb == 4) return launch_kb<4, 4>(a, grid_splits, B, D, stream);
-  if (kb == 4 && vb == 2) return launch_kb<4, 2>(a, grid_splits, B, D, stream);
-  if (kb == 2 && vb == 4) return launch_kb<2, 4>(a, grid_splits, B, D, stream);
-  return launch_kb<2, 2>(a, grid_splits, B, D, stream);
+                            hipStream_t stream, const RotParams* unrot) {
+  if (a.force_partials && !unrot) return hipErrorInvalidValue;
+  if (kb == 4 && vb == 4) return launch_kb<4, 4>(a, grid_splits, B, D, stream, unrot);
+  if (kb == 4 && vb == 2) return launch_kb<4, 2>(a, grid_splits, B, D, stream, unrot);
+  if (kb == 2 && vb == 4) return launch_kb<2, 4>(a, grid_splits, B, D, stream, unrot);
+  return launch_kb<2, 2>(a, grid_splits, B, D, stream, unrot);
 }
 
 }  // namespace kvq

@@ -684,12 +684,16 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
   const int D = cfg.head_dim;
   const size_t blk_elems = (size_t)B * kvq::kSlot * H * D;
   uint8_t* rot_ws = c->dbuf + c->lay.rotation_offset;
+  // rotated values, 16-bit output: the merge applies the transposed rotation
+  // (every pair hands its splits to it, one included); an fp32 output keeps
+  // the fp32 partials and a separate unrotation
+  const bool rot_merge = c->rot.block != 0 && out_dtype == KVQ_BF16;
   a.partial = reinterpret_cast<float*>(c->dbuf + c->lay.workspace_offset);
   a.max_splits = max_splits;
   if (noalloc) {
-    const size_t part = grid_splits > 1 ? align256((uint64_t)B * H * grid_splits * (num_q_heads / H) * (D + 2) *
-                                                   kvq::kSlot * 4)
-                                        : 0;
+    const size_t part = (grid_splits > 1 || rot_merge)
+                            ? align256((uint64_t)B * H * grid_splits * (num_q_heads / H) * (D + 2) * kvq::kSlot * 4)
+                            : 0;
     const size_t rot = c->rot.block ? align256(2 * blk_elems * 4) + align256((uint64_t)B * kvq::kSlot * num_q_heads * D * 4)
                                     : 0;
     if (part + rot > kvq::kNoAllocScratchBytes)
@@ -800,12 +804,17 @@ kvq_status block_attn_impl(kvq_cache* c, int32_t use_suffix, const void* d_q, in
     a.v_blk = p.v_out;
     a.blk_f32 = 1;
     a.v_centred = 1;
-    a.out = rot_o;
-    a.out_f32 = 1;
+    if (rot_merge) {
+      a.force_partials = 1;
+    } else {
+      a.out = rot_o;
+      a.out_f32 = 1;
+    }
   }
-  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st);
+  hipError_t e = kvq::launch_attention(a, grid_splits, B, D, cfg.k_bits, cfg.v_bits, st,
+                                       rot_merge ? &c->rot : nullptr);
   if (e != hipSuccess) return fail(KVQ_EHIP, "attention launch: %s", hipGetErrorString(e));
-  if (rot_o) {
+  if (rot_o && !rot_merge) {
     kvq::UnrotArgs u;
     memset(&u, 0, sizeof(u));
     u.src = rot_o;

@@ -105,6 +105,10 @@ struct AttnArgs {
   // token, fp32 [B][Hkv][kSelHeads][2][32], written by the workgroup that
   // finishes the row (the attention itself with one split, else the combine)
   float* row_stats;
+  // Rotated values with a 16-bit output: every (sequence, kv head) hands its
+  // splits (one included) to the merge as fp16 partials, and the merge also
+  // applies the transposed rotation
+  int32_t force_partials;
   uint32_t wg[kMaxWgTable];
 };
 static_assert(sizeof(AttnArgs) <= 4096, "attention launch arguments fit the kernel-argument segment");
@@ -191,8 +195,9 @@ __host__ __device__ constexpr uint32_t record_bytes_h16(int D, int kb, int vb, i
 // Launchers (defined in the .hip files); return the launch status.
 hipError_t launch_commit(const CommitArgs& a, int ntasks, int D, int kb, int vb, bool f32_in,
                          hipStream_t stream);
+// unrot: with a.force_partials, the rotation whose transpose the merge applies
 hipError_t launch_attention(const AttnArgs& a, int grid_splits, int B, int D, int kb, int vb,
-                            hipStream_t stream);
+                            hipStream_t stream, const RotParams* unrot = nullptr);
 hipError_t launch_blk_prep(const BlkPrepArgs& a, int D, hipStream_t stream);
 hipError_t launch_select(const SelArgs& a, int mode, int grid_splits, int B, int D, int kb, int vb,
                          hipStream_t stream);

@@ -45,8 +45,11 @@ def test_rotated_commit_and_attention(name, T, B, block):
 
 @pytest.mark.parametrize("kb,vb,gv,block", [(2, 2, 32, 16), (4, 2, 128, 64), (2, 4, 64, 16)])
 def test_rotated_value_groups_and_splits(kb, vb, gv, block):
-    """Every value-group size under rotation, with forced split-K (the combine
-    kernel then writes the rotated output before it is rotated back)."""
+    """Every value-group size under rotation, with forced split-K and with one
+    split per pair.  fp32 output: the fp32 merge writes the rotated output,
+    which is then rotated back; bf16 output: every pair's splits (one
+    included) go to the fp16 merge, which also applies the transposed
+    rotation."""
     announce("rotated groups", kb, vb, gv, block)
     cfg = dataclasses.replace(W.CONFIGS["dream7b_4bit"], k_bits=kb, v_bits=vb, v_group=gv)
     w, cache, ora = build_case(cfg, T=300, B=2, v_rot_block=block)
@@ -54,12 +57,15 @@ def test_rotated_value_groups_and_splits(kb, vb, gv, block):
     compare_commit(cache, ora, 0, c.B)
     ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk)
     q, k_, v_ = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
-    for split in (0, 3):
+    for split in (0, 3, 1000):
         cache.set_split_slots(split)
         out = cache.block_attn(q, k_, v_, out_dtype=torch.float32)
         e, x = attention_error(out, ref, "f32")
-        print(f"kb={kb} vb={vb} gv={gv} b={block} split={split}: err={e:.2e}")
+        out16 = cache.block_attn(q, k_, v_, out_dtype=torch.bfloat16)
+        e16, x16 = attention_error(out16, ref, "bf16")
+        print(f"kb={kb} vb={vb} gv={gv} b={block} split={split}: err={e:.2e} bf16-out err={e16:.2e}")
         assert x <= 0, f"fp32 output error {e}"
+        assert x16 <= 0, f"bf16 output error {e16}"
 
 
 def test_rotated_fp32_input_partial_slots():
