@@ -47,9 +47,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "1241375367dbd2c3b7850a955beea2b45e9ed3217f964869e59b9e3c22ac3e01",
-        "kib": {"attn_kernel": {"fetch": 27225.25, "write": 15008},
-                "combine_h16_kernel": {"fetch": 7536, "write": 1792}},
+        "attn_source_sha256": "8529158a4f2a09d164e63df1b8ee54363557323861bc1a4f8447a27728e6da8e",
+        "kib": {"attn_kernel": {"fetch": 27230.25, "write": 15008},
+                "combine_h16_kernel": {"fetch": 7531, "write": 1792}},
     },
 }
 
