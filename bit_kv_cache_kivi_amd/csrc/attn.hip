@@ -747,13 +747,18 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       load_unit(i + 4, pre0, h4);
       __syncthreads();
     }
-    if constexpr (!CEN) {
-      if (fuse) {
-        // the pipeline's last barrier has passed: the producers own rawbuf
-        static_assert(sizeof(typename SlotQuant<KB, VB, D, true, false, FMT>::Lds) + 16 +
-                          SlotQuant<KB, VB, D, true, false, FMT>::REC_MAX <= sizeof(rawbuf),
-                      "the fused commit fits the staging buffers");
-        uint8_t* base = &rawbuf[0][0];
+    if (fuse) {
+      // the pipeline's last barrier has passed: the producers own rawbuf
+      static_assert(sizeof(typename SlotQuant<KB, VB, D, true, false, FMT>::Lds) + 16 +
+                        SlotQuant<KB, VB, D, true, false, FMT>::REC_MAX <= sizeof(rawbuf),
+                    "the fused commit fits the staging buffers");
+      uint8_t* base = &rawbuf[0][0];
+      if constexpr (CEN) {
+        // rotated values: the block's rows are the fp32 keys and the rotated
+        // values staged for this launch (the same rotation, in the same
+        // order, as the commit kernel applies), quantized without rotating
+        commit_block<KB, VB, D, true, FMT>(base, sizeof(rawbuf), a, b, kvh, tid);
+      } else {
         if (blk_f32) commit_block<KB, VB, D, true, FMT>(base, sizeof(rawbuf), a, b, kvh, tid);
         else         commit_block<KB, VB, D, false, FMT>(base, sizeof(rawbuf), a, b, kvh, tid);
       }
@@ -833,7 +838,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   __syncthreads();
   if (ci >= r) {
     for (int i = 0; i < n_int; ++i) __syncthreads();
-    if (!CEN && fuse) __syncthreads();   // the fused commit's barrier
+    if (fuse) __syncthreads();   // the fused commit's barrier
     return;
   }
   half8 pop[2], va[CT][2];
@@ -991,7 +996,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
       base[(D + 1) * kSlot + j] = l_tot;
     }
   }
-  if (!CEN && fuse) __syncthreads();   // the fused commit's barrier
+  if (fuse) __syncthreads();   // the fused commit's barrier
 }
 
 // One workgroup per (query head, sequence, 32-channel chunk): merges the

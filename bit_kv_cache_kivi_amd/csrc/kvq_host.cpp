@@ -979,16 +979,9 @@ kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, 
   kvq_status s = commit_plan(c, KVQ_PREFIX, 0, d_k_blk, d_v_blk, blk_dtype, block_len, h_ntok, h_prot_off,
                              h_prot_idx, plan);
   if (s != KVQ_OK) return s;
-  if (c->cfg.v_rotation_block != 0) {
-    // rotated values: the attention reads a rotated copy of the block, so the
-    // commit (which rotates the raw values itself) is a launch of its own
-    s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
-                        softmax_scale, d_out, out_dtype, stream, false);
-    if (s != KVQ_OK) return s;
-    return commit_run(c, plan, static_cast<hipStream_t>(stream));
-  }
   // one launch: the workgroup holding each (sequence, kv head)'s block also
-  // commits it
+  // commits it (with rotated values, from the rotated copy of the block that
+  // the attention reads)
   s = block_attn_impl(c, use_suffix, d_q, num_q_heads, q_dtype, d_k_blk, d_v_blk, blk_dtype, block_len,
                       softmax_scale, d_out, out_dtype, stream, false, &plan);
   if (s != KVQ_OK) return s;

@@ -363,7 +363,9 @@ kvq_status kvq_attend_select(kvq_cache* c, int32_t use_suffix, const void* d_q, 
  * (sequence b, kv head h) also quantizes that block's keys and values for kv
  * head h into the next prefix slot once its attention work is done (the new
  * slot is one no attention of the call reads).  For a cache with value
- * rotation the commit is a second launch on `stream`.  The commit is checked
+ * rotation the launch quantizes the block's values from the rotated copy the
+ * attention reads (computed in the same order as kvq_commit's rotation, so
+ * the records are the same bytes).  The commit is checked
  * before anything is launched: on an error the cache is unchanged.  Calls on
  * one handle must not overlap. */
 kvq_status kvq_attend_commit(kvq_cache* c, int32_t use_suffix, const void* d_q, int32_t num_q_heads,
