@@ -47,9 +47,9 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "8529158a4f2a09d164e63df1b8ee54363557323861bc1a4f8447a27728e6da8e",
-        "kib": {"attn_kernel": {"fetch": 27230.25, "write": 15008},
-                "combine_h16_kernel": {"fetch": 7531, "write": 1792}},
+        "attn_source_sha256": "3fc4c88f15e8c209fe5fed3f437db1066a38161e890f9840d1f25634b9d873ca",
+        "kib": {"attn_kernel": {"fetch": 27229.25, "write": 15008},
+                "combine_h16_kernel": {"fetch": 7536, "write": 1792}},
     },
 }
 
