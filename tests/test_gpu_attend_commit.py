@@ -19,11 +19,15 @@ from bit_kv_cache_kivi_amd import kvq  # noqa: E402
 from gpu_util import announce, attention_error, build_case, compare_commit, dev  # noqa: E402
 
 
-@pytest.mark.parametrize("name,T,B,nsteps,v_rot", [
-    ("tiny", None, None, 3, 0), ("dream7b_4bit", 300, 2, 4, 0), ("dual_long", 400, 2, 3, 0),
-    ("serve_b32", 200, 6, 2, 0), ("dream7b_4bit", 300, 2, 2, 64)])
-def test_attend_commit_steps(name, T, B, nsteps, v_rot):
-    announce("attend_commit", name, T, B, nsteps, v_rot)
+@pytest.mark.parametrize("name,T,B,nsteps,v_rot,odt", [
+    ("tiny", None, None, 3, 0, "f32"), ("dream7b_4bit", 300, 2, 4, 0, "f32"), ("dual_long", 400, 2, 3, 0, "f32"),
+    ("serve_b32", 200, 6, 2, 0, "f32"), ("dream7b_4bit", 300, 2, 2, 64, "f32"), ("dream7b_4bit", 300, 2, 2, 64, "bf16"),
+    ("dream7b_4bit", 300, 2, 2, 0, "bf16")])
+def test_attend_commit_steps(name, T, B, nsteps, v_rot, odt):
+    """With rotated values and a bf16 output, the merge also rotates the output
+    back and the fused commit quantizes the rotated copy of the block."""
+    announce("attend_commit", name, T, B, nsteps, v_rot, odt)
+    out_dt = torch.float32 if odt == "f32" else torch.bfloat16
     w, cache, ora = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1, v_rot_block=v_rot)
     _, twin, _ = build_case(W.CONFIGS[name], T, B, extra_slots=nsteps + 1, v_rot_block=v_rot)
     c = w.cfg
@@ -39,11 +43,11 @@ def test_attend_commit_steps(name, T, B, nsteps, v_rot):
         ref = O.block_attention(ora, q, kb, vb, use_suffix=use_suffix)
         dq, dk, dv = dev(q, c.dtype), dev(kb, c.dtype), dev(vb, c.dtype)
         out = cache.attend_commit(dq, dk, dv, ntok=ntok, protected=prot_s, use_suffix=use_suffix,
-                                  out_dtype=torch.float32)
-        out2 = twin.block_attn(dq, dk, dv, use_suffix=use_suffix, out_dtype=torch.float32)
+                                  out_dtype=out_dt)
+        out2 = twin.block_attn(dq, dk, dv, use_suffix=use_suffix, out_dtype=out_dt)
         twin.commit(dk, dv, ntok=ntok, protected=prot_s)
         ora.commit(0, kb, vb, ntok=ntok, prot=prot_s)
-        e, x = attention_error(out, ref, "f32")
+        e, x = attention_error(out, ref, odt)
         print(f"{name} step {s}: err={e:.2e}")
         assert x <= 0, (s, e)
         assert torch.equal(out, out2), f"step {s}: attend_commit output differs from block_attn"
