@@ -30,9 +30,14 @@
 // consumers 4..7 first run the softmax of unit i-2, then its PV and the
 // scores of unit i-1.  On each SIMD one consumer's MFMA work thus overlaps
 // the other consumer's softmax and the producer's dequantization.
-// A split's partial (reference maximum, sum, unnormalised O) goes to the
-// workspace and the combine kernel merges splits with log-sum-exp weights; a
-// single split writes the normalised output itself.
+// A split's partial (reference maximum, sum and O: fp32 unnormalised for an
+// fp32 output, fp16 normalised for a 16-bit one) goes to the workspace and a
+// merge kernel combines the splits with log-sum-exp weights; a single split
+// writes the normalised output itself.  With rotated values and a 16-bit
+// output every pair goes through the merge, which also rotates the output
+// back.  Optionally the final per-row maximum and sum are written as well
+// (the selection's softmax statistics), and the workgroup holding a block can
+// also commit it (the one-launch step).
 #include <cstring>
 #include <mutex>
 
