@@ -47,7 +47,7 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "3fc4c88f15e8c209fe5fed3f437db1066a38161e890f9840d1f25634b9d873ca",
+        "attn_source_sha256": "b200ebc3093877972398394dcf139458e63678ad54288250013686dc224d5b58",
         "kib": {"attn_kernel": {"fetch": 27229.25, "write": 15008},
                 "combine_h16_kernel": {"fetch": 7536, "write": 1792}},
     },
