@@ -79,20 +79,25 @@ def test_full_size_unit_selection():
     cache.close()
 
 
-def test_full_size_attend_commit_steps():
+@pytest.mark.parametrize("v_rot,odt", [(0, "f32"), (64, "bf16")])
+def test_full_size_attend_commit_steps(v_rot, odt):
     """Two one-launch steps at full size: each output against the oracle's
-    attention over the cache before its commit; records afterwards."""
-    announce("full size attend_commit")
-    w, cache, ora = build_case(CFG, extra_slots=3)
+    attention over the cache before its commit; records afterwards.  With
+    rotated values and bf16 output (the rotated benchmark's configuration),
+    the merge rotates the output back and the fused commit quantizes the
+    rotated copy of the block."""
+    announce("full size attend_commit", v_rot, odt)
+    w, cache, ora = build_case(CFG, extra_slots=3, v_rot_block=v_rot)
     c = w.cfg
+    out_dt = torch.float32 if odt == "f32" else torch.bfloat16
     for s in range(2):
         kb_, vb_, prot = W.step_block(c, s)
         ref = O.block_attention(ora, w.q, kb_, vb_)
         out = cache.attend_commit(dev(w.q, c.dtype), dev(kb_, c.dtype), dev(vb_, c.dtype), protected=prot,
-                                  out_dtype=torch.float32)
+                                  out_dtype=out_dt)
         ora.commit(0, kb_, vb_, prot=prot)
-        e, x = attention_error(out, ref, "f32")
-        print(f"attend_commit step {s}: err={e:.2e}", flush=True)
+        e, x = attention_error(out, ref, odt)
+        print(f"attend_commit step {s} (rotation {v_rot}, {odt}): err={e:.2e}", flush=True)
         assert x <= 0, (s, e)
     compare_commit(cache, ora, 0, c.B)
     cache.close()
