@@ -1,0 +1,48 @@
+"""Every query-group size r = Hq / Hkv the attention supports (needs an MI355X).
+
+The attention workgroup runs one consumer wave per query head of its kv head:
+the four-consumer build serves r <= 4, the eight-consumer build r = 5..8, and
+the early/late consumer roles split at four, so r from 2 to 8 covers every
+count of live consumers in both builds (the workloads themselves use r = 1, 6
+and 7).  Each case commits a seeded prefix (10% protected key rows, ragged
+lengths, lognormal key channel scales), checks the records byte for byte,
+then attends with fp32 and bf16 outputs at one split, at several and
+automatically (bf16: fp16 split partials and their merge; fp32: fp32
+partials), against the fp64 oracle, with the 2e-3 gate (plus half a bf16 ulp
+for bf16 output).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_util import announce, attention_error, build_case, compare_commit, dev  # noqa: E402
+
+
+@pytest.mark.parametrize("r,D", [(2, 128), (3, 64), (4, 128), (5, 128), (6, 64), (8, 128), (8, 64)])
+def test_query_group_sizes(r, D):
+    announce("group size", r, D)
+    cfg = dataclasses.replace(W.CONFIGS["serve_b32"], Hkv=2, Hq=2 * r, D=D, v_group=64, prot_frac=0.10,
+                              kscale=True, ragged=(200, 420))
+    w, cache, ora = build_case(cfg, T=420, B=3)
+    c = w.cfg
+    assert c.Hq // c.Hkv == r
+    compare_commit(cache, ora, 0, c.B)
+    ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk)
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    for split in (1000, 3, 0):
+        cache.set_split_slots(split)
+        for odt, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+            out = cache.block_attn(q, kb, vb, out_dtype=odt)
+            e, x = attention_error(out, ref, name)
+            print(f"r={r} D={D} split={split} {name}-out err={e:.2e}")
+            assert np.isfinite(e) and x <= 0, f"r={r} D={D} split={split} {name} output error {e}"
