@@ -219,10 +219,11 @@ def main():
     w = W.make(cfg)
     c = cfg
     L = args.layers
-    # commits per layer cache: the warm-up loop and three timed loops of
-    # consecutive steps (the step, the separate-calls step, commit alone),
-    # each spread round-robin over the L caches
-    commits_per_layer = -(-args.warmup // L) + 3 * -(-args.steps // L)
+    # commits per layer cache: the warm-up loop, three timed loops of
+    # consecutive steps (the step, the separate-calls step, commit alone) and
+    # at most 2L single steps timed one by one, each spread round-robin over
+    # the L caches
+    commits_per_layer = -(-args.warmup // L) + 3 * -(-args.steps // L) + 2
     nblk = 4
     blocks = [W.step_block(c, s) for s in range(nblk)]
 
@@ -369,6 +370,19 @@ def main():
     ms_per_step = timed(do_attend_commit, args.steps, args.warmup)
     wall = time.perf_counter() - t0
 
+    # (1a) the distribution of single-step times: each of min(steps, 2L)
+    # further steps bracketed by its own pair of events (per-call GPU time,
+    # taken after the timed loop so that the loop has no events inside it)
+    n_dist = min(args.steps, 2 * L)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    torch.cuda.synchronize()
+    for i, (ea, eb) in enumerate(ev):
+        ea.record(stream)
+        do_attend_commit(args.warmup + args.steps + i)
+        eb.record(stream)
+    torch.cuda.synchronize()
+    step_dist = np.array([ea.elapsed_time(eb) for ea, eb in ev])
+
     # (1b) the same work as two calls: commit the finished block, then attend
     ms_per_step_separate = timed(separate, args.steps, 0)
 
@@ -453,6 +467,8 @@ def main():
         "commit_ms": commit_ms,
         "ms_per_step_attend_commit": ms_per_step,
         "ms_per_step_separate_calls": ms_per_step_separate,
+        "step_ms_p10_p50_p90": [float(np.percentile(step_dist, p)) for p in (10, 50, 90)],
+        "step_ms_samples": int(len(step_dist)),
         "attn_query_tokens_per_s": qtok / attn_s,
         "attn_hbm_gbs": achieved_gbs,
         "attn_tflops": achieved_tflops,
