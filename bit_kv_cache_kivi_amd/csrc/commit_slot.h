@@ -735,15 +735,19 @@ struct SlotQuant {
   // with 128-bit buffer stores; every thread issues the same number of stores
   // (lanes past the record, and the header store of all but one thread, fall
   // outside their resource and are dropped).
+  static constexpr int kStoreNT = 2;   // buffer-store cache policy: nt
   __device__ __forceinline__ void copy_out(const CommitTask& task, const uint8_t* rec) const {
     const uint32_t rbytes = io.record_bytes;
     uint8_t* dst = io.seg.records + (((size_t)task.b * io.hkv + h) * io.seg.slot_cap + task.dst_slot) * rbytes;
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(dst, 0, rbytes, 0x00020000);
+    // records are stored with the non-temporal hint (cache policy bit nt):
+    // nothing reads them again in this kernel, and a prefill commit that left
+    // them dirty in L2 waited longer at the kernel boundary (about 2% per call)
 #pragma unroll
     for (int r = 0; r < NST; ++r) {
       const uint32_t off = (r * 256 + tid) * 16;
       const uint4 val = *reinterpret_cast<const uint4*>(rec + (off < REC_MAX ? off : REC_MAX - 16));
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rr, off < rbytes ? off : 0x7ff00000u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rr, off < rbytes ? off : 0x7ff00000u, 0, kStoreNT);
     }
     uint8_t* hdst = io.seg.headers + ((size_t)task.b * io.seg.slot_cap + task.dst_slot) * kHeaderBytes;
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(hdst, 0, kHeaderBytes, 0x00020000);
