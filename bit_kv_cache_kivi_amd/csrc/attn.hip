@@ -558,11 +558,7 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
   // ---------------- consumers: scores of unit q (part 1) and softmax + PV of
   // unit q (part 2)
   float m_ref = -__builtin_inff(), l_run = 0.f;
-  floatx16 o[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[ct][i] = 0.f;
+  floatx16 o[CT];                            // zeroed once the Q operands are built
   floatx16 sacc;
   // The operand tiles are read from LDS a few k-steps ahead of the MFMAs
   // that use them (the scheduling barriers pin the interleave; left alone
@@ -770,77 +766,91 @@ __global__ __launch_bounds__((NC + kProducerWaves) * 64) void attn_kernel(const 
     }
     return;
   }
+  // Q operands.  Q is the B operand of S^T: lane = query token j; half hh
+  // holds channels (D/2)*hh + 8s + [0, 8) at k-step s.  Q8, Q in e4m3 for the
+  // key lo product: block k holds channels 64k + 32*hh + [0, 32) (the lo-tile
+  // layout).  The fp16 operands of bf16 Q are loaded before the two prologue
+  // barriers and converted after them, so the fetch overlaps the producers'
+  // header reads and first unit loads (the first scores come an interval
+  // later); the barriers order LDS only, so the loads stay in flight across
+  // them.  fp32 Q (twice the registers) is loaded and converted after them.
   {
-    // Q is the B operand of S^T: lane = query token j; half hh holds channels
-    // (D/2)*hh + 8s + [0, 8) at k-step s.
     const int j = lane & 31, hh = lane >> 5;
     const int hq = kvh * r + ci;
     const size_t base = (((size_t)b * kSlot + j) * hq_all + hq) * D + (D / 2) * hh;
-    if (q_f32) {
-      float4 raw[KS][2];
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q_ptr) + base);
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) { raw[s][0] = p[2 * s]; raw[s][1] = p[2 * s + 1]; }
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float x[8] = {raw[s][0].x, raw[s][0].y, raw[s][0].z, raw[s][0].w,
-                            raw[s][1].x, raw[s][1].y, raw[s][1].z, raw[s][1].w};
-        qop[s] = to_half8(x);
-      }
-    } else {
-      uint4 raw[KS];
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_ptr) + base);
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) raw[s] = p[s];
-  #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float x[8] = {bf16_lo(raw[s].x), bf16_hi(raw[s].x), bf16_lo(raw[s].y), bf16_hi(raw[s].y),
-                            bf16_lo(raw[s].z), bf16_hi(raw[s].z), bf16_lo(raw[s].w), bf16_hi(raw[s].w)};
-        qop[s] = to_half8(x);
-      }
-    }
-  }
-  {
-    // Q8: Q in e4m3 for the key lo product; lane = query token j, block k
-    // holds channels 64k + 32*hh + [0, 32) (the lo-tile layout)
-    const int j = lane & 31, hh = lane >> 5;
     const size_t row = (((size_t)b * kSlot + j) * hq_all + kvh * r + min(ci, r - 1)) * D;
-#pragma unroll
-    for (int k = 0; k < KB8; ++k) {
-      const int c0 = 64 * k + 32 * hh;
-      float x[32];
-      if (q_f32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q_ptr) + row + c0);
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float4 t = p[v];
-          x[4 * v] = t.x; x[4 * v + 1] = t.y; x[4 * v + 2] = t.z; x[4 * v + 3] = t.w;
-        }
-      } else {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_ptr) + row + c0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 t = p[v];
-          x[8 * v] = bf16_lo(t.x); x[8 * v + 1] = bf16_hi(t.x); x[8 * v + 2] = bf16_lo(t.y); x[8 * v + 3] = bf16_hi(t.y);
-          x[8 * v + 4] = bf16_lo(t.z); x[8 * v + 5] = bf16_hi(t.z); x[8 * v + 6] = bf16_lo(t.w); x[8 * v + 7] = bf16_hi(t.w);
-        }
-      }
+    auto q8_pack = [&](int k, const float (&x)[32]) __attribute__((always_inline)) {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w], x[4 * w + 1], 0u, false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], d, true);
         q8[k][w] = (int)d;
       }
-    }
-  }
-  if constexpr (CEN) {
-    if (ci < r) {
+    };
+    uint4 raw[KS];
+    if (!q_f32) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_ptr) + base);
 #pragma unroll
-      for (int g = 0; g < D / 32; ++g) zsum[ci][g][lane] = 0.f;
+      for (int s = 0; s < KS; ++s) raw[s] = p[s];
+    }
+    if constexpr (CEN) {
+      if (ci < r) {
+#pragma unroll
+        for (int g = 0; g < D / 32; ++g) zsum[ci][g][lane] = 0.f;
+      }
+    }
+    // the producers' header barrier and prologue barrier
+    lds_barrier();
+    lds_barrier();
+    if (q_f32) {
+      float4 rf[KS][2];
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q_ptr) + base);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) { rf[s][0] = p[2 * s]; rf[s][1] = p[2 * s + 1]; }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float x[8] = {rf[s][0].x, rf[s][0].y, rf[s][0].z, rf[s][0].w,
+                            rf[s][1].x, rf[s][1].y, rf[s][1].z, rf[s][1].w};
+        qop[s] = to_half8(x);
+      }
+#pragma unroll
+      for (int k = 0; k < KB8; ++k) {
+        const float4* p8 = reinterpret_cast<const float4*>(static_cast<const float*>(q_ptr) + row + 64 * k + 32 * hh);
+        float x[32];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float4 t = p8[v];
+          x[4 * v] = t.x; x[4 * v + 1] = t.y; x[4 * v + 2] = t.z; x[4 * v + 3] = t.w;
+        }
+        q8_pack(k, x);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float x[8] = {bf16_lo(raw[s].x), bf16_hi(raw[s].x), bf16_lo(raw[s].y), bf16_hi(raw[s].y),
+                            bf16_lo(raw[s].z), bf16_hi(raw[s].z), bf16_lo(raw[s].w), bf16_hi(raw[s].w)};
+        qop[s] = to_half8(x);
+      }
+#pragma unroll
+      for (int k = 0; k < KB8; ++k) {
+        // the same rows as the fp16 operands, read again in the lo-tile layout
+        // (from L2: this wave has just fetched them)
+        const uint4* p8 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q_ptr) + row + 64 * k + 32 * hh);
+        float x[32];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 t = p8[v];
+          x[8 * v] = bf16_lo(t.x); x[8 * v + 1] = bf16_hi(t.x); x[8 * v + 2] = bf16_lo(t.y); x[8 * v + 3] = bf16_hi(t.y);
+          x[8 * v + 4] = bf16_lo(t.z); x[8 * v + 5] = bf16_hi(t.z); x[8 * v + 6] = bf16_lo(t.w); x[8 * v + 7] = bf16_hi(t.w);
+        }
+        q8_pack(k, x);
+      }
     }
   }
-  __syncthreads();
-  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[ct][i] = 0.f;
   if (ci >= r) {
     for (int i = 0; i < n_int; ++i) __syncthreads();
     if (fuse) __syncthreads();   // the fused commit's barrier
