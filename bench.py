@@ -47,8 +47,8 @@ _FETCH_SCALE = 262144.0 / 131084.0
 _WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     "dream7b_4bit": {
-        "attn_source_sha256": "b200ebc3093877972398394dcf139458e63678ad54288250013686dc224d5b58",
-        "kib": {"attn_kernel": {"fetch": 27229.25, "write": 15008},
+        "attn_source_sha256": "0293a1414c09087caaef9185cecc7f3c1f8d2e1b33f2a3a9fd6ab1641521c7ee",
+        "kib": {"attn_kernel": {"fetch": 27232.25, "write": 15008},
                 "combine_h16_kernel": {"fetch": 7536, "write": 1792}},
     },
 }
