@@ -46,3 +46,31 @@ def test_query_group_sizes(r, D):
             e, x = attention_error(out, ref, name)
             print(f"r={r} D={D} split={split} {name}-out err={e:.2e}")
             assert np.isfinite(e) and x <= 0, f"r={r} D={D} split={split} {name} output error {e}"
+
+
+@pytest.mark.parametrize("r,D", [(1, 128), (7, 128), (6, 64)])
+def test_fp32_inputs(r, D):
+    """fp32 queries and block rows in both builds (the consumers load fp32 Q after
+    their prologue barriers, bf16 Q before them): records byte for byte, outputs
+    within the gate at one split and automatically, both output dtypes.  Keys are
+    N(0, 1), as in the one workload with fp32 inputs (tiny): the MFMA operands
+    take Q rounded to fp16, which is exact for bf16 Q but not for fp32 Q, and with
+    lognormal key channel scales that rounding alone gives 1.8e-3 to 2.05e-3, at
+    the gate (a known limit of fp32 queries, not of the workloads)."""
+    announce("fp32 inputs", r, D)
+    cfg = dataclasses.replace(W.CONFIGS["serve_b32"], Hkv=2, Hq=2 * r, D=D, v_group=64, prot_frac=0.10,
+                              kscale=False, ragged=(200, 420), dtype="f32")
+    w, cache, ora = build_case(cfg, T=420, B=3)
+    c = w.cfg
+    assert c.dtype == "f32" and c.Hq // c.Hkv == r
+    compare_commit(cache, ora, 0, c.B)
+    ref = O.block_attention(ora, w.q, w.k_blk, w.v_blk)
+    q, kb, vb = dev(w.q, c.dtype), dev(w.k_blk, c.dtype), dev(w.v_blk, c.dtype)
+    assert q.dtype == torch.float32
+    for split in (1000, 0):
+        cache.set_split_slots(split)
+        for odt, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+            out = cache.block_attn(q, kb, vb, out_dtype=odt)
+            e, x = attention_error(out, ref, name)
+            print(f"fp32 inputs r={r} D={D} split={split} {name}-out err={e:.2e}")
+            assert np.isfinite(e) and x <= 0, f"fp32 inputs r={r} D={D} split={split} {name} output error {e}"
